@@ -1,0 +1,182 @@
+// C ABI layer of libbiloco_hip: argument checks (no HIP call), workspace
+// sizing, schedule choice, dispatch to the launchers.
+#include "../../include/biloco.h"
+#include "biloco_internal.h"
+
+#include <stdint.h>
+
+using namespace biloco;
+
+namespace {
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + nb && b0 < a0 + na;
+}
+
+
+bool schedule_allowed(int s, int M, int N, int K, int r) {
+    switch (s) {
+        case BILOCO_SCHED_UNFUSED: return true;
+        case BILOCO_SCHED_FUSED_GEMV: return gemv_supported(M, N, K, r);
+        default: return false;
+    }
+}
+
+biloco_status check_shape(int32_t M, int32_t N, int32_t K, int32_t r) {
+    if (M < 1 || N < 1 || K < 1 || r < 0) return BILOCO_ERR_INVALID_VALUE;
+    if (K % 16 != 0) return BILOCO_ERR_INVALID_VALUE;   // NVFP4 blocks of 16
+    if (M > 32) return BILOCO_ERR_UNSUPPORTED;          // decode batches up to 32
+    if (K % 32 != 0 || K < 32) return BILOCO_ERR_UNSUPPORTED;
+    return BILOCO_OK;
+}
+
+int resolve_schedule(int M, int N, int K, int r) {
+    if (M <= 2 && schedule_allowed(BILOCO_SCHED_FUSED_GEMV, M, N, K, r)) return BILOCO_SCHED_FUSED_GEMV;
+    return BILOCO_SCHED_UNFUSED;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *biloco_status_string(biloco_status s) {
+    switch (s) {
+        case BILOCO_OK: return "BILOCO_OK";
+        case BILOCO_ERR_INVALID_VALUE: return "BILOCO_ERR_INVALID_VALUE";
+        case BILOCO_ERR_UNSUPPORTED: return "BILOCO_ERR_UNSUPPORTED";
+        case BILOCO_ERR_HIP: return "BILOCO_ERR_HIP";
+        case BILOCO_ERR_WORKSPACE_TOO_SMALL: return "BILOCO_ERR_WORKSPACE_TOO_SMALL";
+        default: return "BILOCO_ERR_UNKNOWN";
+    }
+}
+
+biloco_status biloco_pack_signs(const int8_t *signs, int64_t rows, int64_t cols, uint32_t *packed,
+                                hipStream_t stream) {
+    if (!signs || !packed || rows < 1 || cols < 1) return BILOCO_ERR_INVALID_VALUE;
+    if (!aligned16(signs) || !aligned16(packed)) return BILOCO_ERR_INVALID_VALUE;
+    if (rows > ((int64_t)1 << 40) / cols) return BILOCO_ERR_UNSUPPORTED;
+    if (overlaps(signs, (size_t)(rows * cols), packed, (size_t)(((rows + 31) / 32) * cols * 4)))
+        return BILOCO_ERR_INVALID_VALUE;
+    return launch_pack_signs(signs, rows, cols, packed, stream) == hipSuccess ? BILOCO_OK
+                                                                             : BILOCO_ERR_HIP;
+}
+
+biloco_status biloco_quant_act_fp4(const uint16_t *x_bf16, int32_t M, int32_t K, uint8_t *a_codes,
+                                   uint8_t *a_scales, hipStream_t stream) {
+    if (!x_bf16 || !a_codes || !a_scales || M < 1 || K < 1) return BILOCO_ERR_INVALID_VALUE;
+    if (K % 16 != 0) return BILOCO_ERR_INVALID_VALUE;
+    if (K % 32 != 0) return BILOCO_ERR_UNSUPPORTED;
+    if (!aligned16(x_bf16) || !aligned16(a_codes) || !aligned16(a_scales))
+        return BILOCO_ERR_INVALID_VALUE;
+    size_t nx = (size_t)M * K * 2, nc = (size_t)M * K / 2, ns = (size_t)M * K / 16;
+    if (overlaps(x_bf16, nx, a_codes, nc) || overlaps(x_bf16, nx, a_scales, ns) ||
+        overlaps(a_codes, nc, a_scales, ns))
+        return BILOCO_ERR_INVALID_VALUE;
+    return launch_quant_act(x_bf16, M, K, a_codes, a_scales, stream) == hipSuccess
+               ? BILOCO_OK
+               : BILOCO_ERR_HIP;
+}
+
+biloco_status biloco_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t r,
+                                          size_t *bytes) {
+    if (!bytes) return BILOCO_ERR_INVALID_VALUE;
+    biloco_status st = check_shape(M, N, K, r);
+    if (st != BILOCO_OK) return st;
+    *bytes = r > 0 ? ws_total_bytes(M, N, K, r) : 0;
+    return BILOCO_OK;
+}
+
+biloco_status biloco_gemm_check(const void *a_codes, const void *a_scales, const void *x_bf16,
+                                const void *w_codes, const void *w_scales, const void *v_packed,
+                                const void *u_packed, const void *alpha_bf16, int32_t M, int32_t N,
+                                int32_t K, int32_t r, const void *y_bf16, const void *workspace,
+                                size_t workspace_bytes, int32_t schedule) {
+    biloco_status st = check_shape(M, N, K, r);
+    if (st != BILOCO_OK) return st;
+    if (!a_codes || !a_scales || !w_codes || !w_scales || !y_bf16) return BILOCO_ERR_INVALID_VALUE;
+    if (r > 0 && (!x_bf16 || !v_packed || !u_packed || !alpha_bf16))
+        return BILOCO_ERR_INVALID_VALUE;
+    const void *ptrs[] = {a_codes, a_scales, x_bf16, w_codes, w_scales,
+                          v_packed, u_packed, alpha_bf16, y_bf16, workspace};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return BILOCO_ERR_INVALID_VALUE;
+    size_t need = r > 0 ? ws_total_bytes(M, N, K, r) : 0;
+    if (need > 0 && !workspace) return BILOCO_ERR_INVALID_VALUE;
+    if (workspace_bytes < need) return BILOCO_ERR_WORKSPACE_TOO_SMALL;
+    // the output must not overlap any operand
+    size_t W = (size_t)(r + 31) / 32;
+    size_t ny = (size_t)M * N * 2;
+    struct { const void *p; size_t n; } ins[] = {
+        {a_codes, (size_t)M * K / 2},  {a_scales, (size_t)M * K / 16},
+        {x_bf16, r > 0 ? (size_t)M * K * 2 : 0},
+        {w_codes, (size_t)N * K / 2},  {w_scales, (size_t)N * K / 16},
+        {v_packed, W * (size_t)K * 4}, {u_packed, W * (size_t)N * 4},
+        {alpha_bf16, (size_t)r * 2},   {workspace, need}};
+    for (auto &in : ins)
+        if (overlaps(y_bf16, ny, in.p, in.n)) return BILOCO_ERR_INVALID_VALUE;
+    if (schedule < BILOCO_SCHED_AUTO || schedule > BILOCO_SCHED_FUSED_MFMA)
+        return BILOCO_ERR_INVALID_VALUE;
+    if (schedule != BILOCO_SCHED_AUTO && !schedule_allowed(schedule, M, N, K, r))
+        return BILOCO_ERR_UNSUPPORTED;
+    return BILOCO_OK;
+}
+
+int32_t biloco_default_schedule(int32_t M, int32_t N, int32_t K, int32_t r) {
+    if (check_shape(M, N, K, r) != BILOCO_OK) return 0;
+    return resolve_schedule(M, N, K, r);
+}
+
+int32_t biloco_schedules_for(int32_t M, int32_t N, int32_t K, int32_t r, int32_t *out,
+                             int32_t cap) {
+    if (check_shape(M, N, K, r) != BILOCO_OK) return 0;
+    int32_t n = 0;
+    for (int s = BILOCO_SCHED_UNFUSED; s <= BILOCO_SCHED_FUSED_MFMA; ++s)
+        if (schedule_allowed(s, M, N, K, r)) {
+            if (out && n < cap) out[n] = s;
+            ++n;
+        }
+    return n;
+}
+
+biloco_status biloco_gemm_lowrank_sched(const uint8_t *a_codes, const uint8_t *a_scales,
+                                        const uint16_t *x_bf16, const uint8_t *w_codes,
+                                        const uint8_t *w_scales, float w_global_scale,
+                                        const uint32_t *v_packed, const uint32_t *u_packed,
+                                        const uint16_t *alpha_bf16, int32_t M, int32_t N,
+                                        int32_t K, int32_t r, uint16_t *y_bf16, void *workspace,
+                                        size_t workspace_bytes, int32_t schedule,
+                                        hipStream_t stream) {
+    biloco_status st = biloco_gemm_check(a_codes, a_scales, x_bf16, w_codes, w_scales, v_packed,
+                                         u_packed, alpha_bf16, M, N, K, r, y_bf16, workspace,
+                                         workspace_bytes, schedule);
+    if (st != BILOCO_OK) return st;
+    GemmArgs a{a_codes, a_scales, x_bf16, w_codes, w_scales, w_global_scale, v_packed,
+               u_packed, alpha_bf16, M,       N,        K,     r,      y_bf16,
+               workspace, workspace_bytes};
+    int s = schedule == BILOCO_SCHED_AUTO ? resolve_schedule(M, N, K, r) : schedule;
+    hipError_t e;
+    switch (s) {
+        case BILOCO_SCHED_FUSED_GEMV: e = launch_gemm_fused_gemv(a, stream); break;
+        case BILOCO_SCHED_FUSED_MFMA: e = launch_gemm_fused_mfma(a, stream); break;
+        default: e = launch_gemm_unfused(a, stream); break;
+    }
+    return e == hipSuccess ? BILOCO_OK : BILOCO_ERR_HIP;
+}
+
+biloco_status biloco_gemm_lowrank(const uint8_t *a_codes, const uint8_t *a_scales,
+                                  const uint16_t *x_bf16, const uint8_t *w_codes,
+                                  const uint8_t *w_scales, float w_global_scale,
+                                  const uint32_t *v_packed, const uint32_t *u_packed,
+                                  const uint16_t *alpha_bf16, int32_t M, int32_t N, int32_t K,
+                                  int32_t r, uint16_t *y_bf16, void *workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+    return biloco_gemm_lowrank_sched(a_codes, a_scales, x_bf16, w_codes, w_scales, w_global_scale,
+                                     v_packed, u_packed, alpha_bf16, M, N, K, r, y_bf16, workspace,
+                                     workspace_bytes, BILOCO_SCHED_AUTO, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,92 @@
+// Device-side helpers of the HIP path: element formats and wave reductions.
+// Formats follow the NVFP4 layout that the BiLoCo README's section "Kernel"
+// names for R and for the activation: E2M1 element codes (two per byte, even
+// element in the low nibble) and E4M3 block scales (one per 16 elements).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace biloco {
+
+// ---------------------------------------------------------------- bf16
+__device__ __forceinline__ float bf16_to_f32(uint32_t h16) {
+    return __uint_as_float(h16 << 16);
+}
+
+// fp32 -> bf16 with round-to-nearest-even; NaN kept quiet.
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// ---------------------------------------------------------------- E4M3 (OCP FN)
+// Byte -> fp32.  Exponent field 0 is subnormal (m * 2^-9).  The NaN pattern
+// never occurs in scales this library writes or accepts as meaningful.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+    uint32_t e = (b >> 3) & 15u, m = b & 7u;
+    float mag = (e == 0u) ? (float)m * 0.001953125f                       // m * 2^-9
+                          : __uint_as_float(((e + 120u) << 23) | (m << 20));
+    return (b & 0x80u) ? -mag : mag;
+}
+
+// Non-negative finite fp32 -> E4M3 byte, round to nearest, ties to an even
+// mantissa; saturates to 448 (0x7E).
+__device__ __forceinline__ uint32_t f32_to_e4m3_rne(float q) {
+    if (q >= 448.0f) return 0x7Eu;
+    if (q < 0.015625f) {                       // below 2^-6: subnormal grid of 2^-9
+        // q * 512 is exact; rint rounds half to even.  A result of 8 is the
+        // smallest normal 2^-6, whose byte is also 8.
+        return (uint32_t)__builtin_rintf(q * 512.0f);
+    }
+    uint32_t u = __float_as_uint(q);
+    uint32_t rnd = u + 0x7FFFFu + ((u >> 20) & 1u);   // round mantissa to 3 bits
+    uint32_t e = (rnd >> 23) - 120u;                  // rebias 127 -> 7
+    return (e << 3) | ((rnd >> 20) & 7u);
+}
+
+// ---------------------------------------------------------------- E2M1
+// Code (0..15) -> fp32.
+__device__ __forceinline__ float e2m1_to_f32(uint32_t c) {
+    uint32_t e = (c >> 1) & 3u, m = c & 1u;
+    float mag = (e == 0u) ? 0.5f * (float)m : __uint_as_float(((e + 126u) << 23) | (m << 22));
+    return (c & 8u) ? -mag : mag;
+}
+
+// Nearest-even E2M1 magnitude code of a = |x| for a scale s > 0.  Each
+// product s * t below is exact in fp32 (s has at most 4 significant bits and
+// every t at most 3), so the comparisons decide the rounding exactly.
+__device__ __forceinline__ uint32_t e2m1_mag_code(float a, float s) {
+    return (uint32_t)(a > 0.25f * s) + (uint32_t)(a >= 0.75f * s) + (uint32_t)(a > 1.25f * s) +
+           (uint32_t)(a >= 1.75f * s) + (uint32_t)(a > 2.5f * s) + (uint32_t)(a >= 3.5f * s) +
+           (uint32_t)(a > 5.0f * s);
+}
+
+// ---------------------------------------------------------------- reductions
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// Sum over the 64 lanes, returned (uniform) to every lane: DPP sums inside
+// each row of 16 lanes (quad pairs, quads, half-row mirror, row mirror),
+// then the four row sums are read into scalars.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+    v += dpp_mov<0xB1>(v);     // quad_perm [1,0,3,2]
+    v += dpp_mov<0x4E>(v);     // quad_perm [2,3,0,1]
+    v += dpp_mov<0x141>(v);    // row_half_mirror
+    v += dpp_mov<0x140>(v);    // row_mirror
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return (r0 + r1) + (r2 + r3);
+}
+
+}  // namespace biloco

@@ -1,0 +1,51 @@
+// Internal interface between the C ABI layer (biloco_api.cpp) and the HIP
+// launch code.  Not installed; not part of the ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace biloco {
+
+struct GemmArgs {
+    const uint8_t *a_codes;
+    const uint8_t *a_scales;
+    const uint16_t *x;
+    const uint8_t *w_codes;
+    const uint8_t *w_scales;
+    float g;
+    const uint32_t *v;
+    const uint32_t *u;
+    const uint16_t *alpha;
+    int M, N, K, r;
+    uint16_t *y;
+    void *ws;
+    size_t ws_bytes;
+};
+
+// Workspace layout (byte offsets).  The header holds the call epoch (word 0)
+// and the arrival counter (word 32) of the one-launch schedules.  Then z as
+// (fp32 value, 32-bit epoch tag) pairs [M][Rpad] for the one-launch schedules,
+// then z as plain fp32 [M][Rpad] for the two-launch schedule (a separate area,
+// so that plain floats can never be read back as tags).
+constexpr size_t kWsHeaderBytes = 256;
+inline int rpad32(int r) { return (r + 31) / 32 * 32; }
+inline size_t ws_zt_offset() { return kWsHeaderBytes; }
+inline size_t ws_zt_bytes(int M, int r) { return (size_t)8 * (size_t)M * (size_t)rpad32(r); }
+inline size_t ws_zf_offset(int M, int r) { return ws_zt_offset() + ws_zt_bytes(M, r); }
+inline size_t ws_zf_bytes(int M, int r) { return (size_t)4 * (size_t)M * (size_t)rpad32(r); }
+inline size_t ws_total_bytes(int M, int N, int K, int r) {
+    (void)N; (void)K;
+    return ws_zf_offset(M, r) + ws_zf_bytes(M, r);
+}
+
+hipError_t launch_pack_signs(const int8_t *signs, int64_t rows, int64_t cols, uint32_t *packed,
+                             hipStream_t stream);
+hipError_t launch_quant_act(const uint16_t *x, int M, int K, uint8_t *codes, uint8_t *scales,
+                            hipStream_t stream);
+hipError_t launch_gemm_unfused(const GemmArgs &a, hipStream_t stream);
+hipError_t launch_gemm_fused_gemv(const GemmArgs &a, hipStream_t stream);
+bool gemv_supported(int M, int N, int K, int r);   // shapes the one-launch vector-ALU schedule handles
+hipError_t launch_gemm_fused_mfma(const GemmArgs &a, hipStream_t stream);
+
+}  // namespace biloco

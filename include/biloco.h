@@ -1,0 +1,162 @@
+/*
+ * biloco.h -- C ABI of libbiloco_hip: the decode-time fused product of BiLoCo
+ * on AMD Instinct MI355X (gfx950).
+ *
+ *     y = Q4(x) . deq(R)^T  +  sum_i alpha_i (x . v_i) u_i
+ *
+ * Source of the operation: "BiLoCo: Binary Low-Rank Corrections for
+ * Post-Training Quantization" (project README).  Its intro gives the weight
+ * model W ~ U diag(alpha) V^T + R with U in {+-1}^{N x r}, V in {+-1}^{K x r}
+ * and R stored in NVFP4; its section "Kernel" gives the fused product, the
+ * decode batch limit (M <= 32), z = alpha (.) (V x) computed from the packed
+ * signs of V, the expansion of z through the packed signs of U before the
+ * bf16 store, and the launcher's operands: NVFP4 codes and block scales of R,
+ * the fp32 global scale, pack_signs(V.T), pack_signs(U.T), alpha in bf16, the
+ * NVFP4 activation (codes + block scales) and the bf16 activation x.
+ *
+ * Conventions shared by every entry point
+ *  - Memory: every array pointer is DEVICE memory owned by the caller.  The
+ *    library allocates nothing on any call path and keeps no pointer after a
+ *    call returns.
+ *  - Asynchrony: calls are ordered on `stream` (NULL = the null stream) and
+ *    return as soon as the work is enqueued.  The status reports host-side
+ *    argument checks and the launch itself, never the kernel's completion.
+ *  - Errors: arguments are checked on the host BEFORE any HIP call; a bad
+ *    argument returns BILOCO_ERR_INVALID_VALUE or BILOCO_ERR_UNSUPPORTED and
+ *    enqueues nothing.  No exception crosses the ABI and nothing is printed.
+ *  - Layouts are row-major.  "bf16" arrays hold raw bfloat16 bit patterns
+ *    (uint16_t); NVFP4 element codes are E2M1, two per byte, element 2j in
+ *    the LOW nibble of byte j; block scales are E4M3 (OCP "FN": bias 7, max
+ *    448, no infinity), one byte per 16 consecutive elements along K.
+ *  - Alignment: every pointer must be 16-byte aligned.
+ *  - Thread safety: the host side keeps no mutable state; concurrent calls
+ *    are safe as long as they do not share an output or a workspace.
+ */
+#ifndef BILOCO_H_
+#define BILOCO_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t biloco_status;
+#define BILOCO_OK                       0
+#define BILOCO_ERR_INVALID_VALUE        1  /* null pointer, bad size, misaligned pointer */
+#define BILOCO_ERR_UNSUPPORTED          2  /* well-formed but outside what the kernels handle */
+#define BILOCO_ERR_HIP                  3  /* the HIP runtime reported an error at launch */
+#define BILOCO_ERR_WORKSPACE_TOO_SMALL  4
+
+/* Schedules of biloco_gemm_lowrank_sched (BiLoCo "Kernel": the launcher picks
+ * the fastest mode for batch size and rank, and can list the modes a shape
+ * allows).  The modes here are this library's own, designed for gfx950. */
+#define BILOCO_SCHED_AUTO        0  /* pick per shape (biloco_default_schedule) */
+#define BILOCO_SCHED_UNFUSED     1  /* z kernel, then GEMM + epilogue kernel (two launches) */
+#define BILOCO_SCHED_FUSED_GEMV  2  /* one launch; vector-ALU dot products; M <= 4 */
+#define BILOCO_SCHED_FUSED_MFMA  3  /* one launch; matrix-core products; any M <= 32 */
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *biloco_status_string(biloco_status s);
+
+/* pack_signs (BiLoCo "Kernel": the launcher receives pack_signs(V.T) and
+ * pack_signs(U.T)).  Packs a sign matrix along its FIRST axis, 32 signs per
+ * 32-bit word:
+ *   signs  int8 [rows][cols]; an entry < 0 means -1, any other value +1.
+ *          Pass V^T ([r][K]) or U^T ([r][N]): rows is the rank axis.
+ *   packed uint32 [ceil(rows/32)][cols]; bit b of word (w, c) is 1 when
+ *          signs[32w+b][c] < 0; bits for 32w+b >= rows are written as 0.
+ * rows >= 1, cols >= 1.  Bit-exact; one launch. */
+biloco_status biloco_pack_signs(const int8_t *signs, int64_t rows, int64_t cols,
+                                uint32_t *packed, hipStream_t stream);
+
+/* Activation FP4 quantisation (BiLoCo "Kernel": the fused product takes
+ * FP4(x) as NVFP4 codes and block scales).  For each row m and each block of
+ * 16 consecutive k: amax = max |x|; scale = E4M3(amax / 6) rounded to
+ * nearest-even (saturating at 448); code = E2M1(x / scale) rounded to
+ * nearest-even (saturating at 6) with the sign of x kept, also for values
+ * that round to zero; a zero scale gives signed-zero codes.
+ *   x_bf16   [M][K] bf16
+ *   a_codes  [M][K/2] uint8  (E2M1 pairs, even k in the low nibble)
+ *   a_scales [M][K/16] uint8 (E4M3)
+ * M >= 1, K >= 32, K % 32 == 0.  Inputs must be finite.  Bit-exact. */
+biloco_status biloco_quant_act_fp4(const uint16_t *x_bf16, int32_t M, int32_t K,
+                                   uint8_t *a_codes, uint8_t *a_scales, hipStream_t stream);
+
+/* Bytes of device workspace biloco_gemm_lowrank needs for this shape.
+ * Same argument rules as biloco_gemm_lowrank. */
+biloco_status biloco_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t r,
+                                          size_t *bytes);
+
+/* The fused product (BiLoCo "Kernel"):
+ *   y[m][n] = bf16( g * sum_k A[m][k] B[n][k]  +  sum_{i<r} z[m][i] U[n][i] )
+ *   A[m][k] = e2m1(a_codes) * e4m3(a_scales[m][k/16])   (the FP4 activation)
+ *   B[n][k] = e2m1(w_codes) * e4m3(w_scales[n][k/16])   (the NVFP4 residual R)
+ *   z[m][i] = alpha_i * sum_k x[m][k] V[k][i]           (bf16 x, not FP4)
+ *   U, V in {+-1}: bit 1 of the packed words means -1.
+ * Operands:
+ *   a_codes  [M][K/2] uint8, a_scales [M][K/16] uint8  (biloco_quant_act_fp4)
+ *   x_bf16   [M][K] bf16
+ *   w_codes  [N][K/2] uint8, w_scales [N][K/16] uint8, w_global_scale (g)
+ *   v_packed [ceil(r/32)][K] uint32  = pack_signs(V^T)
+ *   u_packed [ceil(r/32)][N] uint32  = pack_signs(U^T)
+ *   alpha_bf16 [r] bf16
+ *   y_bf16   [M][N] bf16 (output; exactly M rows; must not alias an input)
+ *   workspace: >= biloco_gemm_workspace_bytes(...) bytes of device memory,
+ *          ZERO-FILLED by the caller before its first use; afterwards the
+ *          library keeps it consistent by itself.  One workspace must not be
+ *          used by two calls that can run at the same time (use one per
+ *          stream).
+ * Limits: 1 <= M <= 32; N >= 1; K >= 32 and K % 32 == 0; r >= 0.
+ * With r == 0, x_bf16, v_packed, u_packed and alpha_bf16 may be NULL.
+ * Accuracy: y is within 8e-3*|y_ref| + 1e-3*rms(y_ref) of the exact value
+ * (fp32 accumulation, bf16 output rounding).  One or two launches on
+ * `stream`, depending on the schedule. */
+biloco_status biloco_gemm_lowrank(const uint8_t *a_codes, const uint8_t *a_scales,
+                                  const uint16_t *x_bf16,
+                                  const uint8_t *w_codes, const uint8_t *w_scales,
+                                  float w_global_scale,
+                                  const uint32_t *v_packed, const uint32_t *u_packed,
+                                  const uint16_t *alpha_bf16,
+                                  int32_t M, int32_t N, int32_t K, int32_t r,
+                                  uint16_t *y_bf16, void *workspace, size_t workspace_bytes,
+                                  hipStream_t stream);
+
+/* As biloco_gemm_lowrank, with an explicit schedule (BILOCO_SCHED_*).  A
+ * schedule the shape does not allow returns BILOCO_ERR_UNSUPPORTED. */
+biloco_status biloco_gemm_lowrank_sched(const uint8_t *a_codes, const uint8_t *a_scales,
+                                        const uint16_t *x_bf16,
+                                        const uint8_t *w_codes, const uint8_t *w_scales,
+                                        float w_global_scale,
+                                        const uint32_t *v_packed, const uint32_t *u_packed,
+                                        const uint16_t *alpha_bf16,
+                                        int32_t M, int32_t N, int32_t K, int32_t r,
+                                        uint16_t *y_bf16, void *workspace, size_t workspace_bytes,
+                                        int32_t schedule, hipStream_t stream);
+
+/* Host-only argument check of biloco_gemm_lowrank_sched: returns the status
+ * the call would return for these arguments before launching anything.
+ * Makes no HIP call (usable without a GPU). */
+biloco_status biloco_gemm_check(const void *a_codes, const void *a_scales, const void *x_bf16,
+                                const void *w_codes, const void *w_scales,
+                                const void *v_packed, const void *u_packed,
+                                const void *alpha_bf16,
+                                int32_t M, int32_t N, int32_t K, int32_t r,
+                                const void *y_bf16, const void *workspace,
+                                size_t workspace_bytes, int32_t schedule);
+
+/* The schedule BILOCO_SCHED_AUTO resolves to for this shape (0 if the shape
+ * is invalid).  No HIP call. */
+int32_t biloco_default_schedule(int32_t M, int32_t N, int32_t K, int32_t r);
+
+/* Writes up to `cap` schedules this shape allows into `out` and returns how
+ * many there are (BiLoCo "Kernel": modes_for(M, r, K)).  No HIP call. */
+int32_t biloco_schedules_for(int32_t M, int32_t N, int32_t K, int32_t r,
+                             int32_t *out, int32_t cap);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BILOCO_H_ */

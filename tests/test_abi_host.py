@@ -1,0 +1,121 @@
+"""The C ABI library loads, exports every entry point include/biloco.h
+declares, and rejects bad arguments on the host (no GPU, no HIP call)."""
+import os
+import re
+
+import pytest
+
+from bit_weight_gemm_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "biloco.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(biloco_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = B.lib()
+    names = _declared()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(names) == sorted(B.EXPORTED)
+
+
+def test_status_strings():
+    assert B.biloco_status_string(0) == "BILOCO_OK"
+    assert B.biloco_status_string(4) == "BILOCO_ERR_WORKSPACE_TOO_SMALL"
+    assert B.biloco_status_string(99) == "BILOCO_ERR_UNKNOWN"
+
+
+A = 1 << 36  # fake, 16-byte aligned, far-apart "device" addresses: never dereferenced
+
+
+def _args(M=1, N=256, K=256, r=16, ws_bytes=None, **over):
+    base = dict(a_codes=A * 1, a_scales=A * 2, x_bf16=A * 3, w_codes=A * 4, w_scales=A * 5,
+                v_packed=A * 6, u_packed=A * 7, alpha_bf16=A * 8, y=A * 10, workspace=A * 20)
+    base.update(over)
+    if ws_bytes is None:
+        ws_bytes = B.biloco_gemm_workspace_bytes(M, N, K, r)
+    return (base["a_codes"], base["a_scales"], base["x_bf16"], base["w_codes"], base["w_scales"],
+            base["v_packed"], base["u_packed"], base["alpha_bf16"], M, N, K, r, base["y"],
+            base["workspace"], ws_bytes)
+
+
+def test_check_accepts_valid():
+    assert B.biloco_gemm_check(*_args()) == B.BILOCO_OK
+    assert B.biloco_gemm_check(*_args(M=32, N=5120, K=13824, r=512)) == B.BILOCO_OK
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=0), B.BILOCO_ERR_INVALID_VALUE),
+    (dict(M=33), B.BILOCO_ERR_UNSUPPORTED),
+    (dict(N=0), B.BILOCO_ERR_INVALID_VALUE),
+    (dict(K=0), B.BILOCO_ERR_INVALID_VALUE),
+    (dict(K=48), B.BILOCO_ERR_UNSUPPORTED),
+    (dict(K=40), B.BILOCO_ERR_INVALID_VALUE),
+    (dict(r=-1), B.BILOCO_ERR_INVALID_VALUE),
+])
+def test_check_rejects_shapes(kw, status):
+    args = list(_args(ws_bytes=1 << 20))
+    M, N, K, r = kw.get("M", 1), kw.get("N", 256), kw.get("K", 256), kw.get("r", 16)
+    args[8:12] = [M, N, K, r]
+    assert B.biloco_gemm_check(*args) == status
+
+
+@pytest.mark.parametrize("name", ["a_codes", "a_scales", "x_bf16", "w_codes", "w_scales",
+                                  "v_packed", "u_packed", "alpha_bf16", "y", "workspace"])
+def test_check_rejects_null(name):
+    assert B.biloco_gemm_check(*_args(**{name: None})) == B.BILOCO_ERR_INVALID_VALUE
+
+
+@pytest.mark.parametrize("name", ["a_codes", "w_scales", "y", "workspace", "v_packed"])
+def test_check_rejects_misaligned(name):
+    good = dict(a_codes=A * 1, w_scales=A * 5, y=A * 10, workspace=A * 20, v_packed=A * 6)
+    assert B.biloco_gemm_check(*_args(**{name: good[name] + 8})) == B.BILOCO_ERR_INVALID_VALUE
+
+
+def test_r0_allows_null_lowrank_operands():
+    args = _args(r=0, x_bf16=None, v_packed=None, u_packed=None, alpha_bf16=None, workspace=None)
+    assert B.biloco_gemm_check(*args) == B.BILOCO_OK
+
+
+def test_workspace_too_small():
+    need = B.biloco_gemm_workspace_bytes(8, 13824, 5120, 512)
+    assert need > 0
+    args = _args(M=8, N=13824, K=5120, r=512, ws_bytes=need - 1)
+    assert B.biloco_gemm_check(*args) == B.BILOCO_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_output_aliasing_rejected():
+    # y overlapping w_codes
+    assert B.biloco_gemm_check(*_args(y=A * 4 + 16)) == B.BILOCO_ERR_INVALID_VALUE
+
+
+def test_schedule_queries():
+    for M, N, K, r in [(1, 256, 256, 16), (1, 5120, 5120, 512), (8, 13824, 5120, 512),
+                       (32, 5120, 13824, 512), (32, 8192, 8192, 1024)]:
+        s = B.biloco_default_schedule(M, N, K, r)
+        avail = B.biloco_schedules_for(M, N, K, r)
+        assert s in avail, (M, s, avail)
+        assert B.BILOCO_SCHED_UNFUSED in avail
+        for sch in avail:
+            assert B.biloco_gemm_check(*_args(M, N, K, r), schedule=sch) == B.BILOCO_OK
+    assert B.biloco_default_schedule(0, 1, 32, 0) == 0
+    assert B.biloco_gemm_check(*_args(), schedule=7) == B.BILOCO_ERR_INVALID_VALUE
+
+
+def test_prep_entry_points_reject_before_hip():
+    L = B.lib()
+    A = 0x10000
+    assert L.biloco_pack_signs(None, 16, 16, A, None) == B.BILOCO_ERR_INVALID_VALUE
+    assert L.biloco_pack_signs(A, 0, 16, A * 2, None) == B.BILOCO_ERR_INVALID_VALUE
+    assert L.biloco_pack_signs(A + 1, 16, 16, A * 2, None) == B.BILOCO_ERR_INVALID_VALUE
+    assert L.biloco_quant_act_fp4(A, 1, 48, A * 2, A * 3, None) == B.BILOCO_ERR_UNSUPPORTED
+    assert L.biloco_quant_act_fp4(A, 0, 64, A * 2, A * 3, None) == B.BILOCO_ERR_INVALID_VALUE
+    assert L.biloco_quant_act_fp4(None, 1, 64, A * 2, A * 3, None) == B.BILOCO_ERR_INVALID_VALUE
+    # codes overlapping x
+    assert L.biloco_quant_act_fp4(A, 1, 64, A + 64, A * 3, None) == B.BILOCO_ERR_INVALID_VALUE
