@@ -23,13 +23,17 @@ struct GemmArgs {
     size_t ws_bytes;
 };
 
-// Workspace layout (byte offsets).  The header holds the call epoch (word 0)
-// and the arrival counter (word 32) of the one-launch schedules.  Then z as
-// (fp32 value, 32-bit epoch tag) pairs [M][Rpad] for the one-launch schedules,
-// then z as plain fp32 [M][Rpad] for the two-launch schedule (a separate area,
-// so that plain floats can never be read back as tags).
-constexpr size_t kWsHeaderBytes = 256;
+// Workspace layout (byte offsets).
+//   [0, 4)            epoch of the one-launch schedules (uint32)
+//   [256, 256 + 4 G)  one "seen" flag per workgroup of a one-launch call
+//   [64 KiB, ...)     z as (fp32 value | 32-bit epoch tag << 32) pairs [M][Rpad]
+//   then              z as plain fp32 [M][Rpad] for the two-launch schedule (a
+//                     separate area, so plain floats are never read as tags)
+constexpr int kGemvMaxWorkgroups = 8192;
+constexpr size_t kWsHeaderBytes = 64 * 1024;
 inline int rpad32(int r) { return (r + 31) / 32 * 32; }
+inline size_t ws_epoch_offset() { return 0; }
+inline size_t ws_seen_offset() { return 256; }
 inline size_t ws_zt_offset() { return kWsHeaderBytes; }
 inline size_t ws_zt_bytes(int M, int r) { return (size_t)8 * (size_t)M * (size_t)rpad32(r); }
 inline size_t ws_zf_offset(int M, int r) { return ws_zt_offset() + ws_zt_bytes(M, r); }
@@ -45,6 +49,7 @@ hipError_t launch_quant_act(const uint16_t *x, int M, int K, uint8_t *codes, uin
                             hipStream_t stream);
 hipError_t launch_gemm_unfused(const GemmArgs &a, hipStream_t stream);
 hipError_t launch_gemm_fused_gemv(const GemmArgs &a, hipStream_t stream);
+hipError_t launch_gemm_gemv_two_launch(const GemmArgs &a, hipStream_t stream);
 bool gemv_supported(int M, int N, int K, int r);   // shapes the one-launch vector-ALU schedule handles
 hipError_t launch_gemm_fused_mfma(const GemmArgs &a, hipStream_t stream);
 

@@ -4,29 +4,34 @@
 // in one launch; side work computes z = alpha (.) (V x) from the packed signs of
 // V while the FP4 product streams R; z values are published with an epoch tag
 // that the output tiles poll; the epilogue expands z through U's packed signs
-// and adds it before the bf16 store.  Designed here for gfx950 and M <= 4,
+// and adds it before the bf16 store.  Designed here for gfx950 and M <= 2,
 // where the product is a matrix-vector stream bound by HBM:
 //
-//  * every wave owns whole output rows (full K), so no partial sums cross
-//    workgroups; lanes stride over the 16-element NVFP4 blocks of a row;
+//  * about one workgroup per CU streams R, 8 waves (two per SIMD), every
+//    wave owning up to R whole rows (full K), so no partial sum crosses a
+//    workgroup; lanes stride over the 16-element NVFP4 blocks of a row;
+//  * the first ceil(r/2) workgroups also produce z, 2 indices i each over
+//    all of K, with their inputs requested before their rows of R: the +-1
+//    signs of two consecutive k come out of one pair of V words as a bf16
+//    pair, so x (bf16) and the signs meet in v_dot2 (bf16) with exact
+//    products;
 //  * R is dequantised in registers: one v_cvt_scalef32_pk_f16_fp4 per code
 //    byte applies the block scale's power of two, the scale's mantissa
 //    (1 + m/8) multiplies the block's fp32 partial sum; the FP4 activation is
-//    pre-scaled once per wave into f16 registers (exact); products are
-//    v_dot2 (f16 x f16 -> fp32);
-//  * z is split over the first workgroups, 8 values of i per workgroup over
-//    all of K; the +-1 signs of two consecutive k come out of one pair of V
-//    words as a bf16 pair, so x (bf16) and the signs meet in v_dot2 (bf16)
-//    with exact products;
-//  * each z value is published as one 64-bit word (fp32 value, 32-bit epoch
-//    tag) with a relaxed device-scope store, read back with device-scope
-//    loads: no fences; a call's epoch is read at start and advanced by the
-//    last workgroup to arrive, so repeated calls never reset anything;
-//  * the correction multiplies U's signs (again as bf16 pairs) with z split
-//    into a bf16 high part and a bf16 low part (about 16 bits of z);
-//  * every wait is bounded: a consumer that has waited too long computes the
-//    z values it needs by itself, so the kernel finishes whatever else runs
-//    on the device.
+//    decoded once per workgroup into LDS (exact f16) and held in registers;
+//    the products are v_dot2 (f16 x f16 -> fp32);
+//  * each z value is published as one 64-bit word (fp32 value | epoch << 32)
+//    with a relaxed device-scope store and read back with device-scope loads:
+//    data and tag travel together, so no fence is needed;
+//  * the call's epoch is a plain load at start; every workgroup then writes a
+//    "seen" flag, and workgroup 0 advances the epoch at its end once every
+//    flag is in: no counter is hit by all workgroups;
+//  * U's words for the wave's rows are fetched at start; the correction
+//    multiplies U's signs (bf16 pairs) with z split into bf16 high and low
+//    parts (about 16 bits of z) and joins the row sum before the one
+//    reduction per row and m;
+//  * a consumer's wait for z is bounded: when it runs out the consumer
+//    computes the z values itself, so the kernel ends whatever else runs.
 #include "biloco_device.h"
 #include "biloco_internal.h"
 
@@ -38,6 +43,8 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
+constexpr int kGemvThreads = 512;   // 8 waves per workgroup
+
 struct GemvParams {
     const uint8_t *a_codes;
     const uint8_t *a_scales;
@@ -48,14 +55,16 @@ struct GemvParams {
     const uint32_t *u;
     const uint16_t *alpha;
     uint16_t *y;
-    uint64_t *hdr;          // workspace header: epoch << 32 | arrival counter
-    uint64_t *zt;           // workspace z: (value | tag << 32) [M][rpad]
+    uint32_t *epoch;        // workspace header word 0
+    uint32_t *seen;         // workspace header flags, one per workgroup
+    uint64_t *zt;           // z as (value | tag << 32), [M][rpad]  (one launch)
+    const float *zf;        // z as plain fp32 [M][rpad] from the z kernel (two launches)
+    float *zf_out;          // the same area, written by the z kernel
     float g;
     int N, K, r, rpad;
-    int rows_per_wave;
+    int rows_per_wg;
     int z_items;            // ceil(r / 8)
-    int z_wgs;              // workgroups that produce z (placed first)
-    uint32_t spin_limit;    // bounded wait on z; 0 = compute z locally at once
+    uint32_t spin_limit;    // bound of a wait on z; 0 = compute z locally at once
 };
 
 __device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float c) {
@@ -66,7 +75,7 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
                                            __builtin_bit_cast(bf16x2_t, b), c, false);
 }
-// Two FP4 codes (byte `sel` of w) -> two f16 values times 2^exponent(scale).
+// Two FP4 codes (byte SEL of w) -> two f16 values times 2^exponent(scale).
 template <int SEL>
 __device__ __forceinline__ uint32_t fp4x2_to_f16x2(uint32_t w, float scale) {
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, scale, SEL));
@@ -74,6 +83,10 @@ __device__ __forceinline__ uint32_t fp4x2_to_f16x2(uint32_t w, float scale) {
 // Sign bits at positions p and p+16 of t -> bf16 pair (+-1, +-1): bit set = -1.
 __device__ __forceinline__ uint32_t signs_bf16x2(uint32_t t, int p) {
     return ((t << (15 - p)) & 0x80008000u) | 0x3F803F80u;
+}
+// Mantissa factor (1 + m/8) of a scale's fp32 form: scale = 2^e * factor.
+__device__ __forceinline__ float scale_mant(float s) {
+    return __uint_as_float((__float_as_uint(s) & 0x007FFFFFu) | 0x3F800000u);
 }
 
 __device__ __forceinline__ uint64_t ld_tagged(const uint64_t *p) {
@@ -83,71 +96,121 @@ __device__ __forceinline__ void st_tagged(uint64_t *p, float v, uint32_t tag) {
     const uint64_t w = ((uint64_t)tag << 32) | __float_as_uint(v);
     __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ uint32_t ld_u32(const uint32_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_u32(uint32_t *p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
-// z for the 8 indices i0..i0+7 (same 32-bit word of V) and all MM rows,
-// computed by one whole workgroup over all of K and published with `tag`.
+// Sum of one value over the 8 waves of the workgroup (red: 8 floats).
+__device__ __forceinline__ float block_sum8(float v, float *red) {
+    const float s = wave_sum_dpp(v);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
+    __syncthreads();
+    const float t =
+        ((red[0] + red[1]) + (red[2] + red[3])) + ((red[4] + red[5]) + (red[6] + red[7]));
+    __syncthreads();
+    return t;
+}
+
+// z for the kZI indices i0.. (bits of one V word) and all MM rows m,
+// computed by the whole workgroup over all of K and published with the tag
+// (the call's epoch + 1).  The inputs of the first round (V words, x pairs,
+// the coefficients) are requested by z_prefetch, early; z_item consumes
+// them and runs any further rounds.
+constexpr int kZU = 8;   // pairs (k, k+1) per thread per round
+constexpr int kZI = 2;   // indices i per z item (two sign bits of one V word)
+
 template <int MM>
-__device__ void z_item(const GemvParams &p, int item, const uint32_t *s_tag, float *red) {
-    const int i0 = item * 8, w = i0 >> 5, o = i0 & 31;
+struct ZInputs {
+    uint2 vv[kZU];
+    uint32_t xp[kZU][MM];
+    uint32_t al[kZI];
+};
+
+template <int MM>
+__device__ __forceinline__ void z_load_round(const GemvParams &p, int item, int kp0,
+                                             ZInputs<MM> &in) {
+    const int w = (item * kZI) >> 5;
+    const uint32_t *vrow = p.v + (int64_t)w * p.K;
+    const int KP = p.K / 2;
+#pragma unroll
+    for (int u = 0; u < kZU; ++u) {
+        const int kp = kp0 + threadIdx.x + kGemvThreads * u, kc = kp < KP ? kp : KP - 1;
+        in.vv[u] = *reinterpret_cast<const uint2 *>(vrow + 2 * kc);
+#pragma unroll
+        for (int m = 0; m < MM; ++m)
+            in.xp[u][m] = *reinterpret_cast<const uint32_t *>(p.x + (int64_t)m * p.K + 2 * kc);
+    }
+}
+
+template <int MM>
+__device__ __forceinline__ void z_prefetch(const GemvParams &p, int item, ZInputs<MM> &in) {
+    const int i0 = item * kZI;
+#pragma unroll
+    for (int i = 0; i < kZI; ++i) {
+        const int ii = i0 + i < p.r ? i0 + i : p.r - 1;
+        in.al[i] = p.alpha[ii];
+    }
+    z_load_round<MM>(p, item, 0, in);
+}
+
+// The sign-by-x products of one z item, summed per thread.
+template <int MM>
+__device__ void z_accumulate(const GemvParams &p, int item, ZInputs<MM> &in, float (&acc)[kZI][MM]) {
+    const int i0 = item * kZI, o = i0 & 31;
     const int s = o & 15;                 // bit offset inside the 16-bit half
     const bool high = o >= 16;
-    const uint32_t *vrow = p.v + (int64_t)w * p.K;
-    float acc[8][MM];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < kZI; ++i)
 #pragma unroll
         for (int m = 0; m < MM; ++m) acc[i][m] = 0.0f;
-    // ZU pairs (k, k+1) per thread per round, all loads issued before use
-    constexpr int ZU = 16;
     const int KP = p.K / 2;
-    for (int kp0 = 0; kp0 < KP; kp0 += 256 * ZU) {
-        uint2 vv[ZU];
-        uint32_t xp[ZU][MM];
+    for (int kp0 = 0; kp0 < KP; kp0 += kGemvThreads * kZU) {
+        if (kp0 > 0) z_load_round<MM>(p, item, kp0, in);
 #pragma unroll
-        for (int u = 0; u < ZU; ++u) {
-            const int kp = kp0 + threadIdx.x + 256 * u, kc = kp < KP ? kp : KP - 1;
-            vv[u] = *reinterpret_cast<const uint2 *>(vrow + 2 * kc);
-#pragma unroll
-            for (int m = 0; m < MM; ++m)
-                xp[u][m] = *reinterpret_cast<const uint32_t *>(p.x + (int64_t)m * p.K + 2 * kc);
-        }
-#pragma unroll
-        for (int u = 0; u < ZU; ++u) {
-            const bool valid = kp0 + (int)threadIdx.x + 256 * u < KP;
+        for (int u = 0; u < kZU; ++u) {
+            const bool valid = kp0 + (int)threadIdx.x + kGemvThreads * u < KP;
             // t: the 16 sign bits of k in the low half, those of k+1 in the high half
-            const uint32_t t = high ? __builtin_amdgcn_perm(vv[u].y, vv[u].x, 0x07060302u)
-                                    : __builtin_amdgcn_perm(vv[u].y, vv[u].x, 0x05040100u);
+            const uint32_t t = high ? __builtin_amdgcn_perm(in.vv[u].y, in.vv[u].x, 0x07060302u)
+                                    : __builtin_amdgcn_perm(in.vv[u].y, in.vv[u].x, 0x05040100u);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
+            for (int i = 0; i < kZI; ++i) {
                 const uint32_t sg = signs_bf16x2(t, s + i);
 #pragma unroll
                 for (int m = 0; m < MM; ++m)
-                    acc[i][m] = dot2_bf16(sg, valid ? xp[u][m] : 0u, acc[i][m]);
+                    acc[i][m] = dot2_bf16(sg, valid ? in.xp[u][m] : 0u, acc[i][m]);
             }
         }
     }
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int m = 0; m < MM; ++m) {
-            const float v = wave_sum_dpp(acc[i][m]);
-            if (lane == 0) red[(wave * 8 + i) * MM + m] = v;
-        }
-    __syncthreads();
-    if (threadIdx.x < 8 * MM) {
-        const int i = threadIdx.x / MM, m = threadIdx.x % MM, ii = i0 + i;
-        if (ii < p.r) {
-            const float sum = (red[(0 * 8 + i) * MM + m] + red[(1 * 8 + i) * MM + m]) +
-                              (red[(2 * 8 + i) * MM + m] + red[(3 * 8 + i) * MM + m]);
-            st_tagged(p.zt + (int64_t)m * p.rpad + ii, sum * bf16_to_f32(p.alpha[ii]), *s_tag);
-        }
-    }
-    __syncthreads();
 }
 
-// Fallback: z[m][i] for one index, computed by one thread alone (slow; only
-// used after a bounded wait ran out).
+// The workgroup sums of a z item, times alpha_i, published with the call's
+// epoch + 1: all sums first, then the kZI * MM stores from as many threads,
+// with no wait behind them (a store would otherwise hold up the next wait).
+template <int MM>
+__device__ void z_publish(const GemvParams &p, int item, const ZInputs<MM> &in,
+                          float (&acc)[kZI][MM], uint32_t epoch, float *red) {
+    const int i0 = item * kZI;
+    float zs[kZI][MM];
+#pragma unroll
+    for (int i = 0; i < kZI; ++i)
+#pragma unroll
+        for (int m = 0; m < MM; ++m) zs[i][m] = block_sum8(acc[i][m], red);
+    const uint32_t tag = epoch + 1u;
+#pragma unroll
+    for (int i = 0; i < kZI; ++i)
+#pragma unroll
+        for (int m = 0; m < MM; ++m) {
+            const int ii = i0 + i;
+            if ((int)threadIdx.x == 64 * i + m && ii < p.r)
+                st_tagged(p.zt + (int64_t)m * p.rpad + ii, zs[i][m] * bf16_to_f32(in.al[i]), tag);
+        }
+}
+
+// Fallback: z[m][i] for one index, computed by one thread alone (slow; used
+// only after a bounded wait ran out).
 __device__ float z_local(const GemvParams &p, int m, int i) {
     const uint32_t *vrow = p.v + (int64_t)(i >> 5) * p.K;
     const int b = i & 31;
@@ -159,290 +222,423 @@ __device__ float z_local(const GemvParams &p, int m, int i) {
     return acc * bf16_to_f32(p.alpha[i]);
 }
 
-// Workgroups [0, z_wgs) compute z items; workgroups [z_wgs, grid) stream R.
-template <int MM, int KBL>
-__global__ void __launch_bounds__(256) fused_gemv_kernel(GemvParams p) {
-    __shared__ uint32_t s_tag;
-    __shared__ uint32_t s_last;
-    __shared__ float s_red[4 * 8 * MM];
-    __shared__ float s_G[4][64][MM];
-    extern __shared__ float s_z[];        // [MM][rpad] z values of this call
+// Rows per wave of the R stream for KBL blocks per lane and MM rows of x:
+// a register budget of about 200 VGPRs for the row buffers (3 KBL each), the
+// activation (8 KBL MM) and U's words (4 per row).
+__host__ __device__ constexpr int gemv_rows_per_wave(int kbl, int mm) {
+    return (200 - 8 * kbl * mm) / (3 * kbl + 4) >= 4 ? 4
+         : ((200 - 8 * kbl * mm) / (3 * kbl + 4) <= 1 ? 1 : (200 - 8 * kbl * mm) / (3 * kbl + 4));
+}
+
+// Correction of the wave's rows: bit pairs (pb, pb + 16), pb = lane / 16 + 4 j,
+// of the lane's U words (lane % 16) + 16 q, against z (LDS, [MM][rpad]) split
+// into bf16 high + bf16 low parts; added to the per-lane row sums.
+template <int MM, int R, int QMAX>
+__device__ __forceinline__ void add_correction(const GemvParams &p, const float *s_z,
+                                               const uint32_t (&uw)[QMAX][R],
+                                               float (&part)[R][MM]) {
+    const int lane = threadIdx.x & 63;
+    const int W = p.rpad >> 5;
+#pragma unroll
+    for (int q = 0; q < QMAX; ++q) {
+        if (16 * q >= W) break;
+        const int w = (lane & 15) + 16 * q;
+        const bool wok = w < W;
+        uint32_t zhi[4][MM], zlo[4][MM];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int pb = (lane >> 4) + 4 * j;
+#pragma unroll
+            for (int m = 0; m < MM; ++m) {
+                const int i0 = 32 * w + pb, i1 = i0 + 16;
+                const float z0 = (wok && i0 < p.r) ? s_z[m * p.rpad + i0] : 0.0f;
+                const float z1 = (wok && i1 < p.r) ? s_z[m * p.rpad + i1] : 0.0f;
+                const uint32_t h0 = __float_as_uint(z0) & 0xFFFF0000u;
+                const uint32_t h1 = __float_as_uint(z1) & 0xFFFF0000u;
+                const uint32_t l0 = __float_as_uint(z0 - __uint_as_float(h0));
+                const uint32_t l1 = __float_as_uint(z1 - __uint_as_float(h1));
+                zhi[j][m] = (h0 >> 16) | h1;
+                zlo[j][m] = (l0 >> 16) | (l1 & 0xFFFF0000u);
+            }
+        }
+#pragma unroll
+        for (int rr = 0; rr < R; ++rr) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t sg = signs_bf16x2(uw[q][rr], (lane >> 4) + 4 * j);
+#pragma unroll
+                for (int m = 0; m < MM; ++m) {
+                    part[rr][m] = dot2_bf16(sg, zhi[j][m], part[rr][m]);
+                    part[rr][m] = dot2_bf16(sg, zlo[j][m], part[rr][m]);
+                }
+            }
+        }
+    }
+}
+
+// ZMODE 0: no correction (r == 0); 1: z produced in this launch by the first
+// workgroups and polled through epoch tags; 2: z complete in the workspace
+// (written by z_kernel earlier on the same stream).
+template <int MM, int KBL, int ZMODE>
+__global__ void __launch_bounds__(kGemvThreads) fused_gemv_kernel(GemvParams p) {
+    constexpr int R = gemv_rows_per_wave(KBL, MM);
+    constexpr bool has_z = ZMODE != 0;
+    constexpr int QMAX = 2;                    // r <= 1024: two rounds of 16 words
+    constexpr int ZP = 2 * MM;                 // z values per thread (MM * r <= MM * 1024)
+    constexpr int AMAX = (MM * KBL * 64 + kGemvThreads - 1) / kGemvThreads;  // blocks per thread
+    __shared__ float s_red[8];
+    __shared__ uint32_t s_bcast;
+    extern __shared__ uint32_t s_dyn[];   // activation f16 pairs [MM][KB][8], then z [MM][rpad]
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int KB = p.K >> 4, KH = p.K >> 1;
+    uint32_t *s_act = s_dyn;
+    float *s_z = reinterpret_cast<float *>(s_dyn + (size_t)MM * KB * 8);
 
-    // one 64-bit fetch-add returns (epoch << 32 | arrivals so far); its value
-    // is first needed after the stream has been issued
-    uint64_t hv = 0;
-    if (threadIdx.x == 0 && p.hdr)
-        hv = __hip_atomic_fetch_add(p.hdr, (uint64_t)1, __ATOMIC_RELAXED,
-                                    __HIP_MEMORY_SCOPE_AGENT);
+    // the call's epoch (one launch): a plain device-scope load by every thread
+    const uint32_t ep = ZMODE == 1 ? ld_u32(p.epoch) : 0u;
 
-    if ((int)blockIdx.x < p.z_wgs) {
-        // ------------------------------------------------ z producer
-        if (threadIdx.x == 0) {
-            s_tag = (uint32_t)(hv >> 32) + 1u;
-            s_last = (uint32_t)hv == gridDim.x - 1;
+    // rows of this workgroup, spread over its 8 waves (the first get one more)
+    const int wg_row0 = blockIdx.x * p.rows_per_wg;
+    int wg_rows = p.N - wg_row0;
+    wg_rows = wg_rows < 0 ? 0 : (wg_rows > p.rows_per_wg ? p.rows_per_wg : wg_rows);
+    const int base = wg_rows >> 3, extra = wg_rows & 7;
+    const int nrows = base + (wave < extra ? 1 : 0);
+    const int row0 = wg_row0 + wave * base + (wave < extra ? wave : extra);
+
+    // ---- small inputs first.  Requested behind the stream of R, scattered
+    // reads come back only once the stream has drained; requested first, they
+    // are in hand before any row of R is asked for.
+    // 1. the FP4 activation blocks this thread decodes (clamped addresses)
+    const int nact = MM * KB;
+    uint2 ac[AMAX];
+    uint32_t asb[AMAX];
+#pragma unroll
+    for (int a = 0; a < AMAX; ++a) {
+        const int ai = threadIdx.x + kGemvThreads * a, aic = ai < nact ? ai : nact - 1;
+        const int m = aic / KB, b = aic - m * KB;
+        ac[a] = *reinterpret_cast<const uint2 *>(p.a_codes + (int64_t)m * KH + b * 8);
+        asb[a] = p.a_scales[(int64_t)m * KB + b];
+    }
+    // 2. a z item's inputs (one launch) or the finished z (two launches)
+    const bool z_wg = ZMODE == 1 && (int)blockIdx.x < p.z_items;
+    ZInputs<MM> zin;
+    if (z_wg) z_prefetch<MM>(p, blockIdx.x, zin);
+    const int nz = MM * p.r;
+    float zpre[ZP];
+    if (ZMODE == 2) {
+#pragma unroll
+        for (int j = 0; j < ZP; ++j) {
+            const int idx = threadIdx.x + kGemvThreads * j;
+            const int ic = idx < nz ? idx : nz - 1;
+            const int m = ic / p.r, i = ic - m * p.r;
+            zpre[j] = p.zf[(int64_t)m * p.rpad + i];
         }
-        __syncthreads();
-        for (int it = blockIdx.x; it < p.z_items; it += p.z_wgs) z_item<MM>(p, it, &s_tag, s_red);
-    } else {
-        // ------------------------------------------------ R stream
-        const int gwave = (blockIdx.x - p.z_wgs) * 4 + wave;
-        const int row0 = gwave * p.rows_per_wave;
-        int nrows = p.N - row0;
-        nrows = nrows < 0 ? 0 : (nrows > p.rows_per_wave ? p.rows_per_wave : nrows);
+    }
+    // 3. U's words for these rows: lane covers word (lane % 16) + 16 q
+    const int W = p.rpad >> 5;
+    uint32_t uw[QMAX][R];
+#pragma unroll
+    for (int q = 0; q < QMAX; ++q)
+#pragma unroll
+        for (int rr = 0; rr < R; ++rr) {
+            uw[q][rr] = 0u;
+            if (has_z && 16 * q < W && rr < nrows) {
+                int w = (lane & 15) + 16 * q;
+                w = w < W ? w : W - 1;
+                uw[q][rr] = p.u[(int64_t)w * p.N + row0 + rr];
+            }
+        }
+    __builtin_amdgcn_sched_barrier(0);
 
-        // activation loads first (they are waited on first), pre-scaled to
-        // f16 pairs: act[t][m][d] holds elements 2d, 2d+1 of block lane + 64t
-        uint2 ac[KBL][MM];
-        uint32_t asb[KBL][MM];
+    // 4. decode the activation into LDS: [m][block][8 f16 pairs], exact values;
+    // z (two launches) into its own LDS area
+#pragma unroll
+    for (int a = 0; a < AMAX; ++a) {
+        const int ai = threadIdx.x + kGemvThreads * a;
+        if (ai < nact) {
+            const float sa = __builtin_amdgcn_cvt_f32_fp8(asb[a], 0);
+            const _Float16 mh = (_Float16)scale_mant(sa);
+            const half2_t mm2 = {mh, mh};
+            const uint32_t raw[8] = {
+                fp4x2_to_f16x2<0>(ac[a].x, sa), fp4x2_to_f16x2<1>(ac[a].x, sa),
+                fp4x2_to_f16x2<2>(ac[a].x, sa), fp4x2_to_f16x2<3>(ac[a].x, sa),
+                fp4x2_to_f16x2<0>(ac[a].y, sa), fp4x2_to_f16x2<1>(ac[a].y, sa),
+                fp4x2_to_f16x2<2>(ac[a].y, sa), fp4x2_to_f16x2<3>(ac[a].y, sa)};
+            uint32_t o[8];
+#pragma unroll
+            for (int d = 0; d < 8; ++d)
+                o[d] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, raw[d]) * mm2);
+            uint4 *dst = reinterpret_cast<uint4 *>(s_act + (size_t)ai * 8);
+            dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+            dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+        }
+    }
+    if (ZMODE == 2) {
+#pragma unroll
+        for (int j = 0; j < ZP; ++j) {
+            const int idx = threadIdx.x + kGemvThreads * j;
+            if (idx < nz) {
+                const int m = idx / p.r, i = idx - m * p.r;
+                s_z[m * p.rpad + i] = zpre[j];
+            }
+        }
+    }
+    __syncthreads();
+    uint32_t act[KBL][MM][8];
+#pragma unroll
+    for (int t = 0; t < KBL; ++t) {
+        const int b = lane + 64 * t, bc = b < KB ? b : KB - 1;
+#pragma unroll
+        for (int m = 0; m < MM; ++m) {
+            const uint4 *src = reinterpret_cast<const uint4 *>(s_act + ((size_t)m * KB + bc) * 8);
+            const uint4 lo = src[0], hi = src[1];
+            act[t][m][0] = lo.x; act[t][m][1] = lo.y; act[t][m][2] = lo.z; act[t][m][3] = lo.w;
+            act[t][m][4] = hi.x; act[t][m][5] = hi.y; act[t][m][6] = hi.z; act[t][m][7] = hi.w;
+        }
+    }
+
+    // 5. one launch: a z item is computed and published before the rows of R
+    // are requested, so that z is out long before any workgroup needs it;
+    // every other workgroup records that it has read the epoch
+    if (ZMODE == 1) {
+        if (z_wg) {
+            float zacc[kZI][MM];
+            z_accumulate<MM>(p, blockIdx.x, zin, zacc);
+            z_publish<MM>(p, blockIdx.x, zin, zacc, ep, s_red);
+            for (int it = blockIdx.x + gridDim.x; it < p.z_items; it += gridDim.x) {
+                z_prefetch<MM>(p, it, zin);
+                z_accumulate<MM>(p, it, zin, zacc);
+                z_publish<MM>(p, it, zin, zacc, ep, s_red);
+            }
+        }
+        if (threadIdx.x == 0 && blockIdx.x > 0) st_u32(p.seen + blockIdx.x, ep + 1u);
+    }
+
+    // 6. the rows of R
+    u32x2_t codes[R][KBL];
+    uint32_t sc[R][KBL];
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) {
+        if (rr >= nrows) continue;
+        const int n = row0 + rr;
 #pragma unroll
         for (int t = 0; t < KBL; ++t) {
+            // blocks past the row end load a valid block; they are zeroed at use
             const int b = lane + 64 * t, bc = b < KB ? b : KB - 1;
-#pragma unroll
-            for (int m = 0; m < MM; ++m) {
-                ac[t][m] = *reinterpret_cast<const uint2 *>(p.a_codes + (int64_t)m * KH + bc * 8);
-                asb[t][m] = p.a_scales[(int64_t)m * KB + bc];
-            }
+            codes[rr][t] = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x2_t *>(p.w_codes + (int64_t)n * KH + bc * 8));
+            sc[rr][t] = __builtin_nontemporal_load(p.w_scales + (int64_t)n * KB + bc);
         }
-        // R rows stream through a ring of PD row buffers
-        constexpr int PD = (40 / KBL) < 2 ? 2 : ((40 / KBL) > 8 ? 8 : (40 / KBL));
-        u32x2_t codes[PD][KBL];
-        uint32_t sc[PD][KBL];
-#pragma unroll
-        for (int sl = 0; sl < PD; ++sl) {
-            if (sl < nrows) {
-                const int64_t n = row0 + sl;
-#pragma unroll
-                for (int t = 0; t < KBL; ++t) {
-                    const int b = lane + 64 * t, bc = b < KB ? b : KB - 1;
-                    codes[sl][t] = __builtin_nontemporal_load(
-                        reinterpret_cast<const u32x2_t *>(p.w_codes + n * KH + bc * 8));
-                    sc[sl][t] = __builtin_nontemporal_load(p.w_scales + n * KB + bc);
-                }
-            }
-        }
-        uint32_t act[KBL][MM][8];
-#pragma unroll
-        for (int t = 0; t < KBL; ++t) {
-            const bool valid = lane + 64 * t < KB;
-#pragma unroll
-            for (int m = 0; m < MM; ++m) {
-                const uint32_t cx = valid ? ac[t][m].x : 0u, cy = valid ? ac[t][m].y : 0u;
-                const float sa = __builtin_amdgcn_cvt_f32_fp8(asb[t][m], 0);
-                const uint32_t mant = (__float_as_uint(sa) & 0x007FFFFFu) | 0x3F800000u;
-                const _Float16 mh = (_Float16)__uint_as_float(mant);
-                const half2_t mm2 = {mh, mh};
-                const uint32_t raw[8] = {fp4x2_to_f16x2<0>(cx, sa), fp4x2_to_f16x2<1>(cx, sa),
-                                         fp4x2_to_f16x2<2>(cx, sa), fp4x2_to_f16x2<3>(cx, sa),
-                                         fp4x2_to_f16x2<0>(cy, sa), fp4x2_to_f16x2<1>(cy, sa),
-                                         fp4x2_to_f16x2<2>(cy, sa), fp4x2_to_f16x2<3>(cy, sa)};
-#pragma unroll
-                for (int d = 0; d < 8; ++d)
-                    act[t][m][d] =
-                        __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, raw[d]) * mm2);
-            }
-        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
 
-        for (int base = 0; base < nrows; base += PD) {
-            float part[PD][MM];
+    // 7. two launches: the correction while the rows stream in
+    float part[R][MM];
 #pragma unroll
-            for (int sl = 0; sl < PD; ++sl) {
-                const int rr = base + sl;
+    for (int rr = 0; rr < R; ++rr)
 #pragma unroll
-                for (int m = 0; m < MM; ++m) part[sl][m] = 0.0f;
-                if (rr < nrows) {
+        for (int m = 0; m < MM; ++m) part[rr][m] = 0.0f;
+    if (ZMODE == 2) add_correction<MM, R, QMAX>(p, s_z, uw, part);
+
+    // 8. the FP4 product of every row, times g, onto the per-lane sums
 #pragma unroll
-                    for (int t = 0; t < KBL; ++t) {
-                        const bool valid = lane + 64 * t < KB;
-                        const float sw = __builtin_amdgcn_cvt_f32_fp8(sc[sl][t], 0);
-                        const float mant = __uint_as_float(
-                            (__float_as_uint(sw) & 0x007FFFFFu) | 0x3F800000u);
-                        const uint32_t c0 = valid ? codes[sl][t].x : 0u;
-                        const uint32_t c1 = valid ? codes[sl][t].y : 0u;
-                        const uint32_t wv[8] = {
-                            fp4x2_to_f16x2<0>(c0, sw), fp4x2_to_f16x2<1>(c0, sw),
-                            fp4x2_to_f16x2<2>(c0, sw), fp4x2_to_f16x2<3>(c0, sw),
-                            fp4x2_to_f16x2<0>(c1, sw), fp4x2_to_f16x2<1>(c1, sw),
-                            fp4x2_to_f16x2<2>(c1, sw), fp4x2_to_f16x2<3>(c1, sw)};
+    for (int rr = 0; rr < R; ++rr) {
+        if (rr < nrows) {
+            float gacc[MM];
 #pragma unroll
-                        for (int m = 0; m < MM; ++m) {
-                            float bl = 0.0f;
+            for (int m = 0; m < MM; ++m) gacc[m] = 0.0f;
 #pragma unroll
-                            for (int d = 0; d < 8; ++d) bl = dot2_f16(wv[d], act[t][m][d], bl);
-                            part[sl][m] = __builtin_fmaf(bl, mant, part[sl][m]);
-                        }
-                    }
-                    // refill this slot with the row PD ahead
-                    if (rr + PD < nrows) {
-                        const int64_t n = row0 + rr + PD;
-#pragma unroll
-                        for (int t = 0; t < KBL; ++t) {
-                            const int b = lane + 64 * t, bc = b < KB ? b : KB - 1;
-                            codes[sl][t] = __builtin_nontemporal_load(
-                                reinterpret_cast<const u32x2_t *>(p.w_codes + n * KH + bc * 8));
-                            sc[sl][t] = __builtin_nontemporal_load(p.w_scales + n * KB + bc);
-                        }
-                    }
-                }
-            }
-            // the PD row sums of this ring cycle, reduced together
-#pragma unroll
-            for (int sl = 0; sl < PD; ++sl)
+            for (int t = 0; t < KBL; ++t) {
+                const bool valid = lane + 64 * t < KB;
+                const float sw = __builtin_amdgcn_cvt_f32_fp8(sc[rr][t], 0);
+                const float mant = scale_mant(sw);
+                const uint32_t c0 = valid ? codes[rr][t].x : 0u;
+                const uint32_t c1 = valid ? codes[rr][t].y : 0u;
+                const uint32_t wv[8] = {
+                    fp4x2_to_f16x2<0>(c0, sw), fp4x2_to_f16x2<1>(c0, sw),
+                    fp4x2_to_f16x2<2>(c0, sw), fp4x2_to_f16x2<3>(c0, sw),
+                    fp4x2_to_f16x2<0>(c1, sw), fp4x2_to_f16x2<1>(c1, sw),
+                    fp4x2_to_f16x2<2>(c1, sw), fp4x2_to_f16x2<3>(c1, sw)};
 #pragma unroll
                 for (int m = 0; m < MM; ++m) {
-                    const float sum = wave_sum_dpp(part[sl][m]);
-                    if (lane == 0 && base + sl < nrows) s_G[wave][base + sl][m] = p.g * sum;
-                }
-        }
-
-        // ------------------------------------------------ z acquire
-        if (threadIdx.x == 0) {
-            s_tag = (uint32_t)(hv >> 32) + 1u;
-            s_last = (uint32_t)hv == gridDim.x - 1;
-        }
-        __syncthreads();
-        const uint32_t tag = s_tag;
-        for (int idx = threadIdx.x; idx < MM * p.r; idx += 256) {
-            const int m = idx / p.r, i = idx - m * p.r;
-            const uint64_t *src = p.zt + (int64_t)m * p.rpad + i;
-            uint64_t a = ld_tagged(src);
-            uint32_t spins = 0;
-            while ((uint32_t)(a >> 32) != tag && spins < p.spin_limit) {
-                __builtin_amdgcn_s_sleep(1);
-                a = ld_tagged(src);
-                ++spins;
-            }
-            s_z[m * p.rpad + i] = (uint32_t)(a >> 32) == tag ? __uint_as_float((uint32_t)a)
-                                                             : z_local(p, m, i);
-        }
-        __syncthreads();
-
-        // ------------------------------------------------ correction + store
-        // lane covers word (lane % 16) + 16 q and bit pairs (pb, pb + 16),
-        // pb = lane / 16 + 4 j, j = 0..3; z as bf16 high + bf16 low parts
-        const int W = p.rpad >> 5;
-        for (int q = 0; q * 16 < W; ++q) {
-            const int w = (lane & 15) + 16 * q;
-            const bool wok = w < W;
-            uint32_t zhi[4][MM], zlo[4][MM];
+                    float bl = 0.0f;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int pb = (lane >> 4) + 4 * j;
-#pragma unroll
-                for (int m = 0; m < MM; ++m) {
-                    const int i0 = 32 * w + pb, i1 = i0 + 16;
-                    const float z0 = (wok && i0 < p.r) ? s_z[m * p.rpad + i0] : 0.0f;
-                    const float z1 = (wok && i1 < p.r) ? s_z[m * p.rpad + i1] : 0.0f;
-                    const uint32_t h0 = __float_as_uint(z0) & 0xFFFF0000u;
-                    const uint32_t h1 = __float_as_uint(z1) & 0xFFFF0000u;
-                    const uint32_t l0 = __float_as_uint(z0 - __uint_as_float(h0));
-                    const uint32_t l1 = __float_as_uint(z1 - __uint_as_float(h1));
-                    zhi[j][m] = (h0 >> 16) | h1;
-                    zlo[j][m] = (l0 >> 16) | (l1 & 0xFFFF0000u);
+                    for (int d = 0; d < 8; ++d) bl = dot2_f16(wv[d], act[t][m][d], bl);
+                    gacc[m] = __builtin_fmaf(bl, mant, gacc[m]);
                 }
             }
-            for (int base = 0; base < nrows; base += 8) {
-                uint32_t uw[8];
 #pragma unroll
-                for (int sl = 0; sl < 8; ++sl) {
-                    const int rr = base + sl < nrows ? base + sl : nrows - 1;
-                    uw[sl] = wok ? p.u[(int64_t)w * p.N + row0 + rr] : 0u;
-                }
-                float c[8][MM];
-#pragma unroll
-                for (int sl = 0; sl < 8; ++sl)
-#pragma unroll
-                    for (int m = 0; m < MM; ++m) c[sl][m] = 0.0f;
-#pragma unroll
-                for (int sl = 0; sl < 8; ++sl)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const uint32_t sg = signs_bf16x2(uw[sl], (lane >> 4) + 4 * j);
-#pragma unroll
-                        for (int m = 0; m < MM; ++m) {
-                            c[sl][m] = dot2_bf16(sg, zhi[j][m], c[sl][m]);
-                            c[sl][m] = dot2_bf16(sg, zlo[j][m], c[sl][m]);
-                        }
-                    }
-#pragma unroll
-                for (int sl = 0; sl < 8; ++sl)
-#pragma unroll
-                    for (int m = 0; m < MM; ++m) {
-                        const float cs = wave_sum_dpp(c[sl][m]);
-                        if (lane == 0 && base + sl < nrows) s_G[wave][base + sl][m] += cs;
-                    }
-            }
-        }
-        if (lane == 0) {
-            for (int rr = 0; rr < nrows; ++rr)
-#pragma unroll
-                for (int m = 0; m < MM; ++m)
-                    p.y[(int64_t)m * p.N + row0 + rr] = f32_to_bf16_rne(s_G[wave][rr][m]);
+            for (int m = 0; m < MM; ++m) part[rr][m] = __builtin_fmaf(p.g, gacc[m], part[rr][m]);
         }
     }
 
-    // last workgroup to arrive: every workgroup has taken this call's epoch,
-    // so the next call may start from epoch + 1 with the counter at zero
-    if (threadIdx.x == 0 && p.hdr && (uint32_t)hv == gridDim.x - 1) {
-        const uint64_t next = ((hv >> 32) + 1u) << 32;
-        __hip_atomic_store(p.hdr, next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // 9. one launch: z of this call into LDS (every thread requests its z
+    // words at once, then re-reads the ones not yet published, bounded), then
+    // the correction
+    if (ZMODE == 1) {
+        if (threadIdx.x == 0) s_bcast = ep;
+        __syncthreads();
+        const uint32_t tag = s_bcast + 1u;
+        uint64_t zv[ZP];
+#pragma unroll
+        for (int j = 0; j < ZP; ++j) {
+            const int idx = threadIdx.x + kGemvThreads * j;
+            const int ic = idx < nz ? idx : nz - 1;
+            const int m = ic / p.r, i = ic - m * p.r;
+            zv[j] = ld_tagged(p.zt + (int64_t)m * p.rpad + i);
+        }
+#pragma unroll
+        for (int j = 0; j < ZP; ++j) {
+            const int idx = threadIdx.x + kGemvThreads * j;
+            if (idx < nz) {
+                const int m = idx / p.r, i = idx - m * p.r;
+                const uint64_t *src = p.zt + (int64_t)m * p.rpad + i;
+                uint64_t a = zv[j];
+                uint32_t spins = 0;
+                while ((uint32_t)(a >> 32) != tag && spins < p.spin_limit) {
+                    __builtin_amdgcn_s_sleep(1);
+                    a = ld_tagged(src);
+                    ++spins;
+                }
+                s_z[m * p.rpad + i] = (uint32_t)(a >> 32) == tag ? __uint_as_float((uint32_t)a)
+                                                                 : z_local(p, m, i);
+            }
+        }
+        __syncthreads();
+        add_correction<MM, R, QMAX>(p, s_z, uw, part);
     }
+
+    // 10. one reduction per row and m, then the bf16 store
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+        for (int m = 0; m < MM; ++m) {
+            const float sum = wave_sum_dpp(part[rr][m]);
+            if (lane == 0 && rr < nrows)
+                p.y[(int64_t)m * p.N + row0 + rr] = f32_to_bf16_rne(sum);
+        }
+
+    // 11. one launch: workgroup 0 advances the epoch once every other
+    // workgroup has read it (its flag shows epoch + 1); the next call then
+    // starts from epoch + 1
+    if (ZMODE == 1 && blockIdx.x == 0) {
+        for (int j = 1 + threadIdx.x; j < (int)gridDim.x; j += kGemvThreads)
+            while (ld_u32(p.seen + j) != ep + 1u) __builtin_amdgcn_s_sleep(2);
+        __syncthreads();
+        if (threadIdx.x == 0) st_u32(p.epoch, ep + 1u);
+    }
+}
+
+// z of the two-launch schedule: one workgroup per z item (kZI indices i over
+// all of K), plain fp32 stores; the product kernel that follows on the same
+// stream reads z complete.
+template <int MM>
+__global__ void __launch_bounds__(kGemvThreads) z_kernel(GemvParams p) {
+    __shared__ float s_red[8];
+    ZInputs<MM> zin;
+    z_prefetch<MM>(p, blockIdx.x, zin);
+    float acc[kZI][MM];
+    z_accumulate<MM>(p, blockIdx.x, zin, acc);
+    const int i0 = blockIdx.x * kZI;
+    float zs[kZI][MM];
+#pragma unroll
+    for (int i = 0; i < kZI; ++i)
+#pragma unroll
+        for (int m = 0; m < MM; ++m) zs[i][m] = block_sum8(acc[i][m], s_red);
+#pragma unroll
+    for (int i = 0; i < kZI; ++i)
+#pragma unroll
+        for (int m = 0; m < MM; ++m) {
+            const int ii = i0 + i;
+            if ((int)threadIdx.x == 64 * i + m && ii < p.r)
+                p.zf_out[(int64_t)m * p.rpad + ii] = zs[i][m] * bf16_to_f32(zin.al[i]);
+        }
 }
 
 namespace {
-template <int MM, int KBL>
-hipError_t launch_t(const GemvParams &p, int grid, hipStream_t stream) {
-    const size_t lds = (size_t)MM * (size_t)(p.rpad > 0 ? p.rpad : 1) * sizeof(float);
-    hipLaunchKernelGGL((fused_gemv_kernel<MM, KBL>), dim3(grid), dim3(256), lds, stream, p);
+size_t gemv_lds_bytes(int M, int K, int rpad) {
+    return (size_t)M * (size_t)(K / 16) * 32 + (size_t)M * (size_t)rpad * 4;
+}
+
+template <int MM, int KBL, int ZMODE>
+hipError_t launch_t(const GemvParams &p, int grid, size_t lds, hipStream_t stream) {
+    hipLaunchKernelGGL((fused_gemv_kernel<MM, KBL, ZMODE>), dim3(grid), dim3(kGemvThreads), lds,
+                       stream, p);
     return hipGetLastError();
 }
 
-template <int MM>
-hipError_t launch_m(const GemvParams &p, int kbl, int grid, hipStream_t stream) {
+template <int MM, int ZMODE>
+hipError_t launch_mz(const GemvParams &p, int kbl, int grid, size_t lds, hipStream_t stream) {
     switch (kbl) {
-        case 1: return launch_t<MM, 1>(p, grid, stream);
-        case 2: return launch_t<MM, 2>(p, grid, stream);
-        case 3: return launch_t<MM, 3>(p, grid, stream);
-        case 4: return launch_t<MM, 4>(p, grid, stream);
-        case 5: if (MM <= 3) return launch_t<MM <= 3 ? MM : 1, 5>(p, grid, stream); break;
-        case 6: if (MM <= 2) return launch_t<MM <= 2 ? MM : 1, 6>(p, grid, stream); break;
+        case 1: return launch_t<MM, 1, ZMODE>(p, grid, lds, stream);
+        case 2: return launch_t<MM, 2, ZMODE>(p, grid, lds, stream);
+        case 3: return launch_t<MM, 3, ZMODE>(p, grid, lds, stream);
+        case 4: return launch_t<MM, 4, ZMODE>(p, grid, lds, stream);
+        case 5: return launch_t<MM, 5, ZMODE>(p, grid, lds, stream);
+        case 6: return launch_t<MM, 6, ZMODE>(p, grid, lds, stream);
         case 7:
-        case 8: if (MM <= 2) return launch_t<MM <= 2 ? MM : 1, 8>(p, grid, stream); break;
+        case 8: return launch_t<MM, 8, ZMODE>(p, grid, lds, stream);
         case 9:
         case 10:
         case 11:
-        case 12: if (MM == 1) return launch_t<1, 12>(p, grid, stream); break;
+        case 12: if (MM == 1) return launch_t<1, 12, ZMODE>(p, grid, lds, stream); break;
         case 13:
         case 14:
         case 15:
-        case 16: if (MM == 1) return launch_t<1, 16>(p, grid, stream); break;
+        case 16: if (MM == 1) return launch_t<1, 16, ZMODE>(p, grid, lds, stream); break;
         default: break;
     }
     return hipErrorNotSupported;
 }
 
+template <int MM>
+hipError_t launch_m(const GemvParams &p, int kbl, int grid, size_t lds, int zmode,
+                    hipStream_t stream) {
+    switch (zmode) {
+        case 0: return launch_mz<MM, 0>(p, kbl, grid, lds, stream);
+        case 1: return launch_mz<MM, 1>(p, kbl, grid, lds, stream);
+        default: return launch_mz<MM, 2>(p, kbl, grid, lds, stream);
+    }
+}
+
 uint32_t spin_limit_default() {
-    // a debug override (BILOCO_DEBUG_SPIN_LIMIT) shortens the bounded wait on
-    // z so that tests can force the self-computing fallback
+    // debug override (BILOCO_DEBUG_SPIN_LIMIT): shortens the bounded wait on z
+    // so that tests can force the self-computing fallback
     const char *s = getenv("BILOCO_DEBUG_SPIN_LIMIT");
     return s ? (uint32_t)strtoul(s, nullptr, 10) : (uint32_t)(1u << 20);
 }
-}  // namespace
 
-int gemv_rows_per_wave(int N) { return (N + 1023) / 1024; }
-
-bool gemv_supported(int M, int N, int K, int r) {
-    const int kbl = (K / 16 + 63) / 64;
-    if (M < 1 || M > 4 || r > 2048 || gemv_rows_per_wave(N) > 64) return false;
-    if (M == 1) return kbl <= 16;
-    if (M == 2) return kbl <= 8;
-    if (M == 3) return kbl <= 5;
-    return kbl <= 4;
+int kbl_of(int K) { return (K / 16 + 63) / 64; }
+// the instantiated KBL a K runs with (see launch_m)
+int kbl_launch(int kbl) {
+    return kbl <= 6 ? kbl : (kbl <= 8 ? 8 : (kbl <= 12 ? 12 : 16));
 }
 
-hipError_t launch_gemm_fused_gemv(const GemmArgs &a, hipStream_t stream) {
+// Stream workgroups and rows per workgroup: about one workgroup per CU while
+// its rows fit the waves' register budget, more workgroups beyond that.
+void gemv_grid(int N, int kbl, int mm, int *wgs, int *rows_per_wg) {
+    const int cap = 8 * gemv_rows_per_wave(kbl, mm);
+    int rpg = (N + 255) / 256;
+    if (rpg > cap) rpg = cap;
+    *rows_per_wg = rpg;
+    *wgs = (N + rpg - 1) / rpg;
+}
+}  // namespace
+
+bool gemv_supported(int M, int N, int K, int r) {
+    const int kbl = kbl_of(K);
+    if (M < 1 || M > 2 || r < 0 || r > 1024 || N < 1) return false;
+    if (M * (K / 16) > 4 * kGemvThreads) return false;
+    if (gemv_lds_bytes(M, K, rpad32(r)) > 64 * 1024) return false;
+    int wgs, rpg;
+    gemv_grid(N, kbl_launch(kbl), M, &wgs, &rpg);
+    if (wgs > kGemvMaxWorkgroups) return false;
+    return M == 1 ? kbl <= 16 : kbl <= 8;
+}
+
+namespace {
+hipError_t launch_gemv(const GemmArgs &a, bool two_launch, hipStream_t stream) {
     if (!gemv_supported(a.M, a.N, a.K, a.r)) return hipErrorNotSupported;
     GemvParams p{};
     p.a_codes = a.a_codes;
@@ -459,26 +655,50 @@ hipError_t launch_gemm_fused_gemv(const GemmArgs &a, hipStream_t stream) {
     p.K = a.K;
     p.r = a.r;
     p.rpad = rpad32(a.r);
-    // rows per wave: aim at ~1024 streaming waves (one per SIMD)
-    p.rows_per_wave = gemv_rows_per_wave(a.N);
-    const int waves = (a.N + p.rows_per_wave - 1) / p.rows_per_wave;
-    const int gemm_wgs = (waves + 3) / 4;
-    p.z_items = (a.r + 7) / 8;
-    p.z_wgs = p.z_items;
-    p.hdr = a.r > 0 ? reinterpret_cast<uint64_t *>(a.ws) : nullptr;
-    p.zt = a.r > 0 ? reinterpret_cast<uint64_t *>(static_cast<char *>(a.ws) + ws_zt_offset())
-                   : nullptr;
+    const int kbl = kbl_of(a.K);
+    int swgs = 0;
+    gemv_grid(a.N, kbl_launch(kbl), a.M, &swgs, &p.rows_per_wg);
+    p.z_items = (a.r + kZI - 1) / kZI;
+    int zmode = 0;
+    if (a.r > 0) {
+        char *ws = static_cast<char *>(a.ws);
+        p.epoch = reinterpret_cast<uint32_t *>(ws + ws_epoch_offset());
+        p.seen = reinterpret_cast<uint32_t *>(ws + ws_seen_offset());
+        p.zt = reinterpret_cast<uint64_t *>(ws + ws_zt_offset());
+        p.zf_out = reinterpret_cast<float *>(ws + ws_zf_offset(a.M, a.r));
+        p.zf = p.zf_out;
+        zmode = two_launch ? 2 : 1;
+    } else {
+        // no correction: the kernel still reads one epoch word and one U word
+        // per lane (results unused); point both at the first bytes of R
+        p.epoch = reinterpret_cast<uint32_t *>(const_cast<uint8_t *>(a.w_codes));
+        p.u = reinterpret_cast<const uint32_t *>(a.w_codes);
+    }
     static const uint32_t spin = spin_limit_default();
     p.spin_limit = spin;
-    const int grid = p.z_wgs + gemm_wgs;
-    const int kbl = (a.K / 16 + 63) / 64;
+    if (zmode == 2) {
+        if (a.M == 1)
+            hipLaunchKernelGGL(z_kernel<1>, dim3(p.z_items), dim3(kGemvThreads), 0, stream, p);
+        else
+            hipLaunchKernelGGL(z_kernel<2>, dim3(p.z_items), dim3(kGemvThreads), 0, stream, p);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const size_t lds = gemv_lds_bytes(a.M, a.K, p.rpad);
     switch (a.M) {
-        case 1: return launch_m<1>(p, kbl, grid, stream);
-        case 2: return launch_m<2>(p, kbl, grid, stream);
-        case 3: return launch_m<3>(p, kbl, grid, stream);
-        case 4: return launch_m<4>(p, kbl, grid, stream);
+        case 1: return launch_m<1>(p, kbl, swgs, lds, zmode, stream);
+        case 2: return launch_m<2>(p, kbl, swgs, lds, zmode, stream);
         default: return hipErrorNotSupported;
     }
+}
+}  // namespace
+
+hipError_t launch_gemm_fused_gemv(const GemmArgs &a, hipStream_t stream) {
+    return launch_gemv(a, false, stream);
+}
+
+hipError_t launch_gemm_gemv_two_launch(const GemmArgs &a, hipStream_t stream) {
+    return launch_gemv(a, true, stream);
 }
 
 }  // namespace biloco

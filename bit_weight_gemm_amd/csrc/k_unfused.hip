@@ -92,6 +92,9 @@ gemv_unfused_kernel(const uint8_t *__restrict__ a_codes, const uint8_t *__restri
 }
 
 hipError_t launch_gemm_unfused(const GemmArgs &a, hipStream_t stream) {
+    // small batches: the z kernel and the streaming product kernel of the
+    // vector-ALU path
+    if (gemv_supported(a.M, a.N, a.K, a.r)) return launch_gemm_gemv_two_launch(a, stream);
     const int rpad = rpad32(a.r);
     float *z = a.r > 0 ? reinterpret_cast<float *>(static_cast<char *>(a.ws) + ws_zf_offset(a.M, a.r))
                        : nullptr;
