@@ -1,0 +1,278 @@
+#!/usr/bin/env python3
+"""Benchmark of the decode hot path on one MI355X: activation FP4 quantisation
+followed by the fused NVFP4 + binary low-rank product (libbiloco_hip).
+
+One step = biloco_quant_act_fp4 + biloco_gemm_lowrank on one batch of seeded
+synthetic decode inputs (weights resident in HBM).  K steps are captured in a
+HIP graph, each on a different copy of the weights (R codes, R scales, U, V)
+so that together they span >= 1.2 GB and the 256 MB Infinity Cache cannot
+serve them; the timed region replays the graph once between synchronisations.
+
+Prints ONE JSON line (see the keys below).  --gpus must be 1.
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, 10^9 B/s
+ROT_BYTES = 1.2e9              # distinct weight bytes a timed graph walks through
+METRIC = "fused GEMM µs/call + effective HBM GB/s (% peak) at M=1..32, r=512"
+
+
+def algorithmic_bytes(M: int, N: int, K: int, r: int) -> int:
+    """Bytes one product call must move once: R codes + R scales + g + the FP4
+    activation (codes + scales) + x (when r > 0) + U + V + alpha + y."""
+    W = (r + 31) // 32
+    b = N * K // 2 + N * K // 16 + 4 + M * K // 2 + M * K // 16 + 2 * M * N
+    if r > 0:
+        b += 2 * M * K + 4 * W * (N + K) + 2 * r
+    return b
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "bit_weight_gemm_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode())
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(cfg: int, sched_name: str, src_hash: str):
+    """HBM bytes per call from the committed rocprofv3 --pmc summary, if it was
+    taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{sched_name}_config{cfg}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("source_hash") != src_hash:
+        return None
+    return d.get("bytes_per_call")
+
+
+class Rotation:
+    """B device copies of the weight operands of one problem."""
+
+    def __init__(self, prob, n_sets: int):
+        import torch
+        self.n = n_sets
+        self.wc = [prob.w_codes] + [prob.w_codes.clone() for _ in range(n_sets - 1)]
+        self.ws = [prob.w_scales] + [prob.w_scales.clone() for _ in range(n_sets - 1)]
+        if prob.r > 0:
+            self.up = [prob.u_packed] + [prob.u_packed.clone() for _ in range(n_sets - 1)]
+            self.vp = [prob.v_packed] + [prob.v_packed.clone() for _ in range(n_sets - 1)]
+        else:
+            self.up = self.vp = [None] * n_sets
+        torch.cuda.synchronize()
+
+    def kw(self, i: int) -> dict:
+        j = i % self.n
+        return dict(w_codes=self.wc[j], w_scales=self.ws[j], u_packed=self.up[j],
+                    v_packed=self.vp[j])
+
+
+def weight_bytes(prob) -> int:
+    b = prob.w_codes.numel() + prob.w_scales.numel()
+    if prob.r > 0:
+        b += 4 * (prob.u_packed.numel() + prob.v_packed.numel())
+    return b
+
+
+def time_graph(fn_step, n: int, reps: int = 3):
+    """Capture n calls of fn_step(i) in a HIP graph; return (best GPU seconds
+    per call over reps replays, graph)."""
+    import torch
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=st):
+        for i in range(n):
+            fn_step(i, st)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best = float("inf")
+    for _ in range(reps):
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1) / 1e3 / n)
+    return best, g
+
+
+def gemm_call_time(prob, sched: int, rot: Rotation | None, calls: int) -> float:
+    def step(i, st):
+        kw = rot.kw(i) if rot is not None else {}
+        prob.gemm(sched, stream=st, **kw)
+    t, _ = time_graph(step, calls)
+    return t
+
+
+def cpu_baseline(cfg: int, seconds: float):
+    import numpy as np
+    import oracle
+    from bit_weight_gemm_amd import workloads as wl
+    d = wl.make_config(cfg)
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.quant_act_fp4(d["x"])
+        oracle.gemm_lowrank(d["x"], d["wcode"], d["wscales"], d["g"], d["V"], d["U"], d["alpha"])
+        n += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = (time.perf_counter() - t0) / n
+    nb = algorithmic_bytes(d["M"], d["N"], d["K"], d["r"])
+    return {"value": round(nb / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "us_per_call": round(dt * 1e6, 1),
+            "sample": f"{n} full calls of the config-{cfg} product on the host (quantise x, then "
+                      f"y in fp64 over all M*N outputs), same seeded inputs as the GPU"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--config", type=int, default=1, help="workload the step runs (default 1)")
+    ap.add_argument("--schedule", type=int, default=0, help="BILOCO_SCHED_* (0 = auto)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true", help="skip the per-config table")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(use --gpus 1).", file=sys.stderr)
+        return 2
+
+    import torch
+    from bit_weight_gemm_amd import binding as B
+    from bit_weight_gemm_amd import workloads as wl
+    from bit_weight_gemm_amd.problem import DeviceProblem
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    B.lib()
+    src_hash = source_hash()
+    cfg = args.config
+    d = wl.make_config(cfg)
+    prob = DeviceProblem(d)
+    M, N, K, r = prob.M, prob.N, prob.K, prob.r
+    sched = args.schedule or B.biloco_default_schedule(M, N, K, r)
+    sched_name = {1: "unfused", 2: "fused_gemv", 3: "fused_mfma"}.get(sched, str(sched))
+    n_sets = max(2, int(ROT_BYTES // weight_bytes(prob)) + 1)
+    rot = Rotation(prob, min(n_sets, args.steps))
+
+    # warmup: W eager steps
+    for i in range(args.warmup):
+        prob.quantize()
+        prob.gemm(sched, **rot.kw(i))
+    torch.cuda.synchronize()
+
+    # the timed region: exactly K steps, captured once, replayed once
+    K_steps = args.steps
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=st):
+        for i in range(K_steps):
+            prob.quantize(stream=st)
+            prob.gemm(sched, stream=st, **rot.kw(i))
+    graph.replay()                       # untimed: first replay uploads the graph
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu = e0.elapsed_time(e1) / 1e3
+    ms_per_step = wall * 1e3 / K_steps
+    nbytes = algorithmic_bytes(M, N, K, r)
+    value = nbytes / (wall / K_steps) / 1e9
+
+    # the product call alone (the dominant work), same rotation, events on its stream
+    t_call = gemm_call_time(prob, sched, rot, min(K_steps, 400))
+    achieved = nbytes / t_call / 1e9
+    t_warm = gemm_call_time(prob, sched, None, 200)
+    traffic = measured_traffic(cfg, sched_name, src_hash)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K_steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp4-e2m1/e4m3 weights, bf16 x, fp32 accumulate, bf16 y",
+        "data": "synthetic (seeded generators; weights rotated over >= 1.2 GB)",
+        "config": {"workload": d["name"], "M": M, "K": K, "N": N, "r": r,
+                   "schedule": sched_name, "global_batch": M, "parallelism": "none (1 GPU)"},
+        "us_per_step": round(wall * 1e6 / K_steps, 3),
+        "us_per_call": round(t_call * 1e6, 3),
+        "us_per_call_cache_resident": round(t_warm * 1e6, 3),
+        "pct_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
+        "step_gpu_us": round(gpu * 1e6 / K_steps, 3),
+        "roofline": {"bound": "hbm", "kernel": f"biloco_gemm_lowrank ({sched_name})",
+                     "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": traffic, "bytes_per_call": nbytes},
+        "source_hash": src_hash,
+    }
+
+    if not args.no_configs:
+        table = {}
+        # correction overhead at this config: the same x and R with r = 0
+        d0 = wl.make_config(cfg, r=0)
+        p0 = DeviceProblem(d0)
+        rot0 = Rotation(p0, max(2, int(ROT_BYTES // weight_bytes(p0)) + 1))
+        s0 = B.biloco_default_schedule(M, N, K, 0)
+        t0c = gemm_call_time(p0, s0, rot0, 400)
+        out["r0_us_per_call"] = round(t0c * 1e6, 3)
+        out["correction_overhead"] = round(t_call / t0c - 1.0, 4)
+        del rot0, p0
+        for c in (1, 2, 3, 4):
+            dc = wl.make_config(c)
+            pc = DeviceProblem(dc)
+            sc = B.biloco_default_schedule(pc.M, pc.N, pc.K, pc.r)
+            rc = Rotation(pc, max(2, int(ROT_BYTES // weight_bytes(pc)) + 1))
+            calls = 100 if pc.M <= 2 else 20
+            tc = gemm_call_time(pc, sc, rc, calls)
+            bc = algorithmic_bytes(pc.M, pc.N, pc.K, pc.r)
+            table[f"config{c}"] = {"M": pc.M, "K": pc.K, "N": pc.N, "r": pc.r,
+                                   "schedule": {1: "unfused", 2: "fused_gemv",
+                                                3: "fused_mfma"}.get(sc, sc),
+                                   "us_per_call": round(tc * 1e6, 3),
+                                   "GBps": round(bc / tc / 1e9, 1),
+                                   "pct_peak": round(100 * bc / tc / 1e9 / PEAK_HBM_GBS, 2)}
+            del rc, pc
+            torch.cuda.empty_cache()
+        out["per_config"] = table
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
