@@ -22,6 +22,7 @@ bool schedule_allowed(int s, int M, int N, int K, int r) {
     switch (s) {
         case BILOCO_SCHED_UNFUSED: return true;
         case BILOCO_SCHED_FUSED_GEMV: return gemv_supported(M, N, K, r);
+        case BILOCO_SCHED_FUSED_MFMA: return mfma_supported(M, N, K, r);
         default: return false;
     }
 }
@@ -34,12 +35,12 @@ biloco_status check_shape(int32_t M, int32_t N, int32_t K, int32_t r) {
     return BILOCO_OK;
 }
 
-// Measured on MI355X: for M <= 2 the two-launch schedule (z kernel, then the
-// vector-ALU product kernel reading z complete) is faster than the one-launch
-// schedule, whose tagged z hand-off waits behind the stream of R in the
-// memory queues.
+// Measured on MI355X: for M <= 2 the two-launch vector-ALU schedule (z
+// kernel, then the product kernel reading z complete) is faster than the
+// one-launch schedule, whose tagged z hand-off waits behind the stream of R
+// in the memory queues.  From M = 3 on, the matrix-core schedule.
 int resolve_schedule(int M, int N, int K, int r) {
-    (void)M; (void)N; (void)K; (void)r;
+    if (M >= 3 && mfma_supported(M, N, K, r)) return BILOCO_SCHED_FUSED_MFMA;
     return BILOCO_SCHED_UNFUSED;
 }
 
@@ -90,7 +91,7 @@ biloco_status biloco_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K, int32
     if (!bytes) return BILOCO_ERR_INVALID_VALUE;
     biloco_status st = check_shape(M, N, K, r);
     if (st != BILOCO_OK) return st;
-    *bytes = r > 0 ? ws_total_bytes(M, N, K, r) : 0;
+    *bytes = ws_total_bytes(M, N, K, r);
     return BILOCO_OK;
 }
 
@@ -108,7 +109,7 @@ biloco_status biloco_gemm_check(const void *a_codes, const void *a_scales, const
                           v_packed, u_packed, alpha_bf16, y_bf16, workspace};
     for (const void *p : ptrs)
         if (p && !aligned16(p)) return BILOCO_ERR_INVALID_VALUE;
-    size_t need = r > 0 ? ws_total_bytes(M, N, K, r) : 0;
+    size_t need = ws_total_bytes(M, N, K, r);
     if (need > 0 && !workspace) return BILOCO_ERR_INVALID_VALUE;
     if (workspace_bytes < need) return BILOCO_ERR_WORKSPACE_TOO_SMALL;
     // the output must not overlap any operand
@@ -165,7 +166,7 @@ biloco_status biloco_gemm_lowrank_sched(const uint8_t *a_codes, const uint8_t *a
     hipError_t e;
     switch (s) {
         case BILOCO_SCHED_FUSED_GEMV: e = launch_gemm_fused_gemv(a, stream); break;
-        case BILOCO_SCHED_FUSED_MFMA: e = launch_gemm_fused_mfma(a, stream); break;
+        case BILOCO_SCHED_FUSED_MFMA: e = launch_gemm_mfma(a, stream); break;
         default: e = launch_gemm_unfused(a, stream); break;
     }
     return e == hipSuccess ? BILOCO_OK : BILOCO_ERR_HIP;

@@ -29,6 +29,9 @@ struct GemmArgs {
 //   [64 KiB, ...)     z as (fp32 value | 32-bit epoch tag << 32) pairs [M][Rpad]
 //   then              z as plain fp32 [M][Rpad] for the two-launch schedule (a
 //                     separate area, so plain floats are never read as tags)
+//   then (256-aligned) the matrix-core schedule's area: z slice partials,
+//                     per-word counters, z/g operands, K-slice partials of y
+//                     and per-row-block counters (sized by mfma_ws_bytes)
 constexpr int kGemvMaxWorkgroups = 8192;
 constexpr size_t kWsHeaderBytes = 64 * 1024;
 inline int rpad32(int r) { return (r + 31) / 32 * 32; }
@@ -38,9 +41,15 @@ inline size_t ws_zt_offset() { return kWsHeaderBytes; }
 inline size_t ws_zt_bytes(int M, int r) { return (size_t)8 * (size_t)M * (size_t)rpad32(r); }
 inline size_t ws_zf_offset(int M, int r) { return ws_zt_offset() + ws_zt_bytes(M, r); }
 inline size_t ws_zf_bytes(int M, int r) { return (size_t)4 * (size_t)M * (size_t)rpad32(r); }
+inline size_t ws_mfma_offset(int M, int r) {
+    return r > 0 ? (ws_zf_offset(M, r) + ws_zf_bytes(M, r) + 255) / 256 * 256 : 0;
+}
+bool mfma_supported(int M, int N, int K, int r);     // shapes the matrix-core schedule handles
+size_t mfma_ws_bytes(int M, int N, int K, int r);    // its workspace area (0 if none is needed)
+// Workspace for every schedule of the shape: nothing for r = 0 unless the
+// matrix-core schedule splits K.
 inline size_t ws_total_bytes(int M, int N, int K, int r) {
-    (void)N; (void)K;
-    return ws_zf_offset(M, r) + ws_zf_bytes(M, r);
+    return ws_mfma_offset(M, r) + mfma_ws_bytes(M, N, K, r);
 }
 
 hipError_t launch_pack_signs(const int8_t *signs, int64_t rows, int64_t cols, uint32_t *packed,
@@ -51,6 +60,6 @@ hipError_t launch_gemm_unfused(const GemmArgs &a, hipStream_t stream);
 hipError_t launch_gemm_fused_gemv(const GemmArgs &a, hipStream_t stream);
 hipError_t launch_gemm_gemv_two_launch(const GemmArgs &a, hipStream_t stream);
 bool gemv_supported(int M, int N, int K, int r);   // shapes the one-launch vector-ALU schedule handles
-hipError_t launch_gemm_fused_mfma(const GemmArgs &a, hipStream_t stream);
+hipError_t launch_gemm_mfma(const GemmArgs &a, hipStream_t stream);
 
 }  // namespace biloco

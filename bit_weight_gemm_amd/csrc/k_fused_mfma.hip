@@ -1,11 +1,686 @@
-// One-launch matrix-core schedule (BILOCO_SCHED_FUSED_MFMA): not built yet.
+// Matrix-core schedule of the fused product, for any decode batch M <= 32.
+//
+// BiLoCo README, section "Kernel": y = FP4(x) FP4(R)^T + sum_i alpha_i (x.v_i) u_i
+// for decode batches up to 32.  z = alpha (.) (V x) is computed from V's
+// packed signs, and z is expanded through U's packed signs into the fp32
+// accumulators before the bf16 store.  The pages run the FP4 GEMM on tensor
+// cores with the batch padded to 128 rows.  Here, on gfx950 matrix cores, the
+// batch is padded to 16 rows (M <= 16) or 32 rows, and the work is two launches
+// on one stream:
+//
+// 1. mfma_z_kernel computes z/g = (alpha/g) (.) (x . V+-) with
+//    v_mfma_f32_16x16x32_bf16.  The bf16 activation x is exact as an
+//    operand.  The +-1 operand is built in registers from V's sign words.
+//    Workgroups own (one 32-bit word of V, one K-slice).  The last workgroup
+//    to arrive for a word (a counter, never a wait) sums the slices.  It
+//    stores z/g as bf16 high + low parts, in the register layout of the
+//    correction MFMA.
+//
+// 2. mfma_product_kernel: one workgroup of 8 waves per CU.  Each workgroup
+//    owns one K-slice and a range of 16-row blocks of R.
+//    - Each wave owns a few 128-k chunks of the slice.  Its activation tile
+//      for them is loaded once and dequantized into registers as exact f16.
+//    - The wave walks the range's row blocks through a ring of 16-byte code
+//      loads.
+//    - Codes are dequantized in registers into the B operand of
+//      v_mfma_f32_16x16x32_f16.  One v_cvt_scalef32_pk_f16_fp4 per byte
+//      applies the power of two of the E4M3 block scale, and a packed f16
+//      multiply applies its mantissa.  Both steps are exact.
+//    - Per row block, the waves' sums meet in LDS.
+//    - Before the stream, each workgroup adds its share of the correction
+//      (z/g) . U+- into the same fp32 accumulators.  Its share is the rank
+//      words w = slice, slice + S, ...
+//    - K-slices meet in the workspace.  The last workgroup to arrive for a
+//      row block sums them, multiplies by g and stores bf16.
+//
+// MFMA operand layout of the 16x16x32 forms (checked on the device):
+//   A[i][k] sits in lane i + 16 (k / 8), element k % 8.
+//   B[k][j] sits in lane j + 16 (k / 8), element k % 8.
+//   D[i][j] sits in lane j + 16 (i / 4), element i % 4.
+// The reduction index k may be any permutation shared by A and B.
+//
+// K order inside a 128-k chunk: lane group q = lane / 16 holds the 32 k from
+// 32 q to 32 q + 31.  These are one 16-byte code load and one 2-byte scale
+// load per row.  K-step d of the chunk takes k = 32 q + 8 d + e, e < 8.
+#include <mutex>
+
+#include "biloco_device.h"
 #include "biloco_internal.h"
 
 namespace biloco {
 
-hipError_t launch_gemm_fused_mfma(const GemmArgs &a, hipStream_t stream) {
-    (void)a; (void)stream;
-    return hipErrorNotSupported;
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kZThreads = 256;          // z kernel: 4 waves
+constexpr int kZStepsPerWave = 8;       // K-steps (32 k) per wave in the z kernel
+constexpr int kPThreads = 512;          // product kernel: 8 waves
+constexpr int kPWaves = kPThreads / 64;
+constexpr int kChunkK = 128;
+constexpr int kMaxRbPass = 16;          // row blocks per pass of a workgroup (upper bound of every variant)
+constexpr int kGridTarget = 256;        // one workgroup per CU
+constexpr size_t kLdsLimit = 160 * 1024 - 1024;
+
+constexpr int kSumBatch = 8;            // K-slice partials loaded at once by a last arrival
+
+// Per batch-tile-height tuning (MB m-blocks of 16 rows):
+//   kCpw       128-k chunks per wave: the activation tile takes 16 kCpw MB
+//              VGPRs, a workgroup covers 8 kCpw chunks of K
+//   kRbw*      row blocks per pass: every wave holds kRbw x kCpw 16-byte code
+//              loads (5 VGPRs each with the scales) in flight at once
+template <int MB> struct MfmaShape {
+    static constexpr int kCpw = MB == 1 ? 3 : 2;
+    static constexpr int kRbwSmall = 3;                 // row blocks per workgroup, small variant
+    static constexpr int kRbwLarge = MB == 1 ? 8 : 9;  // row blocks per workgroup, large variant
+};
+
+struct MfmaParams {
+    const uint8_t *a_codes;
+    const uint8_t *a_scales;
+    const uint16_t *x;
+    const uint8_t *w_codes;
+    const uint8_t *w_scales;
+    const uint32_t *v;
+    const uint32_t *u;
+    const uint16_t *alpha;
+    uint16_t *y;
+    float g;
+    int M, N, K, r, W;          // W = ceil(r / 32)
+    // z kernel
+    int zs, zsteps;             // K-slices and K-steps per slice
+    float *zpart;               // [zs][W][32 m][32 i]
+    uint32_t *zcnt;             // [W]
+    uint32_t *zA;               // [W][MB][2 hi/lo][64 lanes][4] bf16 pairs of z / g
+    // product kernel
+    int S, cps, chunks, RB, Gs;
+    float *ypart;               // [S][RB][MB][64 lanes][4] (D layout)
+    uint32_t *ycnt;             // [RB]
+};
+
+__device__ __forceinline__ float4_t mfma_f16(const u32x4_t &a, const u32x4_t &b, float4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a),
+                                                  __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ float4_t mfma_bf16(const u32x4_t &a, const u32x4_t &b, float4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ half2_t mantissa_pair(float s) {
+    const _Float16 m = (_Float16)__uint_as_float((__float_as_uint(s) & 0x007FFFFFu) | 0x3F800000u);
+    return half2_t{m, m};
+}
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4x2_scaled(uint32_t w, float s, half2_t m2) {
+    const half2_t h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s, SEL);
+    return __builtin_bit_cast(uint32_t, h * m2);
+}
+// eight E2M1 codes (element e in nibble e of `codes`) times an E4M3 scale s
+// -> eight exact f16 values, element e in half e
+__device__ __forceinline__ u32x4_t dequant8(uint32_t codes, float s, half2_t m2) {
+    return u32x4_t{fp4x2_scaled<0>(codes, s, m2), fp4x2_scaled<1>(codes, s, m2),
+                   fp4x2_scaled<2>(codes, s, m2), fp4x2_scaled<3>(codes, s, m2)};
+}
+// bits p and p + 16 of t -> bf16 pair (+-1, +-1); bit set means -1
+__device__ __forceinline__ uint32_t sign_pair_bf16(uint32_t t, int p) {
+    return ((t << (15 - p)) & 0x80008000u) | 0x3F803F80u;
+}
+// Cross-workgroup hand-off without cache-wide fences.  An agent-scope
+// release or acquire fence on gfx950 writes back or invalidates a whole L2
+// (buffer_wbl2 / buffer_inv), which costs tens of microseconds when every
+// workgroup does it.  Instead, data that another workgroup reads in the same
+// launch is written and read with relaxed agent-scope atomics, which are
+// coherent per access (sc1).  A producer waits for its own stores to complete
+// (s_waitcnt 0) before the workgroup barrier that precedes the counter
+// increment.  The counter is a relaxed agent-scope fetch-add.
+__device__ __forceinline__ void put(float *p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float get(const float *p) {
+    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void stores_done() { __builtin_amdgcn_s_waitcnt(0); }
+// Raw buffer resources over R and the FP4 activation.  A buffer load whose
+// offset is past the resource's size returns zeros without a memory access;
+// loads with nothing to fetch (rows past N, chunks past a wave's share, the
+// K tail) use the offset kOob, so every lane and every path issues the same
+// loads.
+constexpr int kOob = 0x7FFFFFF0;
+constexpr int kRsrcWord3 = 0x00020000;    // raw 32-bit buffer, gfx9 family
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void *base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+// The offset goes through an empty asm so that it is one VGPR value: left
+// as a select between a computed offset and the constant kOob, the compiler
+// splits the load into two exec-masked loads of the same registers and waits
+// for the first before issuing the second, which serialises the stream.
+__device__ __forceinline__ int opaque(int v) {
+    __asm__ volatile("" : "+v"(v));
+    return v;
+}
+__device__ __forceinline__ u32x4_t load16(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ uint32_t load2(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t arrive(uint32_t *cnt) {
+    return __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// =====================================================================
+// launch 1: z / g
+// =====================================================================
+// Workgroup (w, s): the 32 indices of word w of V over K-slice s, every row
+// m.  Wave q takes the slice's K-steps q, q + 4, ... (at most 8), loads all of
+// them first, then runs MB x 2 bf16 MFMAs per K-step.
+template <int MB>
+__global__ void __launch_bounds__(kZThreads) mfma_z_kernel(MfmaParams p) {
+    __shared__ float4_t s_acc[4][MB * 2][64];
+    __shared__ uint32_t s_last;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int w = blockIdx.x % p.W, s = blockIdx.x / p.W;
+    const int col = lane & 15, grp = lane >> 4;
+    const int steps = p.K >> 5;
+    const int step0 = s * p.zsteps;
+    const int nsteps = min(p.zsteps, steps - step0);
+    const uint32_t *vrow = p.v + (int64_t)w * p.K;
+
+    u32x4_t xa[kZStepsPerWave][MB];
+    u32x4_t vv[kZStepsPerWave][2];
+#pragma unroll
+    for (int t = 0; t < kZStepsPerWave; ++t) {
+        int st = wave + 4 * t;
+        st = st < nsteps ? st : nsteps - 1;
+        const int k0 = (step0 + st) * 32 + 8 * grp;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            const int m = 16 * mb + col;
+            const int mc = m < p.M ? m : p.M - 1;
+            xa[t][mb] = *reinterpret_cast<const u32x4_t *>(p.x + (int64_t)mc * p.K + k0);
+        }
+        vv[t][0] = *reinterpret_cast<const u32x4_t *>(vrow + k0);
+        vv[t][1] = *reinterpret_cast<const u32x4_t *>(vrow + k0 + 4);
+    }
+    float4_t acc[MB][2];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[mb][0] = acc[mb][1] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < kZStepsPerWave; ++t) {
+        if (wave + 4 * t < nsteps) {
+            const uint32_t vw[8] = {vv[t][0].x, vv[t][0].y, vv[t][0].z, vv[t][0].w,
+                                    vv[t][1].x, vv[t][1].y, vv[t][1].z, vv[t][1].w};
+#pragma unroll
+            for (int ib = 0; ib < 2; ++ib) {
+                const int b = 16 * ib + col;      // rank index inside word w
+                u32x4_t bv;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    bv[e] = (((vw[2 * e] >> b) & 1u) << 15) | (((vw[2 * e + 1] >> b) & 1u) << 31) |
+                            0x3F803F80u;
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) {
+                    u32x4_t a = xa[t][mb];
+                    if (16 * mb + col >= p.M) a = u32x4_t{0u, 0u, 0u, 0u};
+                    acc[mb][ib] = mfma_bf16(a, bv, acc[mb][ib]);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int ib = 0; ib < 2; ++ib) s_acc[wave][mb * 2 + ib][lane] = acc[mb][ib];
+    __syncthreads();
+    // this slice's partial [32 m][32 i]; D element e of lane l is
+    // (m = 16 mb + 4 (l / 16) + e, i = 16 ib + l % 16)
+    float *part = p.zpart + ((int64_t)s * p.W + w) * 1024;
+    for (int idx = threadIdx.x; idx < MB * 2 * 64; idx += kZThreads) {
+        const int l = idx & 63, blk = idx >> 6;
+        const int mb = blk >> 1, ib = blk & 1;
+        const float4_t v = s_acc[0][blk][l] + s_acc[1][blk][l] + s_acc[2][blk][l] + s_acc[3][blk][l];
+        const int i = 16 * ib + (l & 15);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) put(part + (16 * mb + 4 * (l >> 4) + e) * 32 + i, v[e]);
+    }
+    stores_done();
+    __syncthreads();
+    if (threadIdx.x == 0) s_last = arrive(p.zcnt + w) == (uint32_t)(p.zs - 1);
+    __syncthreads();
+    if (!s_last) return;
+    // Last arrival for word w: the slices' sum times alpha_i / g, as bf16
+    // high + low parts in the A layout of the correction MFMA: lane
+    // (m = l % 16, q = l / 16), dword j holds indices (4 q + j, 4 q + j + 16).
+    const float ginv = 1.0f / p.g;
+    for (int idx = threadIdx.x; idx < MB * 64; idx += kZThreads) {
+        const int l = idx & 63, mb = idx >> 6;
+        const int m = 16 * mb + (l & 15), q = l >> 4;
+        // indices 4 q + j (h = 0) and 4 q + j + 16 (h = 1), j < 4
+        float sum[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        for (int t0 = 0; t0 < p.zs; t0 += kSumBatch) {
+            float part[kSumBatch][2][4];
+#pragma unroll
+            for (int tt = 0; tt < kSumBatch; ++tt) {
+                const int t = min(t0 + tt, p.zs - 1);
+                const float *src = p.zpart + ((int64_t)t * p.W + w) * 1024 + m * 32 + 4 * q;
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) part[tt][h][j] = get(src + 16 * h + j);
+            }
+#pragma unroll
+            for (int tt = 0; tt < kSumBatch; ++tt)
+                if (t0 + tt < p.zs) {
+#pragma unroll
+                    for (int h = 0; h < 2; ++h)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) sum[h][j] += part[tt][h][j];
+                }
+        }
+        u32x4_t hi, lo;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            uint32_t vh = 0u, vl = 0u;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int i = 32 * w + 4 * q + j + 16 * h;
+                const float al = bf16_to_f32(p.alpha[i < p.r ? i : p.r - 1]);
+                const float zz = (i < p.r && m < p.M) ? sum[h][j] * al * ginv : 0.0f;
+                const uint32_t zh = f32_to_bf16_rne(zz);
+                const uint32_t zl = f32_to_bf16_rne(zz - bf16_to_f32(zh));
+                vh |= zh << (16 * h);
+                vl |= zl << (16 * h);
+            }
+            hi[j] = vh;
+            lo[j] = vl;
+        }
+        u32x4_t *dst = reinterpret_cast<u32x4_t *>(p.zA) + (((int64_t)w * MB + mb) * 2) * 64 + l;
+        dst[0] = hi;
+        dst[64] = lo;
+    }
+    if (threadIdx.x == 0) p.zcnt[w] = 0u;   // ready for the next call on this workspace
+}
+
+// =====================================================================
+// launch 2: the product
+// =====================================================================
+// Workgroup (slice s, row-block range).  Wave q owns the chunks
+// [q ncs / 8, (q + 1) ncs / 8) of the slice for every row block of the range:
+// its activation tile (those chunks, every K-step, every m-block) lives in
+// registers for the whole launch, so the stream of R meets no LDS read.
+// The range is at most RBW row blocks.  The wave issues every load it needs
+// (RBW x CPW 16-byte code loads and their scales) before computing anything,
+// then consumes the row blocks in issue order.  A slot with no work (row
+// block past the range, chunk past the wave's share) loads zeros through an
+// out-of-range buffer offset, so every path issues the same loads and the
+// hardware wait counts stay exact.
+template <int MB, int RBW>
+__global__ void __launch_bounds__(kPThreads) mfma_product_kernel(MfmaParams p) {
+    using Shape = MfmaShape<MB>;
+    constexpr int CPW = Shape::kCpw;
+    extern __shared__ float4_t s_part[];   // [wave][row block of the range][mb][64 lanes]
+    __shared__ uint32_t s_last[kMaxRbPass];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int col = lane & 15, grp = lane >> 4;
+    const int KH = p.K >> 1, KB = p.K >> 4;
+    const int s = blockIdx.x % p.S, wgi = blockIdx.x / p.S;
+    const int rb_begin = (int)((int64_t)wgi * p.RB / p.Gs);      // Gs row groups of <= RBW blocks
+    const int rb_end = (int)((int64_t)(wgi + 1) * p.RB / p.Gs);
+    const int c0 = s * p.cps;
+    const int ncs = min(p.cps, p.chunks - c0);
+    const int wc0 = c0 + wave * ncs / kPWaves;                 // this wave's chunks
+    const int cpw = c0 + (wave + 1) * ncs / kPWaves - wc0;     // 0 .. CPW
+    const __amdgpu_buffer_rsrc_t r_wc = buffer_of(p.w_codes, (int64_t)p.N * KH);
+    const __amdgpu_buffer_rsrc_t r_ws = buffer_of(p.w_scales, (int64_t)p.N * KB);
+    const __amdgpu_buffer_rsrc_t r_ac = buffer_of(p.a_codes, (int64_t)p.M * KH);
+    const __amdgpu_buffer_rsrc_t r_as = buffer_of(p.a_scales, (int64_t)p.M * KB);
+
+    // ---- activation tile loads (rows >= M, chunks past the wave's share and
+    // the K tail read zeros)
+    u32x4_t act_c[CPW][MB];
+    uint32_t act_s[CPW][MB];
+#pragma unroll
+    for (int c = 0; c < CPW; ++c)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            const int m = 16 * mb + col, gc = wc0 + c;
+            const bool ok = m < p.M && c < cpw && gc * kChunkK + grp * 32 < p.K;
+            act_c[c][mb] = load16(r_ac, opaque(ok ? m * KH + gc * 64 + grp * 16 : kOob));
+            act_s[c][mb] = load2(r_as, opaque(ok ? m * KB + gc * 8 + grp * 2 : kOob));
+        }
+
+    // correction words of this wave: w = s + S (wave + 8 j)
+    const int nws = p.W > s ? (p.W - s + p.S - 1) / p.S : 0;
+    const int pb = rb_begin, nrb = rb_end - rb_begin;     // 1 .. RBW row blocks
+
+    // ---- correction operands for the first word of this wave
+    u32x4_t zz[MB][2];
+    uint32_t uw[RBW];
+    auto corr_load = [&](int wi) {
+        const int w = s + p.S * wi;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                zz[mb][h] = reinterpret_cast<const u32x4_t *>(p.zA)[(((int64_t)w * MB + mb) * 2 + h) * 64 + lane];
+#pragma unroll
+        for (int rbl = 0; rbl < RBW; ++rbl) {
+            const int n = min((pb + min(rbl, nrb - 1)) * 16 + col, p.N - 1);
+            uw[rbl] = p.u[(int64_t)w * p.N + n];
+        }
+    };
+    const bool has_corr = wave < nws;
+    if (has_corr) corr_load(wave);
+
+    // ---- every load of R for this workgroup: codes and scales
+    u32x4_t cw[RBW][CPW];
+    uint32_t sw[RBW][CPW];
+#pragma unroll
+    for (int rbl = 0; rbl < RBW; ++rbl) {
+        const int n = (pb + rbl) * 16 + col;
+#pragma unroll
+        for (int c = 0; c < CPW; ++c) {
+            const int gc = wc0 + c;
+            const bool ok = rbl < nrb && n < p.N && c < cpw && gc * kChunkK + grp * 32 < p.K;
+            cw[rbl][c] = load16(r_wc, opaque(ok ? n * KH + gc * 64 + grp * 16 : kOob));
+            sw[rbl][c] = load2(r_ws, opaque(ok ? n * KB + gc * 8 + grp * 2 : kOob));
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- dequantise the activation tile (its loads are the oldest in flight)
+    u32x4_t act[CPW][4][MB];           // exact f16 A operands, K-step d of chunk c
+#pragma unroll
+    for (int c = 0; c < CPW; ++c)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            // zero codes (the loads that read nothing) give zero operands
+            const float s_lo = __builtin_amdgcn_cvt_f32_fp8(act_s[c][mb], 0);
+            const float s_hi = __builtin_amdgcn_cvt_f32_fp8(act_s[c][mb], 1);
+            const half2_t m_lo = mantissa_pair(s_lo), m_hi = mantissa_pair(s_hi);
+#pragma unroll
+            for (int d = 0; d < 4; ++d)
+                act[c][d][mb] = d < 2 ? dequant8(act_c[c][mb][d], s_lo, m_lo)
+                                      : dequant8(act_c[c][mb][d], s_hi, m_hi);
+        }
+
+    // ---- per row block: the correction of this wave's first word, then the
+    // wave's chunks of the product, into the wave's own LDS slot
+    float4_t *mine = s_part + (size_t)wave * RBW * MB * 64 + lane;
+#pragma unroll
+    for (int rbl = 0; rbl < RBW; ++rbl) {
+        if (rbl < nrb) {
+            float4_t acc[MB][2];
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) acc[mb][0] = acc[mb][1] = float4_t{0.f, 0.f, 0.f, 0.f};
+            if (has_corr) {
+                const uint32_t t = uw[rbl];
+                const u32x4_t bv = {sign_pair_bf16(t, 4 * grp + 0), sign_pair_bf16(t, 4 * grp + 1),
+                                    sign_pair_bf16(t, 4 * grp + 2), sign_pair_bf16(t, 4 * grp + 3)};
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) {
+                    acc[mb][0] = mfma_bf16(zz[mb][0], bv, acc[mb][0]);
+                    acc[mb][1] = mfma_bf16(zz[mb][1], bv, acc[mb][1]);
+                }
+            }
+#pragma unroll
+            for (int c = 0; c < CPW; ++c) {
+                if (c < cpw) {
+                    const float s_lo = __builtin_amdgcn_cvt_f32_fp8(sw[rbl][c], 0);
+                    const float s_hi = __builtin_amdgcn_cvt_f32_fp8(sw[rbl][c], 1);
+                    const half2_t m_lo = mantissa_pair(s_lo), m_hi = mantissa_pair(s_hi);
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) {
+                        const u32x4_t bv = d < 2 ? dequant8(cw[rbl][c][d], s_lo, m_lo)
+                                                 : dequant8(cw[rbl][c][d], s_hi, m_hi);
+#pragma unroll
+                        for (int mb = 0; mb < MB; ++mb)
+                            acc[mb][d & 1] = mfma_f16(act[c][d][mb], bv, acc[mb][d & 1]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) mine[(rbl * MB + mb) * 64] = acc[mb][0] + acc[mb][1];
+        }
+        // keep each row block's dequantisation next to its MFMAs
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // further correction words of this wave (more than 8 per slice)
+    for (int wi = wave + kPWaves; wi < nws; wi += kPWaves) {
+        corr_load(wi);
+#pragma unroll
+        for (int rbl = 0; rbl < RBW; ++rbl) {
+            if (rbl < nrb) {
+                const uint32_t t = uw[rbl];
+                const u32x4_t bv = {sign_pair_bf16(t, 4 * grp + 0), sign_pair_bf16(t, 4 * grp + 1),
+                                    sign_pair_bf16(t, 4 * grp + 2), sign_pair_bf16(t, 4 * grp + 3)};
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) {
+                    float4_t cacc = mfma_bf16(zz[mb][0], bv, float4_t{0.f, 0.f, 0.f, 0.f});
+                    cacc = mfma_bf16(zz[mb][1], bv, cacc);
+                    mine[(rbl * MB + mb) * 64] += cacc;
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- the waves' sums per row block (thread idx: row block, m-block, lane)
+    auto wave_sum = [&](int idx) {
+        float4_t v = s_part[idx];
+#pragma unroll
+        for (int q = 1; q < kPWaves; ++q) v += s_part[(size_t)q * RBW * MB * 64 + idx];
+        return v;
+    };
+
+    // ---- output: direct (one slice) or through the slice partials
+    if (p.S == 1) {
+        for (int idx = threadIdx.x; idx < nrb * MB * 64; idx += kPThreads) {
+            const int l = idx & 63, mb = (idx >> 6) % MB, rbl = idx / (64 * MB);
+            const int n = (pb + rbl) * 16 + (l & 15), m0 = 16 * mb + 4 * (l >> 4);
+            const float4_t v = wave_sum(idx);
+            if (n < p.N) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (m0 + e < p.M) p.y[(int64_t)(m0 + e) * p.N + n] = f32_to_bf16_rne(p.g * v[e]);
+            }
+        }
+    } else {
+        float *ypart = p.ypart;
+        for (int idx = threadIdx.x; idx < nrb * MB * 64; idx += kPThreads) {
+            const int l = idx & 63, mb = (idx >> 6) % MB, rbl = idx / (64 * MB);
+            if (16 * mb + 4 * (l >> 4) < p.M) {
+                const float4_t v = wave_sum(idx);
+                float *dst = ypart + ((((int64_t)s * p.RB + pb + rbl) * MB + mb) * 64 + l) * 4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) put(dst + e, v[e]);
+            }
+        }
+        stores_done();
+        __syncthreads();
+        if (threadIdx.x < nrb)
+            s_last[threadIdx.x] = arrive(p.ycnt + pb + threadIdx.x) == (uint32_t)(p.S - 1);
+        __syncthreads();
+        for (int idx = threadIdx.x; idx < nrb * MB * 64; idx += kPThreads) {
+            const int l = idx & 63, mb = (idx >> 6) % MB, rbl = idx / (64 * MB);
+            const int n = (pb + rbl) * 16 + (l & 15), m0 = 16 * mb + 4 * (l >> 4);
+            if (!s_last[rbl] || m0 >= p.M) continue;
+            float4_t v = float4_t{0.f, 0.f, 0.f, 0.f};
+            for (int t0 = 0; t0 < p.S; t0 += kSumBatch) {
+                float part[kSumBatch][4];
+#pragma unroll
+                for (int tt = 0; tt < kSumBatch; ++tt) {
+                    const int t = min(t0 + tt, p.S - 1);
+                    const float *src = ypart + ((((int64_t)t * p.RB + pb + rbl) * MB + mb) * 64 + l) * 4;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) part[tt][e] = get(src + e);
+                }
+#pragma unroll
+                for (int tt = 0; tt < kSumBatch; ++tt)
+                    if (t0 + tt < p.S) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) v[e] += part[tt][e];
+                    }
+            }
+            if (n < p.N) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (m0 + e < p.M) p.y[(int64_t)(m0 + e) * p.N + n] = f32_to_bf16_rne(p.g * v[e]);
+            }
+        }
+        if (threadIdx.x < nrb && s_last[threadIdx.x]) p.ycnt[pb + threadIdx.x] = 0u;
+    }
+
+}
+
+// =====================================================================
+// host side
+// =====================================================================
+namespace {
+struct MfmaPlan {
+    int mb, W, zs, zsteps, chunks, S, cps, RB, Gs, grid, rbw;
+    size_t lds;
+    // workspace offsets inside the matrix-core area
+    size_t off_zpart, off_zcnt, off_za, off_ypart, off_ycnt, bytes;
+};
+
+size_t align256(size_t b) { return (b + 255) / 256 * 256; }
+
+MfmaPlan mfma_plan(int M, int N, int K, int r) {
+    MfmaPlan q{};
+    q.mb = M <= 16 ? 1 : 2;
+    q.W = (r + 31) / 32;
+    // z: about kGridTarget workgroups over (word, K-slice), at most
+    // 4 x kZStepsPerWave K-steps per slice
+    const int steps = K / 32;
+    if (q.W > 0) {
+        int zs = (kGridTarget + q.W - 1) / q.W;
+        const int zs_min = (steps + 4 * kZStepsPerWave - 1) / (4 * kZStepsPerWave);
+        if (zs < zs_min) zs = zs_min;
+        if (zs > steps) zs = steps;
+        q.zsteps = (steps + zs - 1) / zs;
+        q.zs = (steps + q.zsteps - 1) / q.zsteps;
+    }
+    // product: the fewest K-slices whose chunks the 8 waves' activation
+    // tiles cover
+    q.chunks = (K + kChunkK - 1) / kChunkK;
+    const int cps_max = kPWaves * (q.mb == 1 ? MfmaShape<1>::kCpw : MfmaShape<2>::kCpw);
+    q.S = (q.chunks + cps_max - 1) / cps_max;
+    q.cps = (q.chunks + q.S - 1) / q.S;
+    q.S = (q.chunks + q.cps - 1) / q.cps;
+    q.RB = (N + 15) / 16;
+    // row groups per slice: one workgroup per CU when the range of each fits
+    // the large variant, more workgroups (several rounds) otherwise
+    const int small = q.mb == 1 ? MfmaShape<1>::kRbwSmall : MfmaShape<2>::kRbwSmall;
+    const int large = q.mb == 1 ? MfmaShape<1>::kRbwLarge : MfmaShape<2>::kRbwLarge;
+    q.Gs = kGridTarget / q.S;
+    if (q.Gs < 1) q.Gs = 1;
+    if (q.Gs < (q.RB + large - 1) / large) q.Gs = (q.RB + large - 1) / large;
+    if (q.Gs > q.RB) q.Gs = q.RB;
+    q.grid = q.Gs * q.S;
+    const int rb_wg = (q.RB + q.Gs - 1) / q.Gs;
+    q.rbw = rb_wg <= small ? small : large;
+    q.lds = (size_t)kPWaves * q.rbw * q.mb * 64 * 16;
+    // workspace
+    size_t off = 0;
+    q.off_zpart = off;
+    off += (size_t)q.zs * q.W * 1024 * 4;
+    q.off_zcnt = off;
+    off = align256(off + (size_t)q.W * 4);
+    q.off_za = off;
+    off += (size_t)q.W * q.mb * 2 * 64 * 16;
+    q.off_ypart = off;
+    if (q.S > 1) off += (size_t)q.S * q.RB * q.mb * 64 * 16;
+    q.off_ycnt = off;
+    if (q.S > 1) off += (size_t)q.RB * 4;
+    q.bytes = off > 0 ? align256(off) : 0;
+    return q;
+}
+
+// Dynamic LDS above 64 KiB must be allowed once per kernel.
+template <int MB, int RBW>
+hipError_t allow_lds() {
+    static std::once_flag once;
+    static hipError_t err = hipSuccess;
+    std::call_once(once, [] {
+        err = hipFuncSetAttribute(reinterpret_cast<const void *>(&mfma_product_kernel<MB, RBW>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsLimit);
+    });
+    return err;
+}
+}  // namespace
+
+bool mfma_supported(int M, int N, int K, int r) {
+    if (M < 1 || M > 32 || N < 1 || K < 32 || K % 32 != 0 || r < 0) return false;
+    return mfma_plan(M, N, K, r).lds <= kLdsLimit;
+}
+
+size_t mfma_ws_bytes(int M, int N, int K, int r) {
+    return mfma_supported(M, N, K, r) ? mfma_plan(M, N, K, r).bytes : 0;
+}
+
+hipError_t launch_gemm_mfma(const GemmArgs &a, hipStream_t stream) {
+    if (!mfma_supported(a.M, a.N, a.K, a.r)) return hipErrorNotSupported;
+    const MfmaPlan q = mfma_plan(a.M, a.N, a.K, a.r);
+    MfmaParams p{};
+    p.a_codes = a.a_codes;
+    p.a_scales = a.a_scales;
+    p.x = a.x;
+    p.w_codes = a.w_codes;
+    p.w_scales = a.w_scales;
+    p.v = a.v;
+    p.u = a.u;
+    p.alpha = a.alpha;
+    p.y = a.y;
+    p.g = a.g;
+    p.M = a.M;
+    p.N = a.N;
+    p.K = a.K;
+    p.r = a.r;
+    p.W = q.W;
+    p.zs = q.zs;
+    p.zsteps = q.zsteps;
+    p.S = q.S;
+    p.cps = q.cps;
+    p.chunks = q.chunks;
+    p.RB = q.RB;
+    p.Gs = q.Gs;
+    if (q.bytes > 0) {
+        char *ws = static_cast<char *>(a.ws) + ws_mfma_offset(a.M, a.r);
+        p.zpart = reinterpret_cast<float *>(ws + q.off_zpart);
+        p.zcnt = reinterpret_cast<uint32_t *>(ws + q.off_zcnt);
+        p.zA = reinterpret_cast<uint32_t *>(ws + q.off_za);
+        p.ypart = reinterpret_cast<float *>(ws + q.off_ypart);
+        p.ycnt = reinterpret_cast<uint32_t *>(ws + q.off_ycnt);
+    }
+    hipError_t e = hipSuccess;
+    if (a.r > 0) {
+        if (q.mb == 1)
+            hipLaunchKernelGGL(mfma_z_kernel<1>, dim3(q.W * q.zs), dim3(kZThreads), 0, stream, p);
+        else
+            hipLaunchKernelGGL(mfma_z_kernel<2>, dim3(q.W * q.zs), dim3(kZThreads), 0, stream, p);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const dim3 grid(q.grid), block(kPThreads);
+    constexpr int s1 = MfmaShape<1>::kRbwSmall, l1 = MfmaShape<1>::kRbwLarge;
+    constexpr int s2 = MfmaShape<2>::kRbwSmall, l2 = MfmaShape<2>::kRbwLarge;
+    if (q.mb == 1 && q.rbw == s1) {
+        e = allow_lds<1, s1>();
+        if (e == hipSuccess) hipLaunchKernelGGL((mfma_product_kernel<1, s1>), grid, block, q.lds, stream, p);
+    } else if (q.mb == 1) {
+        e = allow_lds<1, l1>();
+        if (e == hipSuccess) hipLaunchKernelGGL((mfma_product_kernel<1, l1>), grid, block, q.lds, stream, p);
+    } else if (q.rbw == s2) {
+        e = allow_lds<2, s2>();
+        if (e == hipSuccess) hipLaunchKernelGGL((mfma_product_kernel<2, s2>), grid, block, q.lds, stream, p);
+    } else {
+        e = allow_lds<2, l2>();
+        if (e == hipSuccess) hipLaunchKernelGGL((mfma_product_kernel<2, l2>), grid, block, q.lds, stream, p);
+    }
+    return e != hipSuccess ? e : hipGetLastError();
 }
 
 }  // namespace biloco

@@ -55,8 +55,10 @@ typedef int32_t biloco_status;
  * allows).  The modes here are this library's own, designed for gfx950. */
 #define BILOCO_SCHED_AUTO        0  /* pick per shape (biloco_default_schedule) */
 #define BILOCO_SCHED_UNFUSED     1  /* z kernel, then GEMM + epilogue kernel (two launches) */
-#define BILOCO_SCHED_FUSED_GEMV  2  /* one launch; vector-ALU dot products; M <= 4 */
-#define BILOCO_SCHED_FUSED_MFMA  3  /* one launch; matrix-core products; any M <= 32 */
+#define BILOCO_SCHED_FUSED_GEMV  2  /* one launch; vector-ALU dot products; M <= 2 */
+#define BILOCO_SCHED_FUSED_MFMA  3  /* matrix-core products for any M <= 32: a z kernel
+                                       (skipped when r == 0), then one product kernel whose
+                                       accumulators take the correction before the store */
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char *biloco_status_string(biloco_status s);
@@ -85,8 +87,9 @@ biloco_status biloco_pack_signs(const int8_t *signs, int64_t rows, int64_t cols,
 biloco_status biloco_quant_act_fp4(const uint16_t *x_bf16, int32_t M, int32_t K,
                                    uint8_t *a_codes, uint8_t *a_scales, hipStream_t stream);
 
-/* Bytes of device workspace biloco_gemm_lowrank needs for this shape.
- * Same argument rules as biloco_gemm_lowrank. */
+/* Bytes of device workspace biloco_gemm_lowrank needs for this shape, enough
+ * for every schedule the shape allows.  May be 0 (then workspace may be
+ * NULL).  Same argument rules as biloco_gemm_lowrank. */
 biloco_status biloco_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t r,
                                           size_t *bytes);
 

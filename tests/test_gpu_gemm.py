@@ -71,7 +71,15 @@ def test_every_batch_size_ragged(M):
 
 
 @pytest.mark.parametrize("M,K,N,r", [(1, 32, 1, 1), (2, 64, 3, 31), (4, 1024, 700, 33),
-                                     (3, 2048, 64, 0), (1, 16384, 96, 96), (16, 512, 130, 512)])
+                                     (3, 2048, 64, 0), (1, 16384, 96, 96), (16, 512, 130, 512),
+                                     # a K tail inside a 128-k chunk, one K-slice
+                                     (17, 480, 77, 65),
+                                     # several 16-row-block passes per workgroup, one K-slice
+                                     (5, 256, 66000, 8),
+                                     # several passes and two K-slices (batch of 32 rows)
+                                     (17, 4096, 33000, 64),
+                                     # many K-slices with a ragged last one
+                                     (32, 13856, 40, 100)])
 def test_edge_shapes(M, K, N, r):
     d = wl.make_inputs(M, K, N, r, seed=M * 1000 + N)
     y_ref = oracle.gemm_lowrank(d["x"], d["wcode"], d["wscales"], d["g"], d["V"], d["U"],
