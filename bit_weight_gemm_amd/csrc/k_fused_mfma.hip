@@ -5,33 +5,35 @@
 // packed signs, and z is expanded through U's packed signs into the fp32
 // accumulators before the bf16 store.  The pages run the FP4 GEMM on tensor
 // cores with the batch padded to 128 rows.  Here, on gfx950 matrix cores, the
-// batch is padded to 16 rows (M <= 16) or 32 rows, and the work is two launches
-// on one stream:
+// batch is padded to 16 rows (M <= 16) or 32 rows.  The work is two or three
+// launches on one stream:
 //
-// 1. mfma_z_kernel computes z/g = (alpha/g) (.) (x . V+-) with
-//    v_mfma_f32_16x16x32_bf16.  The bf16 activation x is exact as an
-//    operand.  The +-1 operand is built in registers from V's sign words.
-//    Workgroups own (one 32-bit word of V, one K-slice).  The last workgroup
-//    to arrive for a word (a counter, never a wait) sums the slices.  It
-//    stores z/g as bf16 high + low parts, in the register layout of the
-//    correction MFMA.
+// 1. mfma_z_kernel (r > 0) computes z/g = (alpha/g) (.) (x . V+-) with
+//    v_mfma_f32_16x16x32_bf16.  The bf16 activation x is exact as an operand;
+//    the +-1 operand is built in registers from V's sign words.  Workgroups
+//    own (one 32-bit word of V, one K-slice).  The last workgroup to arrive
+//    for a word (a counter, never a wait) sums the slices and stores bf16
+//    high + low parts in the register layout of the correction MFMA.
 //
 // 2. mfma_product_kernel: one workgroup of 8 waves per CU.  Each workgroup
 //    owns one K-slice and a range of 16-row blocks of R.
-//    - Each wave owns a few 128-k chunks of the slice.  Its activation tile
-//      for them is loaded once and dequantized into registers as exact f16.
-//    - The wave walks the range's row blocks through a ring of 16-byte code
-//      loads.
-//    - Codes are dequantized in registers into the B operand of
+//    - Each wave owns up to three 128-k chunks of the slice.  Its activation
+//      tile for them is loaded once and dequantised into registers as exact
+//      f16.
+//    - Every wave issues all of its loads of R (raw buffer loads, zeros for
+//      out-of-range slots) before computing.  Its block scales go through a
+//      wave-private LDS window.
+//    - Codes are dequantised in registers into the B operand of
 //      v_mfma_f32_16x16x32_f16.  One v_cvt_scalef32_pk_f16_fp4 per byte
 //      applies the power of two of the E4M3 block scale, and a packed f16
 //      multiply applies its mantissa.  Both steps are exact.
-//    - Per row block, the waves' sums meet in LDS.
-//    - Before the stream, each workgroup adds its share of the correction
-//      (z/g) . U+- into the same fp32 accumulators.  Its share is the rank
-//      words w = slice, slice + S, ...
-//    - K-slices meet in the workspace.  The last workgroup to arrive for a
-//      row block sums them, multiplies by g and stores bf16.
+//    - Each wave's share of the correction, (z/g) . U+- over rank words
+//      w = slice, slice + S, ..., initialises its accumulators.
+//    - The waves' sums meet in per-wave LDS slots.  With one K-slice the
+//      workgroup stores y; otherwise it stores its slice's partial sums.
+//
+// 3. mfma_epilogue_kernel (K split in S > 1 slices) sums the slices,
+//    multiplies by g and stores bf16.
 //
 // MFMA operand layout of the 16x16x32 forms (checked on the device):
 //   A[i][k] sits in lane i + 16 (k / 8), element k % 8.
@@ -55,12 +57,12 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kZThreads = 256;          // z kernel: 4 waves
+constexpr int kZThreads = 512;          // z kernel: 8 waves
+constexpr int kZWaves = kZThreads / 64;
 constexpr int kZStepsPerWave = 8;       // K-steps (32 k) per wave in the z kernel
 constexpr int kPThreads = 512;          // product kernel: 8 waves
 constexpr int kPWaves = kPThreads / 64;
 constexpr int kChunkK = 128;
-constexpr int kMaxRbPass = 16;          // row blocks per pass of a workgroup (upper bound of every variant)
 constexpr int kGridTarget = 256;        // one workgroup per CU
 constexpr size_t kLdsLimit = 160 * 1024 - 1024;
 
@@ -69,13 +71,16 @@ constexpr int kSumBatch = 8;            // K-slice partials loaded at once by a 
 // Per batch-tile-height tuning (MB m-blocks of 16 rows):
 //   kCpw       128-k chunks per wave: the activation tile takes 16 kCpw MB
 //              VGPRs, a workgroup covers 8 kCpw chunks of K
-//   kRbw*      row blocks per pass: every wave holds kRbw x kCpw 16-byte code
-//              loads (5 VGPRs each with the scales) in flight at once
+//   kRbw*      row blocks per workgroup: every wave holds kRbw x kCpw 16-byte
+//              code loads in flight at once
+// A wave's scale bytes in a row (kCpw x 8 <= 24) fit a 16-byte-aligned window
+// of three 16-byte pieces.
 template <int MB> struct MfmaShape {
-    static constexpr int kCpw = MB == 1 ? 3 : 2;
+    static constexpr int kCpw = 3;
     static constexpr int kRbwSmall = 3;                 // row blocks per workgroup, small variant
-    static constexpr int kRbwLarge = MB == 1 ? 8 : 9;  // row blocks per workgroup, large variant
+    static constexpr int kRbwLarge = MB == 1 ? 8 : 7;   // row blocks per workgroup, large variant
 };
+static_assert(MfmaShape<1>::kCpw * 8 + 14 <= 48 && MfmaShape<2>::kCpw * 8 + 14 <= 48, "scale window");
 
 struct MfmaParams {
     const uint8_t *a_codes;
@@ -91,13 +96,12 @@ struct MfmaParams {
     int M, N, K, r, W;          // W = ceil(r / 32)
     // z kernel
     int zs, zsteps;             // K-slices and K-steps per slice
-    float *zpart;               // [zs][W][32 m][32 i]
+    float *zpart;               // [zs][W][MB][64 lanes][8] (correction A-operand order)
     uint32_t *zcnt;             // [W]
     uint32_t *zA;               // [W][MB][2 hi/lo][64 lanes][4] bf16 pairs of z / g
     // product kernel
     int S, cps, chunks, RB, Gs;
     float *ypart;               // [S][RB][MB][64 lanes][4] (D layout)
-    uint32_t *ycnt;             // [RB]
 };
 
 __device__ __forceinline__ float4_t mfma_f16(const u32x4_t &a, const u32x4_t &b, float4_t c) {
@@ -173,12 +177,20 @@ __device__ __forceinline__ uint32_t arrive(uint32_t *cnt) {
 // =====================================================================
 // launch 1: z / g
 // =====================================================================
-// Workgroup (w, s): the 32 indices of word w of V over K-slice s, every row
-// m.  Wave q takes the slice's K-steps q, q + 4, ... (at most 8), loads all of
-// them first, then runs MB x 2 bf16 MFMAs per K-step.
+// Workgroup (w, s): the 32 indices of word w of V over K-slice s (at most
+// 8 kZStepsPerWave K-steps), every row m.  Wave q takes the slice's K-steps
+// q, q + 8, ...; it loads all of them first, then runs MB x 2 bf16 MFMAs per
+// K-step.  The waves' sums meet in LDS, where the tile is also transposed to
+// the A-operand layout of the correction MFMA: lane l of m-block mb holds,
+// for m = 16 mb + l % 16 and q = l / 16, the eight values
+// z[m][4q + j] (j < 4) and z[m][4q + j - 4 + 16] (j >= 4).  The slice's
+// partial goes to the workspace in that layout; the last workgroup to arrive
+// for the word (a counter, never a wait) sums the slices, scales by
+// alpha_i / g and stores bf16 high and low parts.
 template <int MB>
 __global__ void __launch_bounds__(kZThreads) mfma_z_kernel(MfmaParams p) {
-    __shared__ float4_t s_acc[4][MB * 2][64];
+    __shared__ float4_t s_acc[kZWaves][MB * 2][64];
+    __shared__ float s_t[MB * 16][33];
     __shared__ uint32_t s_last;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int w = blockIdx.x % p.W, s = blockIdx.x / p.W;
@@ -192,13 +204,13 @@ __global__ void __launch_bounds__(kZThreads) mfma_z_kernel(MfmaParams p) {
     u32x4_t vv[kZStepsPerWave][2];
 #pragma unroll
     for (int t = 0; t < kZStepsPerWave; ++t) {
-        int st = wave + 4 * t;
+        int st = wave + kZWaves * t;
         st = st < nsteps ? st : nsteps - 1;
         const int k0 = (step0 + st) * 32 + 8 * grp;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
             const int m = 16 * mb + col;
-            const int mc = m < p.M ? m : p.M - 1;
+            const int mc = m < p.M ? m : m % p.M;
             xa[t][mb] = *reinterpret_cast<const u32x4_t *>(p.x + (int64_t)mc * p.K + k0);
         }
         vv[t][0] = *reinterpret_cast<const u32x4_t *>(vrow + k0);
@@ -209,7 +221,7 @@ __global__ void __launch_bounds__(kZThreads) mfma_z_kernel(MfmaParams p) {
     for (int mb = 0; mb < MB; ++mb) acc[mb][0] = acc[mb][1] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < kZStepsPerWave; ++t) {
-        if (wave + 4 * t < nsteps) {
+        if (wave + kZWaves * t < nsteps) {
             const uint32_t vw[8] = {vv[t][0].x, vv[t][0].y, vv[t][0].z, vv[t][0].w,
                                     vv[t][1].x, vv[t][1].y, vv[t][1].z, vv[t][1].w};
 #pragma unroll
@@ -234,71 +246,60 @@ __global__ void __launch_bounds__(kZThreads) mfma_z_kernel(MfmaParams p) {
 #pragma unroll
         for (int ib = 0; ib < 2; ++ib) s_acc[wave][mb * 2 + ib][lane] = acc[mb][ib];
     __syncthreads();
-    // this slice's partial [32 m][32 i]; D element e of lane l is
-    // (m = 16 mb + 4 (l / 16) + e, i = 16 ib + l % 16)
-    float *part = p.zpart + ((int64_t)s * p.W + w) * 1024;
+    // waves' sum, D layout (m = 16 mb + 4 (l / 16) + e, i = 16 ib + l % 16) -> s_t[m][i]
     for (int idx = threadIdx.x; idx < MB * 2 * 64; idx += kZThreads) {
         const int l = idx & 63, blk = idx >> 6;
-        const int mb = blk >> 1, ib = blk & 1;
-        const float4_t v = s_acc[0][blk][l] + s_acc[1][blk][l] + s_acc[2][blk][l] + s_acc[3][blk][l];
-        const int i = 16 * ib + (l & 15);
+        float4_t v = s_acc[0][blk][l];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) put(part + (16 * mb + 4 * (l >> 4) + e) * 32 + i, v[e]);
+        for (int q = 1; q < kZWaves; ++q) v += s_acc[q][blk][l];
+        const int mb = blk >> 1, ib = blk & 1;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s_t[16 * mb + 4 * (l >> 4) + e][16 * ib + (l & 15)] = v[e];
+    }
+    __syncthreads();
+    // this slice's partial in the operand layout: thread (mb, l, j)
+    float *part = p.zpart + ((int64_t)s * p.W + w) * MB * 64 * 8;
+    for (int idx = threadIdx.x; idx < MB * 64 * 8; idx += kZThreads) {
+        const int j = idx & 7, l = (idx >> 3) & 63, mb = idx >> 9;
+        const int m = 16 * mb + (l & 15), q = l >> 4;
+        put(part + idx, s_t[m][4 * q + (j & 3) + 16 * (j >> 2)]);
     }
     stores_done();
     __syncthreads();
     if (threadIdx.x == 0) s_last = arrive(p.zcnt + w) == (uint32_t)(p.zs - 1);
     __syncthreads();
     if (!s_last) return;
-    // Last arrival for word w: the slices' sum times alpha_i / g, as bf16
-    // high + low parts in the A layout of the correction MFMA: lane
-    // (m = l % 16, q = l / 16), dword j holds indices (4 q + j, 4 q + j + 16).
+    // Last arrival for word w: the slices' sum times alpha_i / g as bf16 high
+    // + low parts.  Thread (mb, l, j) sums one value; lanes j and j + 4 of a
+    // group of 8 threads form the (index, index + 16) pair of dword j & 3.
     const float ginv = 1.0f / p.g;
-    for (int idx = threadIdx.x; idx < MB * 64; idx += kZThreads) {
-        const int l = idx & 63, mb = idx >> 6;
+    for (int idx = threadIdx.x; idx < MB * 64 * 8; idx += kZThreads) {
+        const int j = idx & 7, l = (idx >> 3) & 63, mb = idx >> 9;
         const int m = 16 * mb + (l & 15), q = l >> 4;
-        // indices 4 q + j (h = 0) and 4 q + j + 16 (h = 1), j < 4
-        float sum[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        float sum = 0.0f;
         for (int t0 = 0; t0 < p.zs; t0 += kSumBatch) {
-            float part[kSumBatch][2][4];
+            float part_v[kSumBatch];
 #pragma unroll
             for (int tt = 0; tt < kSumBatch; ++tt) {
                 const int t = min(t0 + tt, p.zs - 1);
-                const float *src = p.zpart + ((int64_t)t * p.W + w) * 1024 + m * 32 + 4 * q;
-#pragma unroll
-                for (int h = 0; h < 2; ++h)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) part[tt][h][j] = get(src + 16 * h + j);
+                part_v[tt] = get(p.zpart + ((int64_t)t * p.W + w) * MB * 64 * 8 + idx);
             }
 #pragma unroll
             for (int tt = 0; tt < kSumBatch; ++tt)
-                if (t0 + tt < p.zs) {
-#pragma unroll
-                    for (int h = 0; h < 2; ++h)
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) sum[h][j] += part[tt][h][j];
-                }
+                if (t0 + tt < p.zs) sum += part_v[tt];
         }
-        u32x4_t hi, lo;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            uint32_t vh = 0u, vl = 0u;
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int i = 32 * w + 4 * q + j + 16 * h;
-                const float al = bf16_to_f32(p.alpha[i < p.r ? i : p.r - 1]);
-                const float zz = (i < p.r && m < p.M) ? sum[h][j] * al * ginv : 0.0f;
-                const uint32_t zh = f32_to_bf16_rne(zz);
-                const uint32_t zl = f32_to_bf16_rne(zz - bf16_to_f32(zh));
-                vh |= zh << (16 * h);
-                vl |= zl << (16 * h);
-            }
-            hi[j] = vh;
-            lo[j] = vl;
+        const int i = 32 * w + 4 * q + (j & 3) + 16 * (j >> 2);
+        const float al = bf16_to_f32(p.alpha[i < p.r ? i : p.r - 1]);
+        const float zz = (i < p.r && m < p.M) ? sum * al * ginv : 0.0f;
+        const uint32_t zh = f32_to_bf16_rne(zz);
+        const uint32_t zl = f32_to_bf16_rne(zz - bf16_to_f32(zh));
+        // pair with the partner thread (j ^ 4) of the same 8-thread group
+        const uint32_t oh = __shfl_xor(zh, 4, 64), ol = __shfl_xor(zl, 4, 64);
+        if (j < 4) {
+            uint16_t *dst = reinterpret_cast<uint16_t *>(p.zA + ((((int64_t)w * MB + mb) * 2) * 64 + l) * 4 + j);
+            reinterpret_cast<uint32_t *>(dst)[0] = zh | (oh << 16);
+            reinterpret_cast<uint32_t *>(dst)[64 * 4] = zl | (ol << 16);
         }
-        u32x4_t *dst = reinterpret_cast<u32x4_t *>(p.zA) + (((int64_t)w * MB + mb) * 2) * 64 + l;
-        dst[0] = hi;
-        dst[64] = lo;
     }
     if (threadIdx.x == 0) p.zcnt[w] = 0u;   // ready for the next call on this workspace
 }
@@ -320,8 +321,11 @@ template <int MB, int RBW>
 __global__ void __launch_bounds__(kPThreads) mfma_product_kernel(MfmaParams p) {
     using Shape = MfmaShape<MB>;
     constexpr int CPW = Shape::kCpw;
-    extern __shared__ float4_t s_part[];   // [wave][row block of the range][mb][64 lanes]
-    __shared__ uint32_t s_last[kMaxRbPass];
+    // LDS: the waves' partial sums [wave][row block][mb][64 lanes], then each
+    // wave's block scales of R [wave][row][3 16-byte pieces]
+    extern __shared__ float4_t s_part[];
+    constexpr int SCL = (RBW * 16 * 3 + 63) / 64;      // scale loads per lane
+    u32x4_t *s_sc = reinterpret_cast<u32x4_t *>(s_part + (size_t)kPWaves * RBW * MB * 64);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int col = lane & 15, grp = lane >> 4;
     const int KH = p.K >> 1, KB = p.K >> 4;
@@ -333,7 +337,10 @@ __global__ void __launch_bounds__(kPThreads) mfma_product_kernel(MfmaParams p) {
     const int wc0 = c0 + wave * ncs / kPWaves;                 // this wave's chunks
     const int cpw = c0 + (wave + 1) * ncs / kPWaves - wc0;     // 0 .. CPW
     const __amdgpu_buffer_rsrc_t r_wc = buffer_of(p.w_codes, (int64_t)p.N * KH);
-    const __amdgpu_buffer_rsrc_t r_ws = buffer_of(p.w_scales, (int64_t)p.N * KB);
+    // the staged scale windows are 16-byte loads: the last one may cover up to
+    // 14 bytes past the array, inside the 16-byte block (and page) that holds
+    // its last byte; those bytes are never used
+    const __amdgpu_buffer_rsrc_t r_ws = buffer_of(p.w_scales, ((int64_t)p.N * KB + 15) & ~(int64_t)15);
     const __amdgpu_buffer_rsrc_t r_ac = buffer_of(p.a_codes, (int64_t)p.M * KH);
     const __amdgpu_buffer_rsrc_t r_as = buffer_of(p.a_scales, (int64_t)p.M * KB);
 
@@ -351,9 +358,23 @@ __global__ void __launch_bounds__(kPThreads) mfma_product_kernel(MfmaParams p) {
             act_s[c][mb] = load2(r_as, opaque(ok ? m * KB + gc * 8 + grp * 2 : kOob));
         }
 
+    // ---- block scales of R for this wave's chunks, every row of the range:
+    // per row the 16-byte-aligned 48-byte window that holds the wave's (at
+    // most 3 x 8) scale bytes; 3 pieces per row, kScLoads 16-byte loads per lane
+    const int pb = rb_begin, nrb = rb_end - rb_begin;     // 1 .. RBW row blocks
+    u32x4_t sc_v[SCL];
+#pragma unroll
+    for (int t = 0; t < SCL; ++t) {
+        const int idx = lane + 64 * t;
+        const int rl = idx / 3, piece = idx - rl * 3;
+        const int n = pb * 16 + rl;
+        const bool ok = rl < nrb * 16 && n < p.N && cpw > 0;
+        const int a0 = (n * KB + wc0 * 8) & ~15;
+        sc_v[t] = load16(r_ws, opaque(ok ? a0 + 16 * piece : kOob));
+    }
+
     // correction words of this wave: w = s + S (wave + 8 j)
     const int nws = p.W > s ? (p.W - s + p.S - 1) / p.S : 0;
-    const int pb = rb_begin, nrb = rb_end - rb_begin;     // 1 .. RBW row blocks
 
     // ---- correction operands for the first word of this wave
     u32x4_t zz[MB][2];
@@ -374,9 +395,8 @@ __global__ void __launch_bounds__(kPThreads) mfma_product_kernel(MfmaParams p) {
     const bool has_corr = wave < nws;
     if (has_corr) corr_load(wave);
 
-    // ---- every load of R for this workgroup: codes and scales
+    // ---- every code load of R for this workgroup
     u32x4_t cw[RBW][CPW];
-    uint32_t sw[RBW][CPW];
 #pragma unroll
     for (int rbl = 0; rbl < RBW; ++rbl) {
         const int n = (pb + rbl) * 16 + col;
@@ -385,10 +405,26 @@ __global__ void __launch_bounds__(kPThreads) mfma_product_kernel(MfmaParams p) {
             const int gc = wc0 + c;
             const bool ok = rbl < nrb && n < p.N && c < cpw && gc * kChunkK + grp * 32 < p.K;
             cw[rbl][c] = load16(r_wc, opaque(ok ? n * KH + gc * 64 + grp * 16 : kOob));
-            sw[rbl][c] = load2(r_ws, opaque(ok ? n * KB + gc * 8 + grp * 2 : kOob));
         }
     }
     __builtin_amdgcn_sched_barrier(0);
+
+    // ---- this wave's scale windows to its own LDS region (no barrier: only
+    // this wave reads them; its scale loads are older than its code loads)
+    u32x4_t *my_sc = s_sc + (size_t)wave * RBW * 16 * 3;
+#pragma unroll
+    for (int t = 0; t < SCL; ++t) {
+        const int idx = lane + 64 * t;
+        if (idx < RBW * 16 * 3) my_sc[idx] = sc_v[t];
+    }
+    // scale pair of chunk c of row block rbl for this lane: bytes 2 grp and
+    // 2 grp + 1 of the chunk's 8, shifted by the row's window alignment
+    auto scale_pair = [&](int rbl, int c) -> uint32_t {
+        const int n = (pb + rbl) * 16 + col;
+        const int delta = (n * KB + wc0 * 8) & 15;
+        const int byte = (rbl * 16 + col) * 48 + delta + c * 8 + grp * 2;
+        return *reinterpret_cast<const uint16_t *>(reinterpret_cast<const uint8_t *>(my_sc) + byte);
+    };
 
     // ---- dequantise the activation tile (its loads are the oldest in flight)
     u32x4_t act[CPW][4][MB];           // exact f16 A operands, K-step d of chunk c
@@ -428,8 +464,9 @@ __global__ void __launch_bounds__(kPThreads) mfma_product_kernel(MfmaParams p) {
 #pragma unroll
             for (int c = 0; c < CPW; ++c) {
                 if (c < cpw) {
-                    const float s_lo = __builtin_amdgcn_cvt_f32_fp8(sw[rbl][c], 0);
-                    const float s_hi = __builtin_amdgcn_cvt_f32_fp8(sw[rbl][c], 1);
+                    const uint32_t sp = scale_pair(rbl, c);
+                    const float s_lo = __builtin_amdgcn_cvt_f32_fp8(sp, 0);
+                    const float s_hi = __builtin_amdgcn_cvt_f32_fp8(sp, 1);
                     const half2_t m_lo = mantissa_pair(s_lo), m_hi = mantissa_pair(s_hi);
 #pragma unroll
                     for (int d = 0; d < 4; ++d) {
@@ -475,7 +512,8 @@ __global__ void __launch_bounds__(kPThreads) mfma_product_kernel(MfmaParams p) {
         return v;
     };
 
-    // ---- output: direct (one slice) or through the slice partials
+    // ---- output: direct (one slice), or this slice's partial sums for the
+    // epilogue launch (plain stores; the launch boundary makes them visible)
     if (p.S == 1) {
         for (int idx = threadIdx.x; idx < nrb * MB * 64; idx += kPThreads) {
             const int l = idx & 63, mb = (idx >> 6) % MB, rbl = idx / (64 * MB);
@@ -488,51 +526,41 @@ __global__ void __launch_bounds__(kPThreads) mfma_product_kernel(MfmaParams p) {
             }
         }
     } else {
-        float *ypart = p.ypart;
+        float4_t *ypart = reinterpret_cast<float4_t *>(p.ypart);
         for (int idx = threadIdx.x; idx < nrb * MB * 64; idx += kPThreads) {
             const int l = idx & 63, mb = (idx >> 6) % MB, rbl = idx / (64 * MB);
-            if (16 * mb + 4 * (l >> 4) < p.M) {
-                const float4_t v = wave_sum(idx);
-                float *dst = ypart + ((((int64_t)s * p.RB + pb + rbl) * MB + mb) * 64 + l) * 4;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) put(dst + e, v[e]);
-            }
+            if (16 * mb + 4 * (l >> 4) < p.M)
+                ypart[(((int64_t)s * p.RB + pb + rbl) * MB + mb) * 64 + l] = wave_sum(idx);
         }
-        stores_done();
-        __syncthreads();
-        if (threadIdx.x < nrb)
-            s_last[threadIdx.x] = arrive(p.ycnt + pb + threadIdx.x) == (uint32_t)(p.S - 1);
-        __syncthreads();
-        for (int idx = threadIdx.x; idx < nrb * MB * 64; idx += kPThreads) {
-            const int l = idx & 63, mb = (idx >> 6) % MB, rbl = idx / (64 * MB);
-            const int n = (pb + rbl) * 16 + (l & 15), m0 = 16 * mb + 4 * (l >> 4);
-            if (!s_last[rbl] || m0 >= p.M) continue;
-            float4_t v = float4_t{0.f, 0.f, 0.f, 0.f};
-            for (int t0 = 0; t0 < p.S; t0 += kSumBatch) {
-                float part[kSumBatch][4];
-#pragma unroll
-                for (int tt = 0; tt < kSumBatch; ++tt) {
-                    const int t = min(t0 + tt, p.S - 1);
-                    const float *src = ypart + ((((int64_t)t * p.RB + pb + rbl) * MB + mb) * 64 + l) * 4;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) part[tt][e] = get(src + e);
-                }
-#pragma unroll
-                for (int tt = 0; tt < kSumBatch; ++tt)
-                    if (t0 + tt < p.S) {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) v[e] += part[tt][e];
-                    }
-            }
-            if (n < p.N) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (m0 + e < p.M) p.y[(int64_t)(m0 + e) * p.N + n] = f32_to_bf16_rne(p.g * v[e]);
-            }
-        }
-        if (threadIdx.x < nrb && s_last[threadIdx.x]) p.ycnt[pb + threadIdx.x] = 0u;
     }
+}
 
+// =====================================================================
+// launch 3 (K split in S > 1 slices): sum the slices, times g, bf16
+// =====================================================================
+// Thread (row block, m-block, lane) holds the D-layout element quadruple
+// (m = 16 mb + 4 (lane / 16) + e, n = 16 rb + lane % 16).
+template <int MB>
+__global__ void __launch_bounds__(256) mfma_epilogue_kernel(MfmaParams p) {
+    const int idx = blockIdx.x * 256 + threadIdx.x;
+    if (idx >= p.RB * MB * 64) return;
+    const int l = idx & 63, mb = (idx >> 6) % MB, rb = idx / (64 * MB);
+    const int n = rb * 16 + (l & 15), m0 = 16 * mb + 4 * (l >> 4);
+    if (m0 >= p.M || n >= p.N) return;
+    const float4_t *ypart = reinterpret_cast<const float4_t *>(p.ypart);
+    float4_t v = float4_t{0.f, 0.f, 0.f, 0.f};
+    for (int t0 = 0; t0 < p.S; t0 += kSumBatch) {
+        float4_t part[kSumBatch];
+#pragma unroll
+        for (int tt = 0; tt < kSumBatch; ++tt)
+            part[tt] = ypart[((int64_t)min(t0 + tt, p.S - 1) * p.RB + rb) * MB * 64 + (int64_t)mb * 64 + l];
+#pragma unroll
+        for (int tt = 0; tt < kSumBatch; ++tt)
+            if (t0 + tt < p.S) v += part[tt];
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        if (m0 + e < p.M) p.y[(int64_t)(m0 + e) * p.N + n] = f32_to_bf16_rne(p.g * v[e]);
 }
 
 // =====================================================================
@@ -543,7 +571,7 @@ struct MfmaPlan {
     int mb, W, zs, zsteps, chunks, S, cps, RB, Gs, grid, rbw;
     size_t lds;
     // workspace offsets inside the matrix-core area
-    size_t off_zpart, off_zcnt, off_za, off_ypart, off_ycnt, bytes;
+    size_t off_zpart, off_zcnt, off_za, off_ypart, bytes;
 };
 
 size_t align256(size_t b) { return (b + 255) / 256 * 256; }
@@ -552,15 +580,12 @@ MfmaPlan mfma_plan(int M, int N, int K, int r) {
     MfmaPlan q{};
     q.mb = M <= 16 ? 1 : 2;
     q.W = (r + 31) / 32;
-    // z: about kGridTarget workgroups over (word, K-slice), at most
-    // 4 x kZStepsPerWave K-steps per slice
+    // z: K-slices of at most kZWaves x kZStepsPerWave K-steps per word
     const int steps = K / 32;
     if (q.W > 0) {
-        int zs = (kGridTarget + q.W - 1) / q.W;
-        const int zs_min = (steps + 4 * kZStepsPerWave - 1) / (4 * kZStepsPerWave);
-        if (zs < zs_min) zs = zs_min;
-        if (zs > steps) zs = steps;
-        q.zsteps = (steps + zs - 1) / zs;
+        const int per = kZWaves * kZStepsPerWave;
+        q.zs = (steps + per - 1) / per;
+        q.zsteps = (steps + q.zs - 1) / q.zs;
         q.zs = (steps + q.zsteps - 1) / q.zsteps;
     }
     // product: the fewest K-slices whose chunks the 8 waves' activation
@@ -582,19 +607,17 @@ MfmaPlan mfma_plan(int M, int N, int K, int r) {
     q.grid = q.Gs * q.S;
     const int rb_wg = (q.RB + q.Gs - 1) / q.Gs;
     q.rbw = rb_wg <= small ? small : large;
-    q.lds = (size_t)kPWaves * q.rbw * q.mb * 64 * 16;
+    q.lds = (size_t)kPWaves * q.rbw * q.mb * 64 * 16 + (size_t)kPWaves * q.rbw * 16 * 48;
     // workspace
     size_t off = 0;
     q.off_zpart = off;
-    off += (size_t)q.zs * q.W * 1024 * 4;
+    off += (size_t)q.zs * q.W * q.mb * 64 * 8 * 4;
     q.off_zcnt = off;
     off = align256(off + (size_t)q.W * 4);
     q.off_za = off;
     off += (size_t)q.W * q.mb * 2 * 64 * 16;
     q.off_ypart = off;
     if (q.S > 1) off += (size_t)q.S * q.RB * q.mb * 64 * 16;
-    q.off_ycnt = off;
-    if (q.S > 1) off += (size_t)q.RB * 4;
     q.bytes = off > 0 ? align256(off) : 0;
     return q;
 }
@@ -653,7 +676,6 @@ hipError_t launch_gemm_mfma(const GemmArgs &a, hipStream_t stream) {
         p.zcnt = reinterpret_cast<uint32_t *>(ws + q.off_zcnt);
         p.zA = reinterpret_cast<uint32_t *>(ws + q.off_za);
         p.ypart = reinterpret_cast<float *>(ws + q.off_ypart);
-        p.ycnt = reinterpret_cast<uint32_t *>(ws + q.off_ycnt);
     }
     hipError_t e = hipSuccess;
     if (a.r > 0) {
@@ -680,7 +702,15 @@ hipError_t launch_gemm_mfma(const GemmArgs &a, hipStream_t stream) {
         e = allow_lds<2, l2>();
         if (e == hipSuccess) hipLaunchKernelGGL((mfma_product_kernel<2, l2>), grid, block, q.lds, stream, p);
     }
-    return e != hipSuccess ? e : hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = hipGetLastError();
+    if (e != hipSuccess || q.S == 1) return e;
+    const int items = q.RB * q.mb * 64;
+    if (q.mb == 1)
+        hipLaunchKernelGGL(mfma_epilogue_kernel<1>, dim3((items + 255) / 256), dim3(256), 0, stream, p);
+    else
+        hipLaunchKernelGGL(mfma_epilogue_kernel<2>, dim3((items + 255) / 256), dim3(256), 0, stream, p);
+    return hipGetLastError();
 }
 
 }  // namespace biloco

@@ -28,7 +28,9 @@
  *    (uint16_t); NVFP4 element codes are E2M1, two per byte, element 2j in
  *    the LOW nibble of byte j; block scales are E4M3 (OCP "FN": bias 7, max
  *    448, no infinity), one byte per 16 consecutive elements along K.
- *  - Alignment: every pointer must be 16-byte aligned.
+ *  - Alignment: every pointer must be 16-byte aligned.  Reads may cover the
+ *    rest of the 16-byte block that holds an array's last byte (never more,
+ *    never across a page); such bytes do not affect any result.
  *  - Thread safety: the host side keeps no mutable state; concurrent calls
  *    are safe as long as they do not share an output or a workspace.
  */
