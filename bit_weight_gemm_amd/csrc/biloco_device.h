@@ -63,6 +63,49 @@ __device__ __forceinline__ uint32_t e2m1_mag_code(float a, float s) {
            (uint32_t)(a > 5.0f * s);
 }
 
+// ---------------------------------------------------------------- buffer loads
+// Raw buffer resources over the arrays a kernel streams.  A buffer load whose
+// offset is past the resource's size returns zeros without a memory access;
+// loads with nothing to fetch (rows past N, blocks past a row, the K tail)
+// use the offset kOob, so every lane and every path issues the same loads
+// and the hardware wait counts stay exact.
+constexpr int kOob = 0x7FFFFFF0;
+constexpr int kRsrcWord3 = 0x00020000;    // raw 32-bit buffer, gfx9 family
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void *base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+// The offset goes through an empty asm so that it is one VGPR value: left
+// as a select between a computed offset and the constant kOob, the compiler
+// splits the load into two exec-masked loads of the same registers and waits
+// for the first before issuing the second, which serialises the stream.
+__device__ __forceinline__ int opaque(int v) {
+    __asm__ volatile("" : "+v"(v));
+    return v;
+}
+__device__ __forceinline__ u32x4_t load16(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ u32x2_t load8(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+__device__ __forceinline__ uint32_t load2(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t load1(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
+}
+// Streaming variants with the non-temporal cache policy (bit 1 of the
+// cache-policy operand on gfx950), for data read once.
+constexpr int kPolicyNt = 2;
+__device__ __forceinline__ u32x2_t load8_nt(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kPolicyNt));
+}
+__device__ __forceinline__ uint32_t load1_nt(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, kPolicyNt);
+}
+
 // ---------------------------------------------------------------- reductions
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

@@ -41,7 +41,6 @@ namespace biloco {
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kGemvThreads = 512;   // 8 waves per workgroup
 

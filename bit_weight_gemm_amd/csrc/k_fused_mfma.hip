@@ -55,7 +55,6 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kZThreads = 512;          // z kernel: 8 waves
 constexpr int kZWaves = kZThreads / 64;
@@ -146,30 +145,6 @@ __device__ __forceinline__ float get(const float *p) {
     return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void stores_done() { __builtin_amdgcn_s_waitcnt(0); }
-// Raw buffer resources over R and the FP4 activation.  A buffer load whose
-// offset is past the resource's size returns zeros without a memory access;
-// loads with nothing to fetch (rows past N, chunks past a wave's share, the
-// K tail) use the offset kOob, so every lane and every path issues the same
-// loads.
-constexpr int kOob = 0x7FFFFFF0;
-constexpr int kRsrcWord3 = 0x00020000;    // raw 32-bit buffer, gfx9 family
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void *base, int64_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kRsrcWord3);
-}
-// The offset goes through an empty asm so that it is one VGPR value: left
-// as a select between a computed offset and the constant kOob, the compiler
-// splits the load into two exec-masked loads of the same registers and waits
-// for the first before issuing the second, which serialises the stream.
-__device__ __forceinline__ int opaque(int v) {
-    __asm__ volatile("" : "+v"(v));
-    return v;
-}
-__device__ __forceinline__ u32x4_t load16(__amdgpu_buffer_rsrc_t r, int off) {
-    return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
-__device__ __forceinline__ uint32_t load2(__amdgpu_buffer_rsrc_t r, int off) {
-    return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
-}
 __device__ __forceinline__ uint32_t arrive(uint32_t *cnt) {
     return __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
