@@ -151,7 +151,15 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-configs", action="store_true", help="skip the per-config table")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="after the bench, run 10 device-to-device copies of BYTES bytes (the "
+                         "known-size reference for HBM counters)")
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU work: turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
+                         "this script into profiles/traffic_<schedule>_config<c>.json and .md")
     args = ap.parse_args()
+    if args.traffic_summary:
+        return traffic_summary(args)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -223,7 +231,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp4-e2m1/e4m3 weights, bf16 x, fp32 accumulate, bf16 y",
+        "dtype": "f16",
         "data": "synthetic (seeded generators; weights rotated over >= 1.2 GB)",
         "config": {"workload": d["name"], "M": M, "K": K, "N": N, "r": r,
                    "schedule": sched_name, "global_batch": M, "parallelism": "none (1 GPU)"},
@@ -271,6 +279,79 @@ def main() -> int:
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+    if args.copy_calibration:
+        n = args.copy_calibration
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+    return 0
+
+
+def _pmc_rows(directory: str):
+    """(kernel name, counter name, value) of every dispatch in a rocprofv3
+    counter-collection CSV under `directory`."""
+    import csv
+    files = glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no *counter_collection.csv under {directory}")
+    rows = []
+    for f in files:
+        with open(f) as fh:
+            for row in csv.DictReader(fh):
+                rows.append((row["Kernel_Name"], row["Counter_Name"], float(row["Counter_Value"])))
+    return rows
+
+
+def traffic_summary(args) -> int:
+    """HBM bytes per product call from rocprofv3 --pmc runs of this script.
+
+    FETCH_SIZE and WRITE_SIZE are per-dispatch counters in KiB.  They are
+    scaled by the same counter over the known-size copy run at the end
+    (--copy-calibration): factor = copy bytes / (counter of the copy kernel).
+    The product call's traffic is the sum over its kernels (every dispatch
+    name that holds biloco:: but not the activation quantiser or the packer)."""
+    import statistics
+    from bit_weight_gemm_amd import workloads as wl
+    fetch_dir, write_dir = args.traffic_summary
+    cfg = args.config
+    d = wl.make_config(cfg)
+    copy_bytes = args.copy_calibration
+    if not copy_bytes:
+        raise SystemExit("--traffic-summary needs the --copy-calibration size the runs used")
+    res = {}
+    for counter, directory in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = [r for r in _pmc_rows(directory) if r[1] == counter]
+        copies = [v for k, c, v in rows if "copy" in k.lower() or "elementwise" in k.lower()]
+        big = sorted(copies)[-10:] if copies else []
+        if not big:
+            raise SystemExit(f"no copy dispatch found for {counter}")
+        kib_copy = statistics.median(big)
+        factor = copy_bytes / kib_copy
+        per_kernel = {}
+        for k, c, v in rows:
+            if "biloco::" in k and "quant_act" not in k and "pack_signs" not in k:
+                per_kernel.setdefault(k.split("(")[0], []).append(v)
+        kernels = {k: statistics.median(v) * factor for k, v in per_kernel.items()}
+        res[counter] = {"factor_bytes_per_unit": factor, "copy_units_median": kib_copy,
+                        "per_kernel_bytes": kernels, "call_bytes": sum(kernels.values())}
+    bytes_per_call = res["FETCH_SIZE"]["call_bytes"] + res["WRITE_SIZE"]["call_bytes"]
+    sched_name = args.sched_name if hasattr(args, "sched_name") else None
+    from bit_weight_gemm_amd import binding as B
+    sched = args.schedule or B.biloco_default_schedule(d["M"], d["N"], d["K"], d["r"])
+    sched_name = {1: "unfused", 2: "fused_gemv", 3: "fused_mfma"}.get(sched, str(sched))
+    nb = algorithmic_bytes(d["M"], d["N"], d["K"], d["r"])
+    out = {"config": cfg, "schedule": sched_name, "source_hash": source_hash(),
+           "bytes_per_call": round(bytes_per_call), "algorithmic_bytes": nb,
+           "ratio_to_algorithmic": round(bytes_per_call / nb, 4),
+           "fetch": res["FETCH_SIZE"], "write": res["WRITE_SIZE"],
+           "copy_calibration_bytes": copy_bytes}
+    base = os.path.join(ROOT, "profiles", f"traffic_{sched_name}_config{cfg}")
+    with open(base + ".json", "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
     return 0
 
 

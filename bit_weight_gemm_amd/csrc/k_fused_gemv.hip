@@ -62,7 +62,7 @@ struct GemvParams {
     float g;
     int N, K, r, rpad;
     int rows_per_wg;
-    int z_items;            // ceil(r / 8)
+    int z_items;            // ceil(r / kZI)
     uint32_t spin_limit;    // bound of a wait on z; 0 = compute z locally at once
 };
 
@@ -535,11 +535,17 @@ __global__ void __launch_bounds__(kGemvThreads) fused_gemv_kernel(GemvParams p) 
 template <int MM>
 __global__ void __launch_bounds__(kGemvThreads) z_kernel(GemvParams p) {
     __shared__ float s_red[8];
+    // Workgroups are dispatched to the 8 XCDs in turn (b % 8).  The items of
+    // one V word (32 / kZI consecutive items) are mapped to workgroups of one
+    // XCD, so that word's column of V is fetched into one L2 only.  The map
+    // is a permutation of [0, z_items) whatever the dispatch does.
+    const int b = blockIdx.x, G = p.z_items, x = b & 7, q = G >> 3, rem = G & 7;
+    const int item = x * q + (x < rem ? x : rem) + (b >> 3);
     ZInputs<MM> zin;
-    z_prefetch<MM>(p, blockIdx.x, zin);
+    z_prefetch<MM>(p, item, zin);
     float acc[kZI][MM];
-    z_accumulate<MM>(p, blockIdx.x, zin, acc);
-    const int i0 = blockIdx.x * kZI;
+    z_accumulate<MM>(p, item, zin, acc);
+    const int i0 = item * kZI;
     float zs[kZI][MM];
 #pragma unroll
     for (int i = 0; i < kZI; ++i)
