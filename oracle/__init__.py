@@ -55,6 +55,8 @@ def _load():
         lib.oracle_bf16_value.argtypes = [ctypes.c_uint16]
         lib.oracle_quant_act_fp4.restype = None
         lib.oracle_quant_act_fp4.argtypes = [p, i64, i64, p, p]
+        lib.oracle_quant_weight_nvfp4.restype = None
+        lib.oracle_quant_weight_nvfp4.argtypes = [p, i64, i64, p, p, p]
         lib.oracle_pack_signs.restype = None
         lib.oracle_pack_signs.argtypes = [p, i64, i64, p]
         lib.oracle_gemm_lowrank.restype = None
@@ -115,6 +117,18 @@ def quant_act_fp4(x_bf16: np.ndarray):
     scales = np.zeros((M, K // 16), np.uint8)
     _load().oracle_quant_act_fp4(_ptr(x), M, K, _ptr(codes), _ptr(scales))
     return codes, scales
+
+
+def quant_weight_nvfp4(w: np.ndarray):
+    """w: float32 [N][K] -> (codes uint8 [N][K/2], scales uint8 [N][K/16], g float32)."""
+    a = np.ascontiguousarray(w, dtype=np.float32)
+    N, K = a.shape
+    assert K % 16 == 0
+    codes = np.zeros((N, K // 2), np.uint8)
+    scales = np.zeros((N, K // 16), np.uint8)
+    g = np.zeros(1, np.float32)
+    _load().oracle_quant_weight_nvfp4(_ptr(a), N, K, _ptr(codes), _ptr(scales), _ptr(g))
+    return codes, scales, np.float32(g[0])
 
 
 def pack_signs(signs: np.ndarray) -> np.ndarray:

@@ -161,6 +161,65 @@ void oracle_quant_act_fp4(const uint16_t *x, int64_t M, int64_t K,
 }
 
 /* ------------------------------------------------------------------ */
+/* NVFP4 weight quantisation of the residual R                          */
+/* ------------------------------------------------------------------ */
+
+/* w: fp32 [N][K] row-major, K a multiple of 16, finite values.
+ * [BiLoCo, intro and "Decomposition": R is stored in NVFP4; "Kernel": the
+ * launcher takes its codes, its block scales and an fp32 global scale.  The
+ * pages give no recipe; the reading taken here is the plain one in which the
+ * largest block scale lands on the largest E4M3 value:]
+ *   amax = max |w|;  g = fp32(amax / (6 * 448))  (g = 1 when amax == 0)
+ *   per row n, block b of 16 consecutive k:
+ *     a = max |w| over the block;  t = fp32(a / 6);  q = fp32(t / g)
+ *     scale byte s = E4M3(q), nearest, ties to even, saturating at 448
+ *     d = fp32(value(s) * g)
+ *     code_k = E2M1 nearest to fp32(|w_k| / d), ties to the even code,
+ *              saturating at 6, sign of w_k kept; d == 0 gives signed zero
+ * so that w_k ~ g * value(s) * e2m1(code_k).  Every fp32(...) above is one
+ * correctly rounded single-precision operation (C float arithmetic).
+ * Outputs: codes [N][K/2] (even k in the low nibble), scales [N][K/16], *g. */
+void oracle_quant_weight_nvfp4(const float *w, int64_t N, int64_t K,
+                               uint8_t *codes, uint8_t *scales, float *g_out)
+{
+    int64_t n, b, j, total = N * K;
+    float amax = 0.0f, g;
+    for (j = 0; j < total; ++j) {
+        float a = fabsf(w[j]);
+        if (a > amax) amax = a;
+    }
+    g = amax > 0.0f ? amax / 2688.0f : 1.0f;
+    *g_out = g;
+    for (n = 0; n < N; ++n) {
+        for (b = 0; b < K / 16; ++b) {
+            const float *blk = w + n * K + b * 16;
+            float a = 0.0f, t, q, d;
+            unsigned sbyte;
+            for (j = 0; j < 16; ++j)
+                if (fabsf(blk[j]) > a) a = fabsf(blk[j]);
+            t = a / 6.0f;
+            q = t / g;
+            sbyte = oracle_e4m3_encode((double)q);
+            scales[n * (K / 16) + b] = (uint8_t)sbyte;
+            d = (float)oracle_e4m3_value(sbyte) * g;
+            for (j = 0; j < 16; j += 2) {
+                unsigned c[2], h;
+                for (h = 0; h < 2; ++h) {
+                    float x = blk[j + h];
+                    unsigned sign = signbit(x) ? 8u : 0u;
+                    if (d == 0.0f) { c[h] = sign; continue; }
+                    {
+                        float tq = fabsf(x) / d;
+                        c[h] = sign | oracle_e2m1_encode((double)tq, 1.0);
+                    }
+                }
+                codes[(n * K + b * 16 + j) / 2] = (uint8_t)(c[0] | (c[1] << 4));
+            }
+        }
+    }
+}
+
+/* ------------------------------------------------------------------ */
 /* Sign packing                                                         */
 /* ------------------------------------------------------------------ */
 
