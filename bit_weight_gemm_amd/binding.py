@@ -28,7 +28,8 @@ BILOCO_SCHED_FUSED_MFMA = 3
 
 EXPORTED = ["biloco_status_string", "biloco_pack_signs", "biloco_quant_act_fp4",
             "biloco_gemm_workspace_bytes", "biloco_gemm_lowrank", "biloco_gemm_lowrank_sched",
-            "biloco_gemm_check", "biloco_default_schedule", "biloco_schedules_for"]
+            "biloco_gemm_check", "biloco_default_schedule", "biloco_schedules_for",
+            "biloco_quant_weight_nvfp4", "biloco_quant_weight_workspace_bytes"]
 
 _lib = None
 
@@ -55,6 +56,10 @@ def lib() -> ctypes.CDLL:
         L.biloco_pack_signs.argtypes = [p, i64, i64, p, p]
         L.biloco_quant_act_fp4.restype = st
         L.biloco_quant_act_fp4.argtypes = [p, i32, i32, p, p, p]
+        L.biloco_quant_weight_nvfp4.restype = st
+        L.biloco_quant_weight_nvfp4.argtypes = [p, i64, i64, p, p, p, p, sz, p]
+        L.biloco_quant_weight_workspace_bytes.restype = st
+        L.biloco_quant_weight_workspace_bytes.argtypes = [i64, i64, ctypes.POINTER(sz)]
         L.biloco_gemm_workspace_bytes.restype = st
         L.biloco_gemm_workspace_bytes.argtypes = [i32, i32, i32, i32, ctypes.POINTER(sz)]
         gemm = [p, p, p, p, p, ctypes.c_float, p, p, p, i32, i32, i32, i32, p, p, sz]
@@ -121,6 +126,34 @@ def biloco_quant_act_fp4(x_bf16: torch.Tensor, codes=None, scales=None, stream=N
     _ok(lib().biloco_quant_act_fp4(_p(x_bf16), M, K, _p(codes), _p(scales), _stream(stream)),
         "biloco_quant_act_fp4")
     return codes, scales
+
+
+def biloco_quant_weight_workspace_bytes(N: int, K: int) -> int:
+    out = ctypes.c_size_t(0)
+    _ok(lib().biloco_quant_weight_workspace_bytes(N, K, ctypes.byref(out)),
+        "biloco_quant_weight_workspace_bytes")
+    return int(out.value)
+
+
+def biloco_quant_weight_nvfp4(w: torch.Tensor, codes=None, scales=None, g=None, workspace=None,
+                              stream=None):
+    """w fp32 [N][K] -> (codes uint8 [N][K/2], scales uint8 [N][K/16], g fp32 [1]), all on w's device."""
+    N, K = w.shape
+    dev = w.device
+    if codes is None:
+        codes = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty((N, K // 16), dtype=torch.uint8, device=dev)
+    if g is None:
+        g = torch.empty(4, dtype=torch.float32, device=dev)[:1]
+    nws = biloco_quant_weight_workspace_bytes(N, K)
+    if workspace is None:
+        workspace = torch.empty(nws, dtype=torch.uint8, device=dev)
+    _ok(lib().biloco_quant_weight_nvfp4(_p(w), N, K, _p(codes), _p(scales), _p(g), _p(workspace),
+                                        workspace.numel() * workspace.element_size(),
+                                        _stream(stream)),
+        "biloco_quant_weight_nvfp4")
+    return codes, scales, g
 
 
 def biloco_gemm_workspace_bytes(M: int, N: int, K: int, r: int) -> int:

@@ -9,6 +9,9 @@ using namespace biloco;
 
 namespace {
 
+// Largest weight matrix (elements) the quantiser takes: 2^38 fp32 values (1 TiB).
+constexpr int64_t kMaxWeightElems = (int64_t)1 << 38;
+
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
@@ -82,6 +85,35 @@ biloco_status biloco_quant_act_fp4(const uint16_t *x_bf16, int32_t M, int32_t K,
         overlaps(a_codes, nc, a_scales, ns))
         return BILOCO_ERR_INVALID_VALUE;
     return launch_quant_act(x_bf16, M, K, a_codes, a_scales, stream) == hipSuccess
+               ? BILOCO_OK
+               : BILOCO_ERR_HIP;
+}
+
+biloco_status biloco_quant_weight_workspace_bytes(int64_t N, int64_t K, size_t *bytes) {
+    if (!bytes || N < 1 || K < 16 || K % 16 != 0) return BILOCO_ERR_INVALID_VALUE;
+    if (N > kMaxWeightElems / K) return BILOCO_ERR_UNSUPPORTED;
+    *bytes = quant_weight_ws_bytes();
+    return BILOCO_OK;
+}
+
+biloco_status biloco_quant_weight_nvfp4(const float *w, int64_t N, int64_t K, uint8_t *codes,
+                                        uint8_t *scales, float *g_out, void *workspace,
+                                        size_t workspace_bytes, hipStream_t stream) {
+    size_t need = 0;
+    biloco_status st = biloco_quant_weight_workspace_bytes(N, K, &need);
+    if (st != BILOCO_OK) return st;
+    if (!w || !codes || !scales || !g_out || !workspace) return BILOCO_ERR_INVALID_VALUE;
+    if (!aligned16(w) || !aligned16(codes) || !aligned16(scales) || !aligned16(g_out) ||
+        !aligned16(workspace))
+        return BILOCO_ERR_INVALID_VALUE;
+    if (workspace_bytes < need) return BILOCO_ERR_WORKSPACE_TOO_SMALL;
+    const size_t n = (size_t)N * (size_t)K;
+    struct { const void *p; size_t n; } arr[] = {
+        {w, 4 * n}, {codes, n / 2}, {scales, n / 16}, {g_out, 4}, {workspace, need}};
+    for (int i = 0; i < 5; ++i)
+        for (int j = i + 1; j < 5; ++j)
+            if (overlaps(arr[i].p, arr[i].n, arr[j].p, arr[j].n)) return BILOCO_ERR_INVALID_VALUE;
+    return launch_quant_weight(w, N, K, codes, scales, g_out, workspace, stream) == hipSuccess
                ? BILOCO_OK
                : BILOCO_ERR_HIP;
 }

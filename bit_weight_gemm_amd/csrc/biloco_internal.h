@@ -56,6 +56,9 @@ hipError_t launch_pack_signs(const int8_t *signs, int64_t rows, int64_t cols, ui
                              hipStream_t stream);
 hipError_t launch_quant_act(const uint16_t *x, int M, int K, uint8_t *codes, uint8_t *scales,
                             hipStream_t stream);
+size_t quant_weight_ws_bytes();   // pass-1 partials of the weight quantiser
+hipError_t launch_quant_weight(const float *w, int64_t N, int64_t K, uint8_t *codes,
+                               uint8_t *scales, float *g_out, void *ws, hipStream_t stream);
 hipError_t launch_gemm_unfused(const GemmArgs &a, hipStream_t stream);
 hipError_t launch_gemm_fused_gemv(const GemmArgs &a, hipStream_t stream);
 hipError_t launch_gemm_gemv_two_launch(const GemmArgs &a, hipStream_t stream);

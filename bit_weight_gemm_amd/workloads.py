@@ -17,6 +17,11 @@ Recipe (fixed draw order, so the r = 0 run shares x and R with the r > 0 run):
   6. U = 1 - 2 * rng.integers(0, 2, (N, r), dtype=int8)
      V = 1 - 2 * rng.integers(0, 2, (K, r), dtype=int8)
   7. alpha_i = bf16(c * i^-0.5), i = 1..r
+
+Residual matrices for the weight quantiser (make_residual): fp32
+  w = sigma * rng.standard_normal((N, K), float32), and with outliers
+  floor(0.01 K) columns (rng.choice) scaled by 20, the heavy-tailed input
+  channels of a language-model layer.
 """
 from __future__ import annotations
 
@@ -82,6 +87,17 @@ def make_inputs(M: int, K: int, N: int, r: int, seed: int, c: float = 0.05,
         alpha = np.zeros((0,), np.uint16)
     return dict(M=M, K=K, N=N, r=r, x=x, wcode=wcode, wcodes_packed=pack_nibbles(wcode),
                 wscales=ws, g=np.float32(g), U=U, V=V, alpha=alpha)
+
+
+def make_residual(N: int, K: int, seed: int, sigma: float = 0.02,
+                  outliers: bool = False) -> np.ndarray:
+    """Seeded fp32 residual R [N][K] for the NVFP4 weight quantiser."""
+    rng = np.random.default_rng(seed)
+    w = (sigma * rng.standard_normal((N, K), dtype=np.float32)).astype(np.float32)
+    if outliers:
+        idx = rng.choice(K, max(1, int(np.floor(0.01 * K))), replace=False)
+        w[:, idx] *= np.float32(20.0)
+    return w
 
 
 def make_config(idx: int, r: int | None = None) -> dict:

@@ -89,6 +89,40 @@ biloco_status biloco_pack_signs(const int8_t *signs, int64_t rows, int64_t cols,
 biloco_status biloco_quant_act_fp4(const uint16_t *x_bf16, int32_t M, int32_t K,
                                    uint8_t *a_codes, uint8_t *a_scales, hipStream_t stream);
 
+/* NVFP4 quantisation of a weight matrix, the residual R (BiLoCo intro and
+ * section "Decomposition": R is stored in NVFP4; section "Kernel": the
+ * product takes R's E2M1 codes, its E4M3 block scales and an fp32 global
+ * scale).  The pages give no rounding recipe; this one puts the largest
+ * block scale on the largest E4M3 value:
+ *   g = fp32(max|w| / 2688)   (2688 = 6 * 448; g = 1 when every w is 0)
+ *   per row n and block b of 16 consecutive k, with a = max |w| over it:
+ *     scale[n][b] = E4M3(fp32(fp32(a / 6) / g)), nearest, ties to even,
+ *                   saturating at 448
+ *     d = fp32(e4m3(scale[n][b]) * g)
+ *     code = E2M1(fp32(|w| / d)), nearest, ties to the even code, saturating
+ *            at 6, sign of w kept (also for values that round to zero);
+ *            d == 0 gives signed-zero codes
+ *   each fp32(...) one correctly rounded single-precision operation, so that
+ *   w ~ g * e4m3(scale) * e2m1(code), the operand form biloco_gemm_lowrank
+ *   takes as (w_codes, w_scales, w_global_scale).
+ *   w        [N][K] fp32, finite (input)
+ *   codes    [N][K/2] uint8  (even k in the low nibble)
+ *   scales   [N][K/16] uint8 (E4M3)
+ *   g_out    one fp32 (device memory)
+ *   workspace >= biloco_quant_weight_workspace_bytes(...) bytes of device
+ *          memory; no fill needed (every call writes it before reading it);
+ *          not shared by calls that can run at the same time.
+ * N >= 1, K >= 16, K % 16 == 0 (biloco_gemm_lowrank further needs K % 32 == 0);
+ * N * K <= 2^38.  No two of the five arrays may overlap.  Two launches on
+ * `stream`.  Bit-exact. */
+biloco_status biloco_quant_weight_nvfp4(const float *w, int64_t N, int64_t K, uint8_t *codes,
+                                        uint8_t *scales, float *g_out, void *workspace,
+                                        size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace biloco_quant_weight_nvfp4 needs (a few KiB, never 0).
+ * Same shape rules. */
+biloco_status biloco_quant_weight_workspace_bytes(int64_t N, int64_t K, size_t *bytes);
+
 /* Bytes of device workspace biloco_gemm_lowrank needs for this shape, enough
  * for every schedule the shape allows.  May be 0 (then workspace may be
  * NULL).  Same argument rules as biloco_gemm_lowrank. */

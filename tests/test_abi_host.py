@@ -119,3 +119,31 @@ def test_prep_entry_points_reject_before_hip():
     assert L.biloco_quant_act_fp4(None, 1, 64, A * 2, A * 3, None) == B.BILOCO_ERR_INVALID_VALUE
     # codes overlapping x
     assert L.biloco_quant_act_fp4(A, 1, 64, A + 64, A * 3, None) == B.BILOCO_ERR_INVALID_VALUE
+
+
+def test_quant_weight_rejects_before_hip():
+    L = B.lib()
+    A = 1 << 36
+    ws = B.biloco_quant_weight_workspace_bytes(64, 64)
+    assert 0 < ws <= 64 * 1024
+    ok = (A, 64, 64, A * 2, A * 3, A * 4, A * 5, ws, None)
+
+    def call(**kw):
+        names = ["w", "N", "K", "codes", "scales", "g", "ws", "wsb", "stream"]
+        args = dict(zip(names, ok))
+        args.update(kw)
+        return L.biloco_quant_weight_nvfp4(*[args[n] for n in names])
+
+    assert call(N=0) == B.BILOCO_ERR_INVALID_VALUE
+    assert call(K=8) == B.BILOCO_ERR_INVALID_VALUE
+    assert call(K=40) == B.BILOCO_ERR_INVALID_VALUE
+    assert call(N=1 << 30, K=1 << 10) == B.BILOCO_ERR_UNSUPPORTED
+    for name in ["w", "codes", "scales", "g", "ws"]:
+        assert call(**{name: None}) == B.BILOCO_ERR_INVALID_VALUE, name
+        assert call(**{name: ok[["w", "N", "K", "codes", "scales", "g", "ws"].index(name)] + 4}) \
+            == B.BILOCO_ERR_INVALID_VALUE, name
+    assert call(wsb=ws - 1) == B.BILOCO_ERR_WORKSPACE_TOO_SMALL
+    assert call(codes=A + 256) == B.BILOCO_ERR_INVALID_VALUE          # codes inside w
+    assert call(g=A * 3 + 16) == B.BILOCO_ERR_INVALID_VALUE           # g inside scales
+    with pytest.raises(B.BilocoError):
+        B.biloco_quant_weight_workspace_bytes(3, 24)

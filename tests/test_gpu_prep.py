@@ -12,6 +12,8 @@ import torch
 import oracle
 from bit_weight_gemm_amd import binding as B
 from bit_weight_gemm_amd import workloads as wl
+from bit_weight_gemm_amd.problem import DeviceProblem
+from util import check_y
 
 pytestmark = pytest.mark.gpu
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -109,3 +111,96 @@ def test_quant_random_binades_and_zeros():
     rc, rs = oracle.quant_act_fp4(x)
     np.testing.assert_array_equal(s, rs)
     np.testing.assert_array_equal(c, rc)
+
+
+# ---------------------------------------------------------------- NVFP4 weights
+def _gpu_wquant(w: np.ndarray):
+    t = torch.from_numpy(np.ascontiguousarray(w, dtype=np.float32)).cuda()
+    c, s, g = B.biloco_quant_weight_nvfp4(t)
+    torch.cuda.synchronize()
+    return c.cpu().numpy(), s.cpu().numpy(), np.float32(g.cpu().numpy()[0])
+
+
+def _check_wquant(w: np.ndarray):
+    c, s, g = _gpu_wquant(w)
+    rc, rs, rg = oracle.quant_weight_nvfp4(w)
+    assert g.tobytes() == rg.tobytes(), (g, rg)
+    np.testing.assert_array_equal(s, rs)
+    np.testing.assert_array_equal(c, rc)
+
+
+# (N, K): the decode shapes' R, a ragged tail tile of both passes, a single
+# block, fewer float4 than one wave, and a shape where every workgroup of
+# both passes loops over several tiles
+@pytest.mark.parametrize("N,K,outliers", [(5120, 5120, False), (13824, 5120, True),
+                                          (5120, 13824, False), (33, 528, False), (1, 16, False),
+                                          (3, 48, True), (8192, 1040, True)])
+def test_wquant_bit_exact(N, K, outliers):
+    _check_wquant(wl.make_residual(N, K, seed=N + K, outliers=outliers))
+
+
+def test_wquant_golden_rows():
+    cases, cur = [], None
+    with open(os.path.join(GOLDEN, "quant_weight_rows.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, rest = line.split(None, 1)
+            if key == "case":
+                cur = {}
+                cases.append(cur)
+            else:
+                cur[key] = rest.split()
+    for case in cases:
+        w = np.array([[float(t) for t in case["w"]]], np.float32)
+        c, s, g = _gpu_wquant(w)
+        assert float(g) == float(case["g"][0])
+        assert s[0].tolist() == [int(t, 16) for t in case["scales"]]
+        assert c[0].tolist() == [int(t, 16) for t in case["codes"]]
+
+
+def test_wquant_zero_and_tiny_magnitudes():
+    w = np.zeros((16, 256), np.float32)
+    w[2, 7] = -0.0
+    _check_wquant(w)                                  # g = 1, zero scales, signed zeros
+    rng = np.random.default_rng(5)
+    # g either side of the fast path's limit 2^-90, g normal but tiny, g
+    # subnormal, subnormal inputs, and magnitudes near the top of fp32
+    for scale in (1e-22, 5e-25, 1e-30, 1e-36, 1e-40, 1e37):
+        _check_wquant((scale * rng.standard_normal((64, 512))).astype(np.float32))
+
+
+def test_wquant_every_block_scale_and_ties():
+    # one row per positive E4M3 scale byte: its block maximum is 6 * scale * g
+    # with g fixed by a first block of amax 2688, and the other entries are
+    # multiples of d on the E2M1 midpoints (exact ties) and just beside them
+    sv = torch.arange(1, 0x7F, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float32).numpy()
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], np.float32)
+    rows = []
+    for d in sv:
+        blk = np.zeros(32, np.float32)
+        blk[0] = 2688.0
+        b = blk[16:]
+        b[0] = 6.0 * d
+        b[1:8] = mids * d
+        b[8:15] = -np.nextafter(mids * d, np.float32(np.inf))
+        b[15] = np.nextafter(mids[3] * d, np.float32(0))
+        rows.append(blk)
+    _check_wquant(np.stack(rows))
+
+
+def test_wquant_feeds_gemm():
+    # the quantiser's output is the product's residual operand (r = 0 and r > 0)
+    for cfg in (0, 1):
+        d = wl.make_config(cfg)
+        w = wl.make_residual(d["N"], d["K"], seed=11 + cfg)
+        c, s, g = _gpu_wquant(w)
+        d["wcodes_packed"], d["wscales"], d["g"] = c, s, g
+        d["wcode"] = np.stack([c & 15, c >> 4], axis=-1).reshape(d["N"], d["K"])
+        y_ref = oracle.gemm_lowrank(d["x"], d["wcode"], d["wscales"], d["g"], d["V"], d["U"],
+                                    d["alpha"])
+        p = DeviceProblem(d)
+        p.gemm()
+        torch.cuda.synchronize()
+        check_y(p.y_float(), y_ref, f"config {cfg} with quantised R")
