@@ -25,6 +25,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, 10^9 B/s
 ROT_BYTES = 1.2e9              # distinct weight bytes a timed graph walks through
+SCHED_NAMES = {1: "unfused", 2: "fused_gemv", 3: "fused_mfma", 4: "composed"}
 METRIC = "fused GEMM µs/call + effective HBM GB/s (% peak) at M=1..32, r=512"
 
 
@@ -120,6 +121,36 @@ def gemm_call_time(prob, sched: int, rot: Rotation | None, calls: int) -> float:
     return t
 
 
+def weight_quant_table() -> dict:
+    """biloco_quant_weight_nvfp4 on fp32 residuals of the decode weight shapes:
+    time per call (a graph of 20 calls over 4 copies of the matrix, 420+ MB),
+    and algorithmic bytes (read w once, write codes and scales) per second."""
+    import torch
+    from bit_weight_gemm_amd import binding as B
+    from bit_weight_gemm_amd import workloads as wl
+    res = {}
+    for N, K in ((5120, 5120), (13824, 5120)):
+        w0 = torch.from_numpy(wl.make_residual(N, K, seed=N + K, outliers=True)).cuda()
+        ws = [w0] + [w0.clone() for _ in range(3)]
+        c = torch.empty((N, K // 2), dtype=torch.uint8, device="cuda")
+        s = torch.empty((N, K // 16), dtype=torch.uint8, device="cuda")
+        g = torch.empty(4, dtype=torch.float32, device="cuda")[:1]
+        wsp = torch.empty(B.biloco_quant_weight_workspace_bytes(N, K), dtype=torch.uint8,
+                          device="cuda")
+        for i in range(4):
+            B.biloco_quant_weight_nvfp4(ws[i], c, s, g, wsp)
+        torch.cuda.synchronize()
+        t, _ = time_graph(lambda i, st: B.biloco_quant_weight_nvfp4(ws[i % 4], c, s, g, wsp,
+                                                                    stream=st), 20)
+        alg = N * K * 4 + N * K // 2 + N * K // 16 + 4
+        res[f"{N}x{K}"] = {"us_per_call": round(t * 1e6, 2), "GBps": round(alg / t / 1e9, 1),
+                           "pct_peak": round(100 * alg / t / 1e9 / PEAK_HBM_GBS, 2),
+                           "bytes_per_call": alg, "passes_over_w": 2}
+        del ws, w0, c, s
+        torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(cfg: int, seconds: float):
     import numpy as np
     import oracle
@@ -180,7 +211,7 @@ def main() -> int:
     prob = DeviceProblem(d)
     M, N, K, r = prob.M, prob.N, prob.K, prob.r
     sched = args.schedule or B.biloco_default_schedule(M, N, K, r)
-    sched_name = {1: "unfused", 2: "fused_gemv", 3: "fused_mfma"}.get(sched, str(sched))
+    sched_name = SCHED_NAMES.get(sched, str(sched))
     n_sets = max(2, int(ROT_BYTES // weight_bytes(prob)) + 1)
     rot = Rotation(prob, min(n_sets, args.steps))
 
@@ -265,16 +296,20 @@ def main() -> int:
             rc = Rotation(pc, max(2, int(ROT_BYTES // weight_bytes(pc)) + 1))
             calls = 100 if pc.M <= 2 else 20
             tc = gemm_call_time(pc, sc, rc, calls)
+            # the same product as separate launches (plain product, z, correction)
+            tcomp = gemm_call_time(pc, B.BILOCO_SCHED_COMPOSED, rc, calls)
             bc = algorithmic_bytes(pc.M, pc.N, pc.K, pc.r)
             table[f"config{c}"] = {"M": pc.M, "K": pc.K, "N": pc.N, "r": pc.r,
-                                   "schedule": {1: "unfused", 2: "fused_gemv",
-                                                3: "fused_mfma"}.get(sc, sc),
+                                   "schedule": SCHED_NAMES.get(sc, sc),
                                    "us_per_call": round(tc * 1e6, 3),
                                    "GBps": round(bc / tc / 1e9, 1),
-                                   "pct_peak": round(100 * bc / tc / 1e9 / PEAK_HBM_GBS, 2)}
+                                   "pct_peak": round(100 * bc / tc / 1e9 / PEAK_HBM_GBS, 2),
+                                   "composed_us_per_call": round(tcomp * 1e6, 3),
+                                   "speedup_vs_composed": round(tcomp / tc, 3)}
             del rc, pc
             torch.cuda.empty_cache()
         out["per_config"] = table
+        out["weight_quant"] = weight_quant_table()
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
@@ -341,7 +376,7 @@ def traffic_summary(args) -> int:
     sched_name = args.sched_name if hasattr(args, "sched_name") else None
     from bit_weight_gemm_amd import binding as B
     sched = args.schedule or B.biloco_default_schedule(d["M"], d["N"], d["K"], d["r"])
-    sched_name = {1: "unfused", 2: "fused_gemv", 3: "fused_mfma"}.get(sched, str(sched))
+    sched_name = SCHED_NAMES.get(sched, str(sched))
     nb = algorithmic_bytes(d["M"], d["N"], d["K"], d["r"])
     out = {"config": cfg, "schedule": sched_name, "source_hash": source_hash(),
            "bytes_per_call": round(bytes_per_call), "algorithmic_bytes": nb,

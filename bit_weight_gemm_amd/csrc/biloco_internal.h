@@ -21,6 +21,7 @@ struct GemmArgs {
     uint16_t *y;
     void *ws;
     size_t ws_bytes;
+    float *yf = nullptr;    // if set: fp32 results here instead of bf16 y (r = 0 products only)
 };
 
 // Workspace layout (byte offsets).
@@ -32,6 +33,7 @@ struct GemmArgs {
 //   then (256-aligned) the matrix-core schedule's area: z slice partials,
 //                     per-word counters, z/g operands, K-slice partials of y
 //                     and per-row-block counters (sized by mfma_ws_bytes)
+//   then (256-aligned, r > 0) the separate-launch schedule's fp32 product [M][N]
 constexpr int kGemvMaxWorkgroups = 8192;
 constexpr size_t kWsHeaderBytes = 64 * 1024;
 inline int rpad32(int r) { return (r + 31) / 32 * 32; }
@@ -46,10 +48,15 @@ inline size_t ws_mfma_offset(int M, int r) {
 }
 bool mfma_supported(int M, int N, int K, int r);     // shapes the matrix-core schedule handles
 size_t mfma_ws_bytes(int M, int N, int K, int r);    // its workspace area (0 if none is needed)
+// The separate-launch schedule's fp32 product [M][N] (r > 0 only) follows.
+inline size_t ws_yf_offset(int M, int N, int K, int r) {
+    return (ws_mfma_offset(M, r) + mfma_ws_bytes(M, N, K, r) + 255) / 256 * 256;
+}
 // Workspace for every schedule of the shape: nothing for r = 0 unless the
 // matrix-core schedule splits K.
 inline size_t ws_total_bytes(int M, int N, int K, int r) {
-    return ws_mfma_offset(M, r) + mfma_ws_bytes(M, N, K, r);
+    return r > 0 ? ws_yf_offset(M, N, K, r) + (size_t)4 * (size_t)M * (size_t)N
+                 : ws_mfma_offset(M, r) + mfma_ws_bytes(M, N, K, r);
 }
 
 hipError_t launch_pack_signs(const int8_t *signs, int64_t rows, int64_t cols, uint32_t *packed,
@@ -62,7 +69,13 @@ hipError_t launch_quant_weight(const float *w, int64_t N, int64_t K, uint8_t *co
 hipError_t launch_gemm_unfused(const GemmArgs &a, hipStream_t stream);
 hipError_t launch_gemm_fused_gemv(const GemmArgs &a, hipStream_t stream);
 hipError_t launch_gemm_gemv_two_launch(const GemmArgs &a, hipStream_t stream);
+hipError_t launch_z_gemv(const GemmArgs &a, float *z, hipStream_t stream);   // M <= 2
 bool gemv_supported(int M, int N, int K, int r);   // shapes the one-launch vector-ALU schedule handles
 hipError_t launch_gemm_mfma(const GemmArgs &a, hipStream_t stream);
+// z = alpha (.) (x . V) as plain fp32 [M][rpad32(r)] at z (r > 0)
+hipError_t launch_z_fp32(const GemmArgs &a, float *z, hipStream_t stream);
+constexpr int kComposedMaxRank = 1024;   // the correction's lookup tables fit 32 KiB of LDS
+bool composed_supported(int M, int N, int K, int r);
+hipError_t launch_gemm_composed(const GemmArgs &a, hipStream_t stream);
 
 }  // namespace biloco

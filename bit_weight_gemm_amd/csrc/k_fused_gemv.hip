@@ -54,6 +54,7 @@ struct GemvParams {
     const uint32_t *u;
     const uint16_t *alpha;
     uint16_t *y;
+    float *yf;              // if set: fp32 results here instead of y
     uint32_t *epoch;        // workspace header word 0
     uint32_t *seen;         // workspace header flags, one per workgroup
     uint64_t *zt;           // z as (value | tag << 32), [M][rpad]  (one launch)
@@ -508,14 +509,16 @@ __global__ void __launch_bounds__(kGemvThreads) fused_gemv_kernel(GemvParams p) 
         add_correction<MM, R, QMAX>(p, s_z, uw, part);
     }
 
-    // 10. one reduction per row and m, then the bf16 store
+    // 10. one reduction per row and m, then the bf16 (or fp32) store
 #pragma unroll
     for (int rr = 0; rr < R; ++rr)
 #pragma unroll
         for (int m = 0; m < MM; ++m) {
             const float sum = wave_sum_dpp(part[rr][m]);
-            if (lane == 0 && rr < nrows)
-                p.y[(int64_t)m * p.N + row0 + rr] = f32_to_bf16_rne(sum);
+            if (lane == 0 && rr < nrows) {
+                if (p.yf) p.yf[(int64_t)m * p.N + row0 + rr] = sum;
+                else p.y[(int64_t)m * p.N + row0 + rr] = f32_to_bf16_rne(sum);
+            }
         }
 
     // 11. one launch: workgroup 0 advances the epoch once every other
@@ -655,6 +658,7 @@ hipError_t launch_gemv(const GemmArgs &a, bool two_launch, hipStream_t stream) {
     p.u = a.u;
     p.alpha = a.alpha;
     p.y = a.y;
+    p.yf = a.yf;
     p.g = a.g;
     p.N = a.N;
     p.K = a.K;
@@ -697,6 +701,26 @@ hipError_t launch_gemv(const GemmArgs &a, bool two_launch, hipStream_t stream) {
     }
 }
 }  // namespace
+
+// The z kernel alone (plain fp32 z at z), for compositions of separate launches.
+hipError_t launch_z_gemv(const GemmArgs &a, float *z, hipStream_t stream) {
+    if (a.M < 1 || a.M > 2 || a.r < 1) return hipErrorNotSupported;
+    GemvParams p{};
+    p.x = a.x;
+    p.v = a.v;
+    p.alpha = a.alpha;
+    p.N = a.N;
+    p.K = a.K;
+    p.r = a.r;
+    p.rpad = rpad32(a.r);
+    p.z_items = (a.r + kZI - 1) / kZI;
+    p.zf_out = z;
+    if (a.M == 1)
+        hipLaunchKernelGGL(z_kernel<1>, dim3(p.z_items), dim3(kGemvThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL(z_kernel<2>, dim3(p.z_items), dim3(kGemvThreads), 0, stream, p);
+    return hipGetLastError();
+}
 
 hipError_t launch_gemm_fused_gemv(const GemmArgs &a, hipStream_t stream) {
     return launch_gemv(a, false, stream);

@@ -91,6 +91,7 @@ struct MfmaParams {
     const uint32_t *u;
     const uint16_t *alpha;
     uint16_t *y;
+    float *yf;              // if set: fp32 results here instead of y
     float g;
     int M, N, K, r, W;          // W = ceil(r / 32)
     // z kernel
@@ -102,6 +103,12 @@ struct MfmaParams {
     int S, cps, chunks, RB, Gs;
     float *ypart;               // [S][RB][MB][64 lanes][4] (D layout)
 };
+
+// One output element: bf16 into y, or fp32 into yf when the caller asked for it.
+__device__ __forceinline__ void store_y(const MfmaParams &p, int64_t idx, float v) {
+    if (p.yf) p.yf[idx] = v;
+    else p.y[idx] = f32_to_bf16_rne(v);
+}
 
 __device__ __forceinline__ float4_t mfma_f16(const u32x4_t &a, const u32x4_t &b, float4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a),
@@ -497,7 +504,7 @@ __global__ void __launch_bounds__(kPThreads) mfma_product_kernel(MfmaParams p) {
             if (n < p.N) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    if (m0 + e < p.M) p.y[(int64_t)(m0 + e) * p.N + n] = f32_to_bf16_rne(p.g * v[e]);
+                    if (m0 + e < p.M) store_y(p, (int64_t)(m0 + e) * p.N + n, p.g * v[e]);
             }
         }
     } else {
@@ -535,7 +542,7 @@ __global__ void __launch_bounds__(256) mfma_epilogue_kernel(MfmaParams p) {
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-        if (m0 + e < p.M) p.y[(int64_t)(m0 + e) * p.N + n] = f32_to_bf16_rne(p.g * v[e]);
+        if (m0 + e < p.M) store_y(p, (int64_t)(m0 + e) * p.N + n, p.g * v[e]);
 }
 
 // =====================================================================
@@ -632,6 +639,7 @@ hipError_t launch_gemm_mfma(const GemmArgs &a, hipStream_t stream) {
     p.u = a.u;
     p.alpha = a.alpha;
     p.y = a.y;
+    p.yf = a.yf;
     p.g = a.g;
     p.M = a.M;
     p.N = a.N;

@@ -56,7 +56,8 @@ __global__ void __launch_bounds__(256)
 gemv_unfused_kernel(const uint8_t *__restrict__ a_codes, const uint8_t *__restrict__ a_scales,
                     const uint8_t *__restrict__ w_codes, const uint8_t *__restrict__ w_scales,
                     float g, const uint32_t *__restrict__ u, const float *__restrict__ z, int M,
-                    int N, int K, int r, int rpad, uint16_t *__restrict__ y) {
+                    int N, int K, int r, int rpad, uint16_t *__restrict__ y,
+                    float *__restrict__ yf) {
     const int lane = threadIdx.x & 63;
     const int64_t gw = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 6;
     const int64_t nw = (int64_t)gridDim.x * 4;
@@ -86,9 +87,19 @@ gemv_unfused_kernel(const uint8_t *__restrict__ a_codes, const uint8_t *__restri
                 cacc += ((word >> (i & 31)) & 1u) ? -zz : zz;
             }
             const float gs = wave_sum(acc), cs = wave_sum(cacc);
-            if (lane == 0) y[(int64_t)m * N + n] = f32_to_bf16_rne(g * gs + cs);
+            if (lane == 0) {
+                if (yf) yf[(int64_t)m * N + n] = g * gs + cs;
+                else y[(int64_t)m * N + n] = f32_to_bf16_rne(g * gs + cs);
+            }
         }
     }
+}
+
+hipError_t launch_z_fp32(const GemmArgs &a, float *z, hipStream_t stream) {
+    if (gemv_supported(a.M, a.N, a.K, a.r)) return launch_z_gemv(a, z, stream);
+    hipLaunchKernelGGL(z_unfused_kernel, dim3(rpad32(a.r) / 32, a.M), dim3(256), 0, stream, a.x,
+                       a.v, a.alpha, a.K, a.r, rpad32(a.r), z);
+    return hipGetLastError();
 }
 
 hipError_t launch_gemm_unfused(const GemmArgs &a, hipStream_t stream) {
@@ -108,7 +119,7 @@ hipError_t launch_gemm_unfused(const GemmArgs &a, hipStream_t stream) {
     const unsigned grid = (unsigned)(blocks < 4096 ? blocks : 4096);
     hipLaunchKernelGGL(gemv_unfused_kernel, dim3(grid), dim3(256), 0, stream, a.a_codes,
                        a.a_scales, a.w_codes, a.w_scales, a.g, a.u, z, a.M, a.N, a.K, a.r, rpad,
-                       a.y);
+                       a.y, a.yf);
     return hipGetLastError();
 }
 

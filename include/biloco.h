@@ -61,6 +61,10 @@ typedef int32_t biloco_status;
 #define BILOCO_SCHED_FUSED_MFMA  3  /* matrix-core products for any M <= 32: a z kernel
                                        (skipped when r == 0), then one product kernel whose
                                        accumulators take the correction before the store */
+#define BILOCO_SCHED_COMPOSED    4  /* separate launches: the plain FP4 product (fp32, in the
+                                       workspace), z, then y = bf16(product + z . U^T) by
+                                       4-bit sign lookup tables: the unfused form the fused
+                                       schedules are timed against; r <= 1024 */
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char *biloco_status_string(biloco_status s);
