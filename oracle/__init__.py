@@ -7,7 +7,8 @@ touches the HIP library.
 
 Each wrapper takes numpy arrays in the layouts documented in the C file and
 returns numpy arrays; the C routines are the plain definitions (see the
-header of ``biloco_oracle.c`` for the passages they follow).
+header of ``biloco_oracle.c`` for the passages they follow).  The sign
+peeling decomposition is plain numpy in ``peel.py``.
 """
 from __future__ import annotations
 
