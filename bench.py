@@ -151,6 +151,34 @@ def weight_quant_table() -> dict:
     return res
 
 
+def decompose_time(m: int = 5120, n: int = 5120, r: int = 512, T: int = 5) -> dict:
+    """biloco_peel_decompose on a seeded fp32 weight of the config-1 shape: one
+    full decomposition (r terms of T sign steps, refit, residual) between HIP
+    events on torch's stream, after one untimed run.  Each sign step is one
+    pass over W for R v and one for R^T u; the residual reads W and writes R:
+    (2 T r + 2) * 4 m n bytes in all."""
+    import numpy as np
+    import torch
+    from bit_weight_gemm_amd import binding as B
+    from bit_weight_gemm_amd import workloads as wl
+    W = torch.from_numpy(wl.make_residual(m, n, seed=2024, outliers=True)).cuda()
+    vi = torch.from_numpy(wl.make_start_signs(r, n, seed=77).view(np.int32)).cuda()
+    ws = torch.empty(B.biloco_peel_workspace_bytes(m, n, r), dtype=torch.uint8, device="cuda")
+    B.biloco_peel_decompose(W, r, T, vi, workspace=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    B.biloco_peel_decompose(W, r, T, vi, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / 1e3
+    nbytes = (2 * T * r + 2) * 4 * m * n
+    return {"m": m, "n": n, "r": r, "T": T, "ms": round(t * 1e3, 2),
+            "GBps": round(nbytes / t / 1e9, 1),
+            "pct_peak": round(100 * nbytes / t / 1e9 / PEAK_HBM_GBS, 2),
+            "bytes": nbytes}
+
+
 def cpu_baseline(cfg: int, seconds: float):
     import numpy as np
     import oracle
@@ -310,6 +338,7 @@ def main() -> int:
             torch.cuda.empty_cache()
         out["per_config"] = table
         out["weight_quant"] = weight_quant_table()
+        out["decompose"] = decompose_time()
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)

@@ -30,7 +30,8 @@ BILOCO_SCHED_COMPOSED = 4
 EXPORTED = ["biloco_status_string", "biloco_pack_signs", "biloco_quant_act_fp4",
             "biloco_gemm_workspace_bytes", "biloco_gemm_lowrank", "biloco_gemm_lowrank_sched",
             "biloco_gemm_check", "biloco_default_schedule", "biloco_schedules_for",
-            "biloco_quant_weight_nvfp4", "biloco_quant_weight_workspace_bytes"]
+            "biloco_quant_weight_nvfp4", "biloco_quant_weight_workspace_bytes",
+            "biloco_peel_decompose", "biloco_peel_workspace_bytes"]
 
 _lib = None
 
@@ -61,6 +62,10 @@ def lib() -> ctypes.CDLL:
         L.biloco_quant_weight_nvfp4.argtypes = [p, i64, i64, p, p, p, p, sz, p]
         L.biloco_quant_weight_workspace_bytes.restype = st
         L.biloco_quant_weight_workspace_bytes.argtypes = [i64, i64, ctypes.POINTER(sz)]
+        L.biloco_peel_decompose.restype = st
+        L.biloco_peel_decompose.argtypes = [p, i64, i64, i32, i32, p, p, p, p, p, p, p, sz, p]
+        L.biloco_peel_workspace_bytes.restype = st
+        L.biloco_peel_workspace_bytes.argtypes = [i64, i64, i32, ctypes.POINTER(sz)]
         L.biloco_gemm_workspace_bytes.restype = st
         L.biloco_gemm_workspace_bytes.argtypes = [i32, i32, i32, i32, ctypes.POINTER(sz)]
         gemm = [p, p, p, p, p, ctypes.c_float, p, p, p, i32, i32, i32, i32, p, p, sz]
@@ -155,6 +160,36 @@ def biloco_quant_weight_nvfp4(w: torch.Tensor, codes=None, scales=None, g=None, 
                                         _stream(stream)),
         "biloco_quant_weight_nvfp4")
     return codes, scales, g
+
+
+def biloco_peel_workspace_bytes(m: int, n: int, r: int) -> int:
+    out = ctypes.c_size_t(0)
+    _ok(lib().biloco_peel_workspace_bytes(m, n, r, ctypes.byref(out)),
+        "biloco_peel_workspace_bytes")
+    return int(out.value)
+
+
+def biloco_peel_decompose(W: torch.Tensor, r: int, T: int, v_init: torch.Tensor,
+                          want_residual: bool = True, workspace=None, stream=None):
+    """W fp32 [m][n], v_init int32 words [r][ceil(n/32)] (bit set = -1) ->
+    dict(u_packed [ceil(r/32)][m], v_packed [ceil(r/32)][n] (int32 words),
+    alpha [r], alpha_greedy [r], R [m][n] or None), all on W's device."""
+    m, n = W.shape
+    dev = W.device
+    RW = (r + 31) // 32
+    out = {"u_packed": torch.empty((RW, m), dtype=torch.int32, device=dev),
+           "v_packed": torch.empty((RW, n), dtype=torch.int32, device=dev),
+           "alpha": torch.empty(r, dtype=torch.float32, device=dev),
+           "alpha_greedy": torch.empty(r, dtype=torch.float32, device=dev),
+           "R": torch.empty((m, n), dtype=torch.float32, device=dev) if want_residual else None}
+    if workspace is None:
+        workspace = torch.empty(biloco_peel_workspace_bytes(m, n, r), dtype=torch.uint8, device=dev)
+    _ok(lib().biloco_peel_decompose(_p(W), m, n, r, T, _p(v_init), _p(out["u_packed"]),
+                                    _p(out["v_packed"]), _p(out["alpha"]), _p(out["alpha_greedy"]),
+                                    _p(out["R"]), _p(workspace),
+                                    workspace.numel() * workspace.element_size(), _stream(stream)),
+        "biloco_peel_decompose")
+    return out
 
 
 def biloco_gemm_workspace_bytes(M: int, N: int, K: int, r: int) -> int:

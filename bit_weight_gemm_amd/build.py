@@ -17,7 +17,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libbiloco_hip.so")
 
 SOURCES = ["biloco_api.cpp", "k_prep.hip", "k_unfused.hip", "k_fused_gemv.hip", "k_fused_mfma.hip",
-           "k_composed.hip"]
+           "k_composed.hip", "k_peel.hip"]
 HEADERS = ["biloco_device.h", "biloco_internal.h", os.path.join("..", "..", "include", "biloco.h")]
 
 ARCH = "gfx950"

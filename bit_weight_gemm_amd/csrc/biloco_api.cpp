@@ -119,6 +119,46 @@ biloco_status biloco_quant_weight_nvfp4(const float *w, int64_t N, int64_t K, ui
                : BILOCO_ERR_HIP;
 }
 
+// Limits of the sign-peeling decomposition: coordinates per side (one
+// packed sign row in 32 KiB of LDS) and rank (a one-workgroup solve).
+constexpr int64_t kPeelMaxDim = (int64_t)1 << 18;
+constexpr int32_t kPeelMaxRank = 1024;
+
+biloco_status biloco_peel_workspace_bytes(int64_t m, int64_t n, int32_t r, size_t *bytes) {
+    if (!bytes || m < 1 || n < 4 || n % 4 != 0 || r < 1) return BILOCO_ERR_INVALID_VALUE;
+    if (m > kPeelMaxDim || n > kPeelMaxDim || r > kPeelMaxRank) return BILOCO_ERR_UNSUPPORTED;
+    *bytes = peel_ws_bytes(m, n, r);
+    return BILOCO_OK;
+}
+
+biloco_status biloco_peel_decompose(const float *W, int64_t m, int64_t n, int32_t r, int32_t T,
+                                    const uint32_t *v_init, uint32_t *u_packed, uint32_t *v_packed,
+                                    float *alpha, float *alpha_greedy, float *R, void *workspace,
+                                    size_t workspace_bytes, hipStream_t stream) {
+    size_t need = 0;
+    biloco_status st = biloco_peel_workspace_bytes(m, n, r, &need);
+    if (st != BILOCO_OK) return st;
+    if (T < 1) return BILOCO_ERR_INVALID_VALUE;
+    if (!W || !v_init || !u_packed || !v_packed || !alpha || !workspace)
+        return BILOCO_ERR_INVALID_VALUE;
+    const void *ptrs[] = {W, v_init, u_packed, v_packed, alpha, alpha_greedy, R, workspace};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return BILOCO_ERR_INVALID_VALUE;
+    if (workspace_bytes < need) return BILOCO_ERR_WORKSPACE_TOO_SMALL;
+    const size_t RW = (size_t)(r + 31) / 32, mn = (size_t)m * (size_t)n;
+    struct { const void *p; size_t n; } arr[] = {
+        {W, 4 * mn},           {v_init, (size_t)r * ((n + 31) / 32) * 4},
+        {u_packed, RW * m * 4}, {v_packed, RW * n * 4}, {alpha, (size_t)r * 4},
+        {alpha_greedy, (size_t)r * 4}, {R, 4 * mn},  {workspace, need}};
+    for (int i = 0; i < 8; ++i)
+        for (int j = i + 1; j < 8; ++j)
+            if (overlaps(arr[i].p, arr[i].n, arr[j].p, arr[j].n)) return BILOCO_ERR_INVALID_VALUE;
+    return launch_peel(W, m, n, r, T, v_init, u_packed, v_packed, alpha, alpha_greedy, R, workspace,
+                       stream) == hipSuccess
+               ? BILOCO_OK
+               : BILOCO_ERR_HIP;
+}
+
 biloco_status biloco_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t r,
                                           size_t *bytes) {
     if (!bytes) return BILOCO_ERR_INVALID_VALUE;

@@ -66,6 +66,10 @@ hipError_t launch_quant_act(const uint16_t *x, int M, int K, uint8_t *codes, uin
 size_t quant_weight_ws_bytes();   // pass-1 partials of the weight quantiser
 hipError_t launch_quant_weight(const float *w, int64_t N, int64_t K, uint8_t *codes,
                                uint8_t *scales, float *g_out, void *ws, hipStream_t stream);
+size_t peel_ws_bytes(int64_t m, int64_t n, int r);
+hipError_t launch_peel(const float *W, int64_t m, int64_t n, int r, int T, const uint32_t *v_init,
+                       uint32_t *u_packed, uint32_t *v_packed, float *alpha, float *alpha_greedy,
+                       float *R, void *ws, hipStream_t stream);
 hipError_t launch_gemm_unfused(const GemmArgs &a, hipStream_t stream);
 hipError_t launch_gemm_fused_gemv(const GemmArgs &a, hipStream_t stream);
 hipError_t launch_gemm_gemv_two_launch(const GemmArgs &a, hipStream_t stream);

@@ -18,6 +18,14 @@ Recipe (fixed draw order, so the r = 0 run shares x and R with the r > 0 run):
      V = 1 - 2 * rng.integers(0, 2, (K, r), dtype=int8)
   7. alpha_i = bf16(c * i^-0.5), i = 1..r
 
+Start signs of the sign-peeling decomposition (make_start_signs): uint32
+  words rng.integers(0, 2^32, (r, ceil(n/32))), bits >= n cleared; every
+  bit is an independent fair coin (a set bit meaning -1).
+
+Weights with planted sign structure (make_planted_weight): fp32
+  W = sum_{l<L} decay^-l u_l v_l^T + noise * N(0,1), u_l, v_l i.i.d. fair
+  +-1 (the case where peeling has clear sign decisions to make).
+
 Residual matrices for the weight quantiser (make_residual): fp32
   w = sigma * rng.standard_normal((N, K), float32), and with outliers
   floor(0.01 K) columns (rng.choice) scaled by 20, the heavy-tailed input
@@ -97,6 +105,27 @@ def make_residual(N: int, K: int, seed: int, sigma: float = 0.02,
     if outliers:
         idx = rng.choice(K, max(1, int(np.floor(0.01 * K))), replace=False)
         w[:, idx] *= np.float32(20.0)
+    return w
+
+
+def make_planted_weight(m: int, n: int, L: int, decay: float, seed: int,
+                        noise: float = 1e-3) -> np.ndarray:
+    rng = np.random.default_rng(seed)
+    U = np.where(rng.random((m, L)) < 0.5, -1.0, 1.0)
+    V = np.where(rng.random((n, L)) < 0.5, -1.0, 1.0)
+    c = decay ** -np.arange(L, dtype=np.float64)
+    W = (U * c) @ V.T + noise * rng.standard_normal((m, n))
+    return W.astype(np.float32)
+
+
+def make_start_signs(r: int, n: int, seed: int) -> np.ndarray:
+    """uint32 [r][ceil(n/32)] random sign words for the peel's start vectors."""
+    rng = np.random.default_rng(seed)
+    nw = (n + 31) // 32
+    w = rng.integers(0, 2 ** 32, (r, nw), dtype=np.uint64).astype(np.uint32)
+    rem = n - 32 * (nw - 1)
+    if rem < 32:
+        w[:, -1] &= np.uint32((1 << rem) - 1)
     return w
 
 

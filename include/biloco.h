@@ -127,6 +127,43 @@ biloco_status biloco_quant_weight_nvfp4(const float *w, int64_t N, int64_t K, ui
  * Same shape rules. */
 biloco_status biloco_quant_weight_workspace_bytes(int64_t N, int64_t K, size_t *bytes);
 
+/* Greedy sign peeling with the joint coefficient refit (BiLoCo intro and
+ * section "Decomposition"): W ~ U diag(alpha) V^T + R with U in {+-1}^{m x r},
+ * V in {+-1}^{n x r}.  Term i (i = 0 .. r-1) starts from the signs v_init[i],
+ * then T times: u = sign(R v), v = sign(R^T u), with R = W minus the terms
+ * found so far and sign(0) = +1; its greedy coefficient is u^T R v / (m n)
+ * (the Frobenius optimum for fixed signs), and R loses that term.  After the
+ * r terms the coefficients are refit together by least squares for the fixed
+ * signs (normal equations G alpha = b, G_ij = (u_i . u_j)(v_i . v_j),
+ * b_i = u_i^T W v_i), and R = W - U diag(alpha) V^T with the refit ones.
+ *   W          [m][n] fp32 (input; finite)
+ *   v_init     uint32 [r][ceil(n/32)]: start signs of each term, bit b of word
+ *              w is coordinate 32w+b, a set bit meaning -1 (bits >= n ignored).
+ *              The caller draws them: the pages start each term from random
+ *              signs.
+ *   u_packed   uint32 [ceil(r/32)][m] = pack_signs(U^T)  (output; the form
+ *   v_packed   uint32 [ceil(r/32)][n] = pack_signs(V^T)   biloco_gemm_lowrank takes)
+ *   alpha      fp32 [r]: refit coefficients (output)
+ *   alpha_greedy fp32 [r] or NULL: the coefficients found during the peel
+ *   R          fp32 [m][n] or NULL: the residual W - U diag(alpha) V^T
+ *   workspace  >= biloco_peel_workspace_bytes(m, n, r) bytes; no fill needed.
+ * 1 <= m <= 2^18, 4 <= n <= 2^18 with n % 4 == 0, 1 <= r <= 1024, T >= 1.
+ * Arithmetic: fp32 sums for R v and R^T u (the terms found so far enter
+ * through exact integer sign dot products), fp64 for the refit.  A sign
+ * decision can differ from another summation order's where |(R v)_a| or
+ * |(R^T u)_k| is within rounding of 0.  If the sign terms are linearly
+ * dependent (a Cholesky pivot of G falls below 1e-6 m n, e.g. a term found
+ * twice), alpha holds the greedy coefficients.
+ * About (5 T + 1) r + 4 launches on `stream`; no two of the output and
+ * input arrays may overlap. */
+biloco_status biloco_peel_decompose(const float *W, int64_t m, int64_t n, int32_t r, int32_t T,
+                                    const uint32_t *v_init, uint32_t *u_packed, uint32_t *v_packed,
+                                    float *alpha, float *alpha_greedy, float *R, void *workspace,
+                                    size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace biloco_peel_decompose needs.  Same shape rules. */
+biloco_status biloco_peel_workspace_bytes(int64_t m, int64_t n, int32_t r, size_t *bytes);
+
 /* Bytes of device workspace biloco_gemm_lowrank needs for this shape, enough
  * for every schedule the shape allows.  May be 0 (then workspace may be
  * NULL).  Same argument rules as biloco_gemm_lowrank. */

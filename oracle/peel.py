@@ -20,7 +20,9 @@ Readings where the pages leave a step open:
     (|u|^2 = m, |v|^2 = n);
   * the refit solves the normal equations G a = b with
     G_ij = (u_i . u_j)(v_i . v_j) and b_i = u_i^T W v_i, and the returned
-    residual is W - U diag(a) V^T with the refit coefficients.
+    residual is W - U diag(a) V^T with the refit coefficients;
+  * if the r sign outer products are linearly dependent (G singular, e.g. a
+    term found twice), the refit keeps the greedy coefficients.
 
 Matrix products (numpy @) are the only library primitive used.
 """
@@ -82,7 +84,10 @@ def peel(W: np.ndarray, r: int, T: int, v_init: np.ndarray, trace: bool = False)
             bil.append(seq)
     G = (U.T @ U) * (V.T @ V)
     b = np.einsum("ai,ai->i", U, Wd @ V)
-    alpha = np.linalg.solve(G, b)
+    if np.linalg.matrix_rank(G) < r:
+        alpha = ag.copy()
+    else:
+        alpha = np.linalg.solve(G, b)
     out = {"U": U, "V": V, "alpha_greedy": ag, "alpha": alpha,
            "R": Wd - (U * alpha[None, :]) @ V.T}
     if trace:

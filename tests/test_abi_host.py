@@ -147,3 +147,30 @@ def test_quant_weight_rejects_before_hip():
     assert call(g=A * 3 + 16) == B.BILOCO_ERR_INVALID_VALUE           # g inside scales
     with pytest.raises(B.BilocoError):
         B.biloco_quant_weight_workspace_bytes(3, 24)
+
+
+def test_peel_rejects_before_hip():
+    L = B.lib()
+    A = 1 << 36
+    ws = B.biloco_peel_workspace_bytes(64, 64, 8)
+    assert ws > 0
+    names = ["W", "m", "n", "r", "T", "vi", "up", "vp", "alpha", "ag", "R", "ws", "wsb", "stream"]
+    ok = dict(W=A, m=64, n=64, r=8, T=2, vi=A * 2, up=A * 3, vp=A * 4, alpha=A * 5, ag=A * 6,
+              R=A * 7, ws=A * 8, wsb=ws, stream=None)
+
+    def call(**kw):
+        args = dict(ok)
+        args.update(kw)
+        return L.biloco_peel_decompose(*[args[k] for k in names])
+
+    assert call(m=0) == B.BILOCO_ERR_INVALID_VALUE
+    assert call(n=6) == B.BILOCO_ERR_INVALID_VALUE
+    assert call(r=0) == B.BILOCO_ERR_INVALID_VALUE
+    assert call(T=0) == B.BILOCO_ERR_INVALID_VALUE
+    assert call(r=1025) == B.BILOCO_ERR_UNSUPPORTED
+    assert call(m=1 << 19) == B.BILOCO_ERR_UNSUPPORTED
+    for k in ["W", "vi", "up", "vp", "alpha", "ws"]:
+        assert call(**{k: None}) == B.BILOCO_ERR_INVALID_VALUE, k
+        assert call(**{k: ok[k] + 8}) == B.BILOCO_ERR_INVALID_VALUE, k
+    assert call(wsb=ws - 1) == B.BILOCO_ERR_WORKSPACE_TOO_SMALL
+    assert call(R=A + 64) == B.BILOCO_ERR_INVALID_VALUE               # R inside W
