@@ -216,9 +216,17 @@ def main() -> int:
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no GPU work: turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
                          "this script into profiles/traffic_<schedule>_config<c>.json and .md")
+    ap.add_argument("--only", choices=["weight-quant", "decompose"],
+                    help="time only this NEXT-row operation and print its JSON (for profiling)")
     args = ap.parse_args()
     if args.traffic_summary:
         return traffic_summary(args)
+    if args.only:
+        import torch
+        assert torch.cuda.is_available(), "bench.py needs a GPU"
+        res = weight_quant_table() if args.only == "weight-quant" else decompose_time()
+        print(json.dumps({args.only: res}), flush=True)
+        return 0
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
