@@ -25,7 +25,8 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, 10^9 B/s
 ROT_BYTES = 1.2e9              # distinct weight bytes a timed graph walks through
-SCHED_NAMES = {1: "unfused", 2: "fused_gemv", 3: "fused_mfma", 4: "composed"}
+SCHED_NAMES = {1: "unfused", 2: "fused_gemv", 3: "fused_mfma", 4: "composed",
+               5: "composed_mfma"}
 METRIC = "fused GEMM µs/call + effective HBM GB/s (% peak) at M=1..32, r=512"
 
 
@@ -334,6 +335,7 @@ def main() -> int:
             tc = gemm_call_time(pc, sc, rc, calls)
             # the same product as separate launches (plain product, z, correction)
             tcomp = gemm_call_time(pc, B.BILOCO_SCHED_COMPOSED, rc, calls)
+            tcm = gemm_call_time(pc, B.BILOCO_SCHED_COMPOSED_MFMA, rc, calls)
             bc = algorithmic_bytes(pc.M, pc.N, pc.K, pc.r)
             table[f"config{c}"] = {"M": pc.M, "K": pc.K, "N": pc.N, "r": pc.r,
                                    "schedule": SCHED_NAMES.get(sc, sc),
@@ -341,6 +343,7 @@ def main() -> int:
                                    "GBps": round(bc / tc / 1e9, 1),
                                    "pct_peak": round(100 * bc / tc / 1e9 / PEAK_HBM_GBS, 2),
                                    "composed_us_per_call": round(tcomp * 1e6, 3),
+                                   "composed_mfma_us_per_call": round(tcm * 1e6, 3),
                                    "speedup_vs_composed": round(tcomp / tc, 3)}
             del rc, pc
             torch.cuda.empty_cache()

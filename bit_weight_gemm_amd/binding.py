@@ -26,6 +26,7 @@ BILOCO_SCHED_UNFUSED = 1
 BILOCO_SCHED_FUSED_GEMV = 2
 BILOCO_SCHED_FUSED_MFMA = 3
 BILOCO_SCHED_COMPOSED = 4
+BILOCO_SCHED_COMPOSED_MFMA = 5
 
 EXPORTED = ["biloco_status_string", "biloco_pack_signs", "biloco_quant_act_fp4",
             "biloco_gemm_workspace_bytes", "biloco_gemm_lowrank", "biloco_gemm_lowrank_sched",

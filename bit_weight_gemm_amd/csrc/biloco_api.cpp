@@ -26,7 +26,8 @@ bool schedule_allowed(int s, int M, int N, int K, int r) {
         case BILOCO_SCHED_UNFUSED: return true;
         case BILOCO_SCHED_FUSED_GEMV: return gemv_supported(M, N, K, r);
         case BILOCO_SCHED_FUSED_MFMA: return mfma_supported(M, N, K, r);
-        case BILOCO_SCHED_COMPOSED: return composed_supported(M, N, K, r);
+        case BILOCO_SCHED_COMPOSED:
+        case BILOCO_SCHED_COMPOSED_MFMA: return composed_supported(M, N, K, r);
         default: return false;
     }
 }
@@ -196,7 +197,7 @@ biloco_status biloco_gemm_check(const void *a_codes, const void *a_scales, const
         {alpha_bf16, (size_t)r * 2},   {workspace, need}};
     for (auto &in : ins)
         if (overlaps(y_bf16, ny, in.p, in.n)) return BILOCO_ERR_INVALID_VALUE;
-    if (schedule < BILOCO_SCHED_AUTO || schedule > BILOCO_SCHED_COMPOSED)
+    if (schedule < BILOCO_SCHED_AUTO || schedule > BILOCO_SCHED_COMPOSED_MFMA)
         return BILOCO_ERR_INVALID_VALUE;
     if (schedule != BILOCO_SCHED_AUTO && !schedule_allowed(schedule, M, N, K, r))
         return BILOCO_ERR_UNSUPPORTED;
@@ -212,7 +213,7 @@ int32_t biloco_schedules_for(int32_t M, int32_t N, int32_t K, int32_t r, int32_t
                              int32_t cap) {
     if (check_shape(M, N, K, r) != BILOCO_OK) return 0;
     int32_t n = 0;
-    for (int s = BILOCO_SCHED_UNFUSED; s <= BILOCO_SCHED_COMPOSED; ++s)
+    for (int s = BILOCO_SCHED_UNFUSED; s <= BILOCO_SCHED_COMPOSED_MFMA; ++s)
         if (schedule_allowed(s, M, N, K, r)) {
             if (out && n < cap) out[n] = s;
             ++n;
@@ -240,7 +241,8 @@ biloco_status biloco_gemm_lowrank_sched(const uint8_t *a_codes, const uint8_t *a
     switch (s) {
         case BILOCO_SCHED_FUSED_GEMV: e = launch_gemm_fused_gemv(a, stream); break;
         case BILOCO_SCHED_FUSED_MFMA: e = launch_gemm_mfma(a, stream); break;
-        case BILOCO_SCHED_COMPOSED: e = launch_gemm_composed(a, stream); break;
+        case BILOCO_SCHED_COMPOSED: e = launch_gemm_composed(a, false, stream); break;
+        case BILOCO_SCHED_COMPOSED_MFMA: e = launch_gemm_composed(a, true, stream); break;
         default: e = launch_gemm_unfused(a, stream); break;
     }
     return e == hipSuccess ? BILOCO_OK : BILOCO_ERR_HIP;

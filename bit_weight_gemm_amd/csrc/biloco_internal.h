@@ -34,6 +34,7 @@ struct GemmArgs {
 //                     per-word counters, z/g operands, K-slice partials of y
 //                     and per-row-block counters (sized by mfma_ws_bytes)
 //   then (256-aligned, r > 0) the separate-launch schedule's fp32 product [M][N]
+//                     and its r = 0 product's split-K partials
 constexpr int kGemvMaxWorkgroups = 8192;
 constexpr size_t kWsHeaderBytes = 64 * 1024;
 inline int rpad32(int r) { return (r + 31) / 32 * 32; }
@@ -48,14 +49,18 @@ inline size_t ws_mfma_offset(int M, int r) {
 }
 bool mfma_supported(int M, int N, int K, int r);     // shapes the matrix-core schedule handles
 size_t mfma_ws_bytes(int M, int N, int K, int r);    // its workspace area (0 if none is needed)
-// The separate-launch schedule's fp32 product [M][N] (r > 0 only) follows.
+// The separate-launch schedule's fp32 product [M][N] (r > 0 only) follows,
+// then that schedule's own area for the r = 0 product's K-slice partials.
 inline size_t ws_yf_offset(int M, int N, int K, int r) {
     return (ws_mfma_offset(M, r) + mfma_ws_bytes(M, N, K, r) + 255) / 256 * 256;
+}
+inline size_t ws_g0_offset(int M, int N, int K, int r) {
+    return (ws_yf_offset(M, N, K, r) + (size_t)4 * (size_t)M * (size_t)N + 255) / 256 * 256;
 }
 // Workspace for every schedule of the shape: nothing for r = 0 unless the
 // matrix-core schedule splits K.
 inline size_t ws_total_bytes(int M, int N, int K, int r) {
-    return r > 0 ? ws_yf_offset(M, N, K, r) + (size_t)4 * (size_t)M * (size_t)N
+    return r > 0 ? ws_g0_offset(M, N, K, r) + mfma_ws_bytes(M, N, K, 0)
                  : ws_mfma_offset(M, r) + mfma_ws_bytes(M, N, K, r);
 }
 
@@ -76,10 +81,11 @@ hipError_t launch_gemm_gemv_two_launch(const GemmArgs &a, hipStream_t stream);
 hipError_t launch_z_gemv(const GemmArgs &a, float *z, hipStream_t stream);   // M <= 2
 bool gemv_supported(int M, int N, int K, int r);   // shapes the one-launch vector-ALU schedule handles
 hipError_t launch_gemm_mfma(const GemmArgs &a, hipStream_t stream);
+hipError_t launch_z_mfma(const GemmArgs &a, float *zf, hipStream_t stream);   // M >= 1, r >= 1
 // z = alpha (.) (x . V) as plain fp32 [M][rpad32(r)] at z (r > 0)
 hipError_t launch_z_fp32(const GemmArgs &a, float *z, hipStream_t stream);
 constexpr int kComposedMaxRank = 1024;   // the correction's lookup tables fit 32 KiB of LDS
 bool composed_supported(int M, int N, int K, int r);
-hipError_t launch_gemm_composed(const GemmArgs &a, hipStream_t stream);
+hipError_t launch_gemm_composed(const GemmArgs &a, bool mfma_correction, hipStream_t stream);
 
 }  // namespace biloco

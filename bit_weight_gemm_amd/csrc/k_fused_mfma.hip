@@ -99,6 +99,8 @@ struct MfmaParams {
     float *zpart;               // [zs][W][MB][64 lanes][8] (correction A-operand order)
     uint32_t *zcnt;             // [W]
     uint32_t *zA;               // [W][MB][2 hi/lo][64 lanes][4] bf16 pairs of z / g
+    float *zf;                  // if set: plain fp32 z [M][rpad] as well (separate-launch use)
+    int rpad;
     // product kernel
     int S, cps, chunks, RB, Gs;
     float *ypart;               // [S][RB][MB][64 lanes][4] (D layout)
@@ -273,6 +275,7 @@ __global__ void __launch_bounds__(kZThreads) mfma_z_kernel(MfmaParams p) {
         const int i = 32 * w + 4 * q + (j & 3) + 16 * (j >> 2);
         const float al = bf16_to_f32(p.alpha[i < p.r ? i : p.r - 1]);
         const float zz = (i < p.r && m < p.M) ? sum * al * ginv : 0.0f;
+        if (p.zf && i < p.r && m < p.M) p.zf[(int64_t)m * p.rpad + i] = sum * al;
         const uint32_t zh = f32_to_bf16_rne(zz);
         const uint32_t zl = f32_to_bf16_rne(zz - bf16_to_f32(zh));
         // pair with the partner thread (j ^ 4) of the same 8-thread group
@@ -626,9 +629,11 @@ size_t mfma_ws_bytes(int M, int N, int K, int r) {
     return mfma_supported(M, N, K, r) ? mfma_plan(M, N, K, r).bytes : 0;
 }
 
-hipError_t launch_gemm_mfma(const GemmArgs &a, hipStream_t stream) {
-    if (!mfma_supported(a.M, a.N, a.K, a.r)) return hipErrorNotSupported;
+namespace {
+// Parameters and workspace areas of one call (shared by the launchers below).
+MfmaParams mfma_params(const GemmArgs &a, MfmaPlan &q_out) {
     const MfmaPlan q = mfma_plan(a.M, a.N, a.K, a.r);
+    q_out = q;
     MfmaParams p{};
     p.a_codes = a.a_codes;
     p.a_scales = a.a_scales;
@@ -660,6 +665,28 @@ hipError_t launch_gemm_mfma(const GemmArgs &a, hipStream_t stream) {
         p.zA = reinterpret_cast<uint32_t *>(ws + q.off_za);
         p.ypart = reinterpret_cast<float *>(ws + q.off_ypart);
     }
+    p.rpad = rpad32(a.r);
+    return p;
+}
+}  // namespace
+
+// The z kernel alone, also storing plain fp32 z at zf (separate-launch use).
+hipError_t launch_z_mfma(const GemmArgs &a, float *zf, hipStream_t stream) {
+    if (a.r < 1 || !mfma_supported(a.M, a.N, a.K, a.r)) return hipErrorNotSupported;
+    MfmaPlan q;
+    MfmaParams p = mfma_params(a, q);
+    p.zf = zf;
+    if (q.mb == 1)
+        hipLaunchKernelGGL(mfma_z_kernel<1>, dim3(q.W * q.zs), dim3(kZThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL(mfma_z_kernel<2>, dim3(q.W * q.zs), dim3(kZThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_mfma(const GemmArgs &a, hipStream_t stream) {
+    if (!mfma_supported(a.M, a.N, a.K, a.r)) return hipErrorNotSupported;
+    MfmaPlan q;
+    const MfmaParams p = mfma_params(a, q);
     hipError_t e = hipSuccess;
     if (a.r > 0) {
         if (q.mb == 1)

@@ -96,7 +96,8 @@ gemv_unfused_kernel(const uint8_t *__restrict__ a_codes, const uint8_t *__restri
 }
 
 hipError_t launch_z_fp32(const GemmArgs &a, float *z, hipStream_t stream) {
-    if (gemv_supported(a.M, a.N, a.K, a.r)) return launch_z_gemv(a, z, stream);
+    if (a.M <= 2 && gemv_supported(a.M, a.N, a.K, a.r)) return launch_z_gemv(a, z, stream);
+    if (mfma_supported(a.M, a.N, a.K, a.r)) return launch_z_mfma(a, z, stream);
     hipLaunchKernelGGL(z_unfused_kernel, dim3(rpad32(a.r) / 32, a.M), dim3(256), 0, stream, a.x,
                        a.v, a.alpha, a.K, a.r, rpad32(a.r), z);
     return hipGetLastError();

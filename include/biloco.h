@@ -65,6 +65,9 @@ typedef int32_t biloco_status;
                                        workspace), z, then y = bf16(product + z . U^T) by
                                        4-bit sign lookup tables: the unfused form the fused
                                        schedules are timed against; r <= 1024 */
+#define BILOCO_SCHED_COMPOSED_MFMA 5 /* as BILOCO_SCHED_COMPOSED, the correction by bf16
+                                       MFMAs of z (high + low) against U's +-1 signs
+                                       instead of lookup tables; r <= 1024 */
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char *biloco_status_string(biloco_status s);
