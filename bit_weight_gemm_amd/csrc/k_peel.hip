@@ -17,8 +17,8 @@
 // pack (u = sign(s), gamma_j = alpha_j (u_j . u)), col (K-slice partials of
 // W^T u), colfin (t = R^T u, v = sign(t)); after the T steps one
 // term-finishing launch.  At the end: the Gram matrix of the sign terms, a
-// one-workgroup Cholesky solve of the normal equations, and R = W - U
-// diag(alpha) V^T with 4-bit lookup tables of the coefficients.
+// blocked Cholesky solve of the normal equations, and R = W - U diag(alpha)
+// V^T with 4-bit lookup tables of the coefficients.
 //
 // Sign words: bit set = -1.  Term-major rows (bits of term j over the m or n
 // coordinates, for the popcounts) live in the workspace; the outputs are the
@@ -38,7 +38,7 @@ constexpr int kColUnroll = 8;          // rows in flight per thread in the colum
 struct PeelLayout {
     int64_t m, n;
     int r, Wm, Wn, RW, S, rows_per_slice, NBf;
-    size_t ubits, vbits, ucur, vcur, s, coef, ag, tpart, red, bvec, gram, sol, total;
+    size_t ubits, vbits, ucur, vcur, s, coef, ag, tpart, red, bvec, gram, sol, bad, total;
 };
 
 size_t al256(size_t x) { return (x + 255) / 256 * 256; }
@@ -71,6 +71,7 @@ PeelLayout peel_layout(int64_t m, int64_t n, int r) {
     L.bvec = take((size_t)r * 8);
     L.gram = take((size_t)r * r * 8);
     L.sol = take((size_t)r * 8);
+    L.bad = take(4);
     L.total = o;
     return L;
 }
@@ -79,6 +80,7 @@ struct PeelPtrs {
     uint32_t *ubits, *vbits, *ucur, *vcur;
     float *s, *coef, *ag, *tpart, *red;
     double *bvec, *gram, *sol;
+    int *bad;
 };
 
 PeelPtrs peel_ptrs(const PeelLayout &L, void *ws) {
@@ -88,7 +90,8 @@ PeelPtrs peel_ptrs(const PeelLayout &L, void *ws) {
                     reinterpret_cast<float *>(b + L.s),        reinterpret_cast<float *>(b + L.coef),
                     reinterpret_cast<float *>(b + L.ag),       reinterpret_cast<float *>(b + L.tpart),
                     reinterpret_cast<float *>(b + L.red),      reinterpret_cast<double *>(b + L.bvec),
-                    reinterpret_cast<double *>(b + L.gram),    reinterpret_cast<double *>(b + L.sol)};
+                    reinterpret_cast<double *>(b + L.gram),    reinterpret_cast<double *>(b + L.sol),
+                    reinterpret_cast<int *>(b + L.bad)};
 }
 
 // mask of the valid bits of word w of a length-len sign row
@@ -372,46 +375,104 @@ peel_gram_kernel(const uint32_t *__restrict__ ubits, const uint32_t *__restrict_
 }
 
 // ---------------------------------------------------------------------------
-// solve: one workgroup.  In-place Cholesky G = L L^T (lower triangle, right
-// looking), then L y = b and L^T x = y; x -> alpha (fp32) and the greedy
-// coefficients -> alpha_greedy (fp32, if requested).  A pivot below 1e-6 m n
-// (the sign terms are linearly dependent) leaves the greedy coefficients in
-// alpha.
+// solve: blocked right-looking Cholesky G = L L^T in place (lower triangle,
+// fp64), panels of kChol columns.  Per panel, one workgroup factors the
+// diagonal block in LDS and solves the rows below it (L21 = A21 L11^-T, one
+// thread per row), then a tiled update A22 -= L21 L21^T runs over many
+// workgroups.  A last workgroup solves L y = b, L^T x = y.  A pivot below
+// 1e-6 m n (every diagonal entry of G is m n; the sign terms are linearly
+// dependent) sets a flag, and then alpha keeps the greedy coefficients.
+constexpr int kChol = 32;
+
 __global__ void __launch_bounds__(1024)
-peel_solve_kernel(double *__restrict__ G, const double *__restrict__ b, double *__restrict__ x, int r,
-                  double G_diag, const float *__restrict__ ag, float *__restrict__ alpha,
-                  float *__restrict__ alpha_greedy) {
-    __shared__ int bad;
-    __shared__ double piv;
-    if (threadIdx.x == 0) bad = 0;
+peel_chol_panel_kernel(double *__restrict__ G, int r, int k0, double G_diag, int *__restrict__ bad) {
+    __shared__ double L[kChol][kChol + 1];
+    const int kb = r - k0 < kChol ? r - k0 : kChol;
+    if (k0 == 0 && threadIdx.x == 0) *bad = 0;
+    for (int e = threadIdx.x; e < kb * kb; e += 1024) {
+        const int a = e / kb, c = e % kb;
+        L[a][c] = G[(int64_t)(k0 + a) * r + k0 + c];
+    }
     __syncthreads();
-    for (int k = 0; k < r; ++k) {
+    for (int c = 0; c < kb; ++c) {
         if (threadIdx.x == 0) {
-            // every diagonal entry of G is m n; a pivot that elimination
-            // brings down to ~0 means the sign terms are dependent
-            const double d = G[(int64_t)k * r + k];
+            const double d = L[c][c];
             const bool ok = d > 1e-6 * G_diag;
-            if (!ok) bad = 1;
-            piv = ok ? sqrt(d) : 1.0;
-            G[(int64_t)k * r + k] = piv;
+            if (!ok) *bad = 1;
+            L[c][c] = ok ? sqrt(d) : 1.0;
         }
         __syncthreads();
-        for (int i = k + 1 + threadIdx.x; i < r; i += 1024) G[(int64_t)i * r + k] /= piv;
+        for (int a = c + 1 + (int)threadIdx.x; a < kb; a += 1024) L[a][c] /= L[c][c];
         __syncthreads();
-        // trailing update of the lower triangle, rows i > k, columns k < j <= i:
-        // the 32 x 32 threads tile the square of remaining rows and columns
-        const int rem = r - k - 1, ty = threadIdx.x >> 5, tx = threadIdx.x & 31;
-        for (int ii = ty; ii < rem; ii += 32) {
-            const int64_t gi = k + 1 + ii;
-            const double lik = G[gi * r + k];
-            for (int jj = tx; jj <= ii; jj += 32) {
-                const int64_t gj = k + 1 + jj;
-                G[gi * r + gj] -= lik * G[gj * r + k];
-            }
+        const int rem = kb - c - 1;
+        for (int e = threadIdx.x; e < rem * rem; e += 1024) {
+            const int a = c + 1 + e / rem, cc = c + 1 + e % rem;
+            if (cc <= a) L[a][cc] -= L[a][c] * L[cc][c];
         }
         __syncthreads();
     }
-    // forward: L y = b (y in x)
+    for (int e = threadIdx.x; e < kb * kb; e += 1024) {
+        const int a = e / kb, c = e % kb;
+        if (c <= a) G[(int64_t)(k0 + a) * r + k0 + c] = L[a][c];
+    }
+    // rows below the block: L21[i][:] = A21[i][:] L11^-T (forward substitution)
+    for (int i = k0 + kb + (int)threadIdx.x; i < r; i += 1024) {
+        double x[kChol];
+        double *row = G + (int64_t)i * r + k0;
+#pragma unroll
+        for (int c = 0; c < kChol; ++c) x[c] = c < kb ? row[c] : 0.0;
+#pragma unroll
+        for (int c = 0; c < kChol; ++c) {
+            if (c < kb) {
+                double v = x[c];
+#pragma unroll
+                for (int cc = 0; cc < c; ++cc) v -= x[cc] * L[c][cc];
+                x[c] = v / L[c][c];
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < kChol; ++c)
+            if (c < kb) row[c] = x[c];
+    }
+}
+
+// A22 -= L21 L21^T on the lower triangle of the trailing matrix: workgroup =
+// one 32 x 32 tile (ti >= tj), thread = 4 entries; both panels via LDS.
+__global__ void __launch_bounds__(256)
+peel_chol_update_kernel(double *__restrict__ G, int r, int k0) {
+    __shared__ double Pi[kChol][kChol + 1], Pj[kChol][kChol + 1];
+    const int kb = r - k0 < kChol ? r - k0 : kChol;
+    const int base = k0 + kb;
+    // blockIdx.x -> (ti, tj), tj <= ti
+    int ti = (int)((sqrt(8.0 * (double)blockIdx.x + 1.0) - 1.0) * 0.5);
+    while ((ti + 1) * (ti + 2) / 2 <= (int)blockIdx.x) ++ti;
+    while (ti * (ti + 1) / 2 > (int)blockIdx.x) --ti;
+    const int tj = (int)blockIdx.x - ti * (ti + 1) / 2;
+    const int i0 = base + 32 * ti, j0 = base + 32 * tj;
+    for (int e = threadIdx.x; e < 32 * kChol; e += 256) {
+        const int a = e / kChol, c = e % kChol;
+        Pi[a][c] = (i0 + a < r && c < kb) ? G[(int64_t)(i0 + a) * r + k0 + c] : 0.0;
+        Pj[a][c] = (j0 + a < r && c < kb) ? G[(int64_t)(j0 + a) * r + k0 + c] : 0.0;
+    }
+    __syncthreads();
+    const int a = threadIdx.x >> 3, c0 = (threadIdx.x & 7) * 4;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int gi = i0 + a, gj = j0 + c0 + q;
+        if (gi < r && gj < r && gj <= gi) {
+            double v = 0.0;
+#pragma unroll
+            for (int c = 0; c < kChol; ++c) v += Pi[a][c] * Pj[c0 + q][c];
+            G[(int64_t)gi * r + gj] -= v;
+        }
+    }
+}
+
+// L y = b and L^T x = y (one workgroup), then the outputs.
+__global__ void __launch_bounds__(1024)
+peel_trisolve_kernel(const double *__restrict__ G, const double *__restrict__ b, double *__restrict__ x,
+                     int r, const int *__restrict__ bad, const float *__restrict__ ag,
+                     float *__restrict__ alpha, float *__restrict__ alpha_greedy) {
     for (int t = threadIdx.x; t < r; t += 1024) x[t] = b[t];
     __syncthreads();
     for (int i = 0; i < r; ++i) {
@@ -420,15 +481,15 @@ peel_solve_kernel(double *__restrict__ G, const double *__restrict__ b, double *
         for (int t = i + 1 + threadIdx.x; t < r; t += 1024) x[t] -= G[(int64_t)t * r + i] * x[i];
         __syncthreads();
     }
-    // backward: L^T x = y
     for (int i = r - 1; i >= 0; --i) {
         if (threadIdx.x == 0) x[i] /= G[(int64_t)i * r + i];
         __syncthreads();
         for (int t = threadIdx.x; t < i; t += 1024) x[t] -= G[(int64_t)i * r + t] * x[i];
         __syncthreads();
     }
+    const bool dependent = *bad != 0;
     for (int i = threadIdx.x; i < r; i += 1024) {
-        alpha[i] = bad ? ag[i] : (float)x[i];
+        alpha[i] = dependent ? ag[i] : (float)x[i];
         if (alpha_greedy) alpha_greedy[i] = ag[i];
     }
 }
@@ -541,8 +602,20 @@ hipError_t launch_peel(const float *W, int64_t m, int64_t n, int r, int T, const
     hipLaunchKernelGGL(peel_gram_kernel, dim3(gt, gt), dim3(256), 0, stream, P.ubits, P.vbits, L.Wm,
                        L.Wn, r, m, n, P.gram);
     PEEL_CHECK();
-    hipLaunchKernelGGL(peel_solve_kernel, dim3(1), dim3(1024), 0, stream, P.gram, P.bvec, P.sol, r,
-                       (double)m * (double)n, P.ag, alpha, alpha_greedy);
+    for (int k0 = 0; k0 < r; k0 += kChol) {
+        hipLaunchKernelGGL(peel_chol_panel_kernel, dim3(1), dim3(1024), 0, stream, P.gram, r, k0,
+                           (double)m * (double)n, P.bad);
+        PEEL_CHECK();
+        const int rest = r - k0 - kChol;
+        if (rest > 0) {
+            const int T = (rest + 31) / 32;
+            hipLaunchKernelGGL(peel_chol_update_kernel, dim3((unsigned)(T * (T + 1) / 2)), dim3(256), 0,
+                               stream, P.gram, r, k0);
+            PEEL_CHECK();
+        }
+    }
+    hipLaunchKernelGGL(peel_trisolve_kernel, dim3(1), dim3(1024), 0, stream, P.gram, P.bvec, P.sol, r,
+                       P.bad, P.ag, alpha, alpha_greedy);
     PEEL_CHECK();
     if (R) {
         const int64_t g = ((n4 + kPeelThreads - 1) / kPeelThreads) * m;
