@@ -248,6 +248,55 @@ biloco_status biloco_gemm_lowrank_sched(const uint8_t *a_codes, const uint8_t *a
     return e == hipSuccess ? BILOCO_OK : BILOCO_ERR_HIP;
 }
 
+biloco_status biloco_gemm_lowrank_quant(const uint16_t *x_bf16, uint8_t *a_codes, uint8_t *a_scales,
+                                        const uint8_t *w_codes, const uint8_t *w_scales,
+                                        float w_global_scale, const uint32_t *v_packed,
+                                        const uint32_t *u_packed, const uint16_t *alpha_bf16,
+                                        int32_t M, int32_t N, int32_t K, int32_t r, uint16_t *y_bf16,
+                                        void *workspace, size_t workspace_bytes, int32_t schedule,
+                                        hipStream_t stream) {
+    if (!x_bf16) return BILOCO_ERR_INVALID_VALUE;
+    biloco_status st = biloco_gemm_check(a_codes, a_scales, x_bf16, w_codes, w_scales, v_packed,
+                                         u_packed, alpha_bf16, M, N, K, r, y_bf16, workspace,
+                                         workspace_bytes, schedule);
+    if (st != BILOCO_OK) return st;
+    // the activation outputs must not overlap any other array of the call
+    const size_t nc = (size_t)M * K / 2, ns = (size_t)M * K / 16;
+    const size_t W = (size_t)(r + 31) / 32;
+    struct { const void *p; size_t n; } others[] = {
+        {x_bf16, (size_t)M * K * 2},   {w_codes, (size_t)N * K / 2}, {w_scales, (size_t)N * K / 16},
+        {v_packed, W * (size_t)K * 4}, {u_packed, W * (size_t)N * 4}, {alpha_bf16, (size_t)r * 2},
+        {workspace, ws_total_bytes(M, N, K, r)}, {a_scales, ns}};
+    for (auto &o : others) {
+        if (overlaps(a_codes, nc, o.p, o.n)) return BILOCO_ERR_INVALID_VALUE;
+        if (o.p != a_scales && overlaps(a_scales, ns, o.p, o.n)) return BILOCO_ERR_INVALID_VALUE;
+    }
+    GemmArgs a{a_codes, a_scales, x_bf16, w_codes, w_scales, w_global_scale, v_packed,
+               u_packed, alpha_bf16, M,       N,        K,     r,      y_bf16,
+               workspace, workspace_bytes};
+    const int s = schedule == BILOCO_SCHED_AUTO ? resolve_schedule(M, N, K, r) : schedule;
+    // the z launch quantises x where the schedule has one; otherwise a launch
+    // of its own comes first
+    const bool in_z = r > 0 && ((s == BILOCO_SCHED_UNFUSED && M <= 2 && gemv_supported(M, N, K, r)) ||
+                                s == BILOCO_SCHED_FUSED_MFMA);
+    hipError_t e = hipSuccess;
+    if (in_z) {
+        a.qa_codes = a_codes;
+        a.qa_scales = a_scales;
+    } else {
+        e = launch_quant_act(x_bf16, M, K, a_codes, a_scales, stream);
+        if (e != hipSuccess) return BILOCO_ERR_HIP;
+    }
+    switch (s) {
+        case BILOCO_SCHED_FUSED_GEMV: e = launch_gemm_fused_gemv(a, stream); break;
+        case BILOCO_SCHED_FUSED_MFMA: e = launch_gemm_mfma(a, stream); break;
+        case BILOCO_SCHED_COMPOSED: e = launch_gemm_composed(a, false, stream); break;
+        case BILOCO_SCHED_COMPOSED_MFMA: e = launch_gemm_composed(a, true, stream); break;
+        default: e = launch_gemm_unfused(a, stream); break;
+    }
+    return e == hipSuccess ? BILOCO_OK : BILOCO_ERR_HIP;
+}
+
 biloco_status biloco_gemm_lowrank(const uint8_t *a_codes, const uint8_t *a_scales,
                                   const uint16_t *x_bf16, const uint8_t *w_codes,
                                   const uint8_t *w_scales, float w_global_scale,

@@ -63,6 +63,41 @@ __device__ __forceinline__ uint32_t e2m1_mag_code(float a, float s) {
            (uint32_t)(a > 5.0f * s);
 }
 
+// ---------------------------------------------------------------- activation FP4
+// One block of 16 activations (blocks are numbered row-major over [M][K/16]):
+// two 16-byte loads, amax by integer max over the magnitude bits (bf16
+// magnitudes order like integers), scale = E4M3(amax / 6) with a correctly
+// rounded fp32 division, codes by exact comparisons with the E2M1 midpoints
+// times the scale; one 8-byte store of the codes and one byte of scale.
+__device__ __forceinline__ void quant_act_block(const uint16_t *__restrict__ x, int64_t blk,
+                                                uint8_t *__restrict__ codes,
+                                                uint8_t *__restrict__ scales) {
+    const uint4 *src = reinterpret_cast<const uint4 *>(x + blk * 16);
+    const uint4 v0 = src[0], v1 = src[1];
+    const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    uint32_t amax_bits = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        amax_bits = max(amax_bits, w[j] & 0x7FFFu);
+        amax_bits = max(amax_bits, (w[j] >> 16) & 0x7FFFu);
+    }
+    const float amax = bf16_to_f32(amax_bits);
+    const uint32_t sb = f32_to_e4m3_rne(amax / 6.0f);
+    const float s = e4m3_to_f32(sb);
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const uint32_t h = (j & 1) ? (w[j >> 1] >> 16) : (w[j >> 1] & 0xFFFFu);
+        const float a = bf16_to_f32(h & 0x7FFFu);
+        const uint32_t mag = (sb == 0u) ? 0u : e2m1_mag_code(a, s);
+        const uint32_t code = mag | ((h >> 12) & 8u);
+        if (j < 8) lo |= code << (4 * j);
+        else hi |= code << (4 * (j - 8));
+    }
+    *reinterpret_cast<uint2 *>(codes + blk * 8) = make_uint2(lo, hi);
+    scales[blk] = (uint8_t)sb;
+}
+
 // ---------------------------------------------------------------- buffer loads
 // Raw buffer resources over the arrays a kernel streams.  A buffer load whose
 // offset is past the resource's size returns zeros without a memory access;

@@ -22,6 +22,10 @@ struct GemmArgs {
     void *ws;
     size_t ws_bytes;
     float *yf = nullptr;    // if set: fp32 results here instead of bf16 y (r = 0 products only)
+    // if set: the z launch also quantises x into these (they are a_codes and
+    // a_scales of the same call); only for schedules whose z has a launch
+    uint8_t *qa_codes = nullptr;
+    uint8_t *qa_scales = nullptr;
 };
 
 // Workspace layout (byte offsets).

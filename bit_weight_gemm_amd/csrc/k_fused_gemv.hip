@@ -55,6 +55,8 @@ struct GemvParams {
     const uint16_t *alpha;
     uint16_t *y;
     float *yf;              // if set: fp32 results here instead of y
+    uint8_t *qa_codes;      // if set: z_kernel also quantises x (codes, scales)
+    uint8_t *qa_scales;
     uint32_t *epoch;        // workspace header word 0
     uint32_t *seen;         // workspace header flags, one per workgroup
     uint64_t *zt;           // z as (value | tag << 32), [M][rpad]  (one launch)
@@ -538,6 +540,13 @@ __global__ void __launch_bounds__(kGemvThreads) fused_gemv_kernel(GemvParams p) 
 template <int MM>
 __global__ void __launch_bounds__(kGemvThreads) z_kernel(GemvParams p) {
     __shared__ float s_red[8];
+    // the activation's FP4 quantisation rides along (read by the product)
+    if (p.qa_codes) {
+        const int64_t nb = (int64_t)MM * (p.K >> 4);
+        for (int64_t blk = (int64_t)blockIdx.x * kGemvThreads + threadIdx.x; blk < nb;
+             blk += (int64_t)gridDim.x * kGemvThreads)
+            quant_act_block(p.x, blk, p.qa_codes, p.qa_scales);
+    }
     // Workgroups are dispatched to the 8 XCDs in turn (b % 8).  The items of
     // one V word (32 / kZI consecutive items) are mapped to workgroups of one
     // XCD, so that word's column of V is fetched into one L2 only.  The map
@@ -659,6 +668,8 @@ hipError_t launch_gemv(const GemmArgs &a, bool two_launch, hipStream_t stream) {
     p.alpha = a.alpha;
     p.y = a.y;
     p.yf = a.yf;
+    p.qa_codes = a.qa_codes;
+    p.qa_scales = a.qa_scales;
     p.g = a.g;
     p.N = a.N;
     p.K = a.K;

@@ -100,6 +100,8 @@ struct MfmaParams {
     uint32_t *zcnt;             // [W]
     uint32_t *zA;               // [W][MB][2 hi/lo][64 lanes][4] bf16 pairs of z / g
     float *zf;                  // if set: plain fp32 z [M][rpad] as well (separate-launch use)
+    uint8_t *qa_codes;          // if set: the z kernel also quantises x (codes, scales)
+    uint8_t *qa_scales;
     int rpad;
     // product kernel
     int S, cps, chunks, RB, Gs;
@@ -178,6 +180,13 @@ __global__ void __launch_bounds__(kZThreads) mfma_z_kernel(MfmaParams p) {
     __shared__ uint32_t s_last;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int w = blockIdx.x % p.W, s = blockIdx.x / p.W;
+    // the activation's FP4 quantisation rides along (read by the product)
+    if (p.qa_codes) {
+        const int64_t nb = (int64_t)p.M * (p.K >> 4);
+        for (int64_t blk = (int64_t)blockIdx.x * kZThreads + threadIdx.x; blk < nb;
+             blk += (int64_t)gridDim.x * kZThreads)
+            quant_act_block(p.x, blk, p.qa_codes, p.qa_scales);
+    }
     const int col = lane & 15, grp = lane >> 4;
     const int steps = p.K >> 5;
     const int step0 = s * p.zsteps;
@@ -645,6 +654,8 @@ MfmaParams mfma_params(const GemmArgs &a, MfmaPlan &q_out) {
     p.alpha = a.alpha;
     p.y = a.y;
     p.yf = a.yf;
+    p.qa_codes = a.qa_codes;
+    p.qa_scales = a.qa_scales;
     p.g = a.g;
     p.M = a.M;
     p.N = a.N;

@@ -33,40 +33,14 @@ hipError_t launch_pack_signs(const int8_t *signs, int64_t rows, int64_t cols, ui
     return hipGetLastError();
 }
 
-// One thread per block of 16 activations (row m, block b): two 16-byte loads,
-// amax by integer max over the magnitude bits (bf16 magnitudes order like
-// integers), scale = E4M3(amax / 6) with a correctly rounded fp32 division,
-// codes by exact comparisons with the E2M1 midpoints times the scale; one
-// 8-byte store of the codes and one byte of scale.
+// One thread per block of 16 activations (row m, block b); the arithmetic is
+// quant_act_block (biloco_device.h).
 __global__ void __launch_bounds__(256)
 quant_act_kernel(const uint16_t *__restrict__ x, int64_t nblocks, uint8_t *__restrict__ codes,
                  uint8_t *__restrict__ scales) {
     const int64_t blk = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (blk >= nblocks) return;
-    const uint4 *src = reinterpret_cast<const uint4 *>(x + blk * 16);
-    const uint4 v0 = src[0], v1 = src[1];
-    const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-    uint32_t amax_bits = 0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        amax_bits = max(amax_bits, w[j] & 0x7FFFu);
-        amax_bits = max(amax_bits, (w[j] >> 16) & 0x7FFFu);
-    }
-    const float amax = bf16_to_f32(amax_bits);
-    const uint32_t sb = f32_to_e4m3_rne(amax / 6.0f);
-    const float s = e4m3_to_f32(sb);
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        const uint32_t h = (j & 1) ? (w[j >> 1] >> 16) : (w[j >> 1] & 0xFFFFu);
-        const float a = bf16_to_f32(h & 0x7FFFu);
-        const uint32_t mag = (sb == 0u) ? 0u : e2m1_mag_code(a, s);
-        const uint32_t code = mag | ((h >> 12) & 8u);
-        if (j < 8) lo |= code << (4 * j);
-        else hi |= code << (4 * (j - 8));
-    }
-    *reinterpret_cast<uint2 *>(codes + blk * 8) = make_uint2(lo, hi);
-    scales[blk] = (uint8_t)sb;
+    quant_act_block(x, blk, codes, scales);
 }
 
 hipError_t launch_quant_act(const uint16_t *x, int M, int K, uint8_t *codes, uint8_t *scales,

@@ -61,6 +61,20 @@ class DeviceProblem:
         self.quantize(stream)
         return self.gemm(schedule, stream)
 
+    def gemm_quant(self, schedule: int = B.BILOCO_SCHED_AUTO, stream=None, w_codes=None,
+                   w_scales=None, u_packed=None, v_packed=None, y=None, ws=None):
+        """The same pass as one call: quantise x (into a_codes / a_scales) and the
+        product, the quantisation folded into the z launch where there is one."""
+        return B.biloco_gemm_lowrank_quant(
+            self.x, self.a_codes, self.a_scales,
+            self.w_codes if w_codes is None else w_codes,
+            self.w_scales if w_scales is None else w_scales, self.g,
+            self.v_packed if v_packed is None else v_packed,
+            self.u_packed if u_packed is None else u_packed, self.alpha,
+            self.M, self.N, self.K, self.r, self.y if y is None else y,
+            self.ws if ws is None else ws, self.ws_bytes if ws is None else ws.numel(),
+            schedule=schedule, stream=stream)
+
     def y_float(self) -> np.ndarray:
         bits = self.y.cpu().numpy().view(np.uint16).astype(np.uint32) << 16
         return bits.view(np.float32).astype(np.float64)

@@ -219,6 +219,24 @@ biloco_status biloco_gemm_lowrank_sched(const uint8_t *a_codes, const uint8_t *a
                                         uint16_t *y_bf16, void *workspace, size_t workspace_bytes,
                                         int32_t schedule, hipStream_t stream);
 
+/* The activation quantisation and the product in one call (the per-token
+ * hot path of the BiLoCo README's section "Kernel": FP4(x), then the fused
+ * product).  Writes a_codes / a_scales exactly as biloco_quant_act_fp4 would
+ * (they are OUTPUTS here, and must not overlap any other array), then
+ * computes y exactly as biloco_gemm_lowrank_sched.  Where the schedule
+ * computes z in a launch of its own (r > 0: BILOCO_SCHED_UNFUSED at M <= 2,
+ * BILOCO_SCHED_FUSED_MFMA), that launch also quantises x, so the call takes
+ * one launch fewer than the two calls; elsewhere the quantisation is a
+ * launch of its own.  x_bf16 is required also when r == 0.  Same limits,
+ * workspace and errors as biloco_gemm_lowrank_sched. */
+biloco_status biloco_gemm_lowrank_quant(const uint16_t *x_bf16, uint8_t *a_codes, uint8_t *a_scales,
+                                        const uint8_t *w_codes, const uint8_t *w_scales,
+                                        float w_global_scale, const uint32_t *v_packed,
+                                        const uint32_t *u_packed, const uint16_t *alpha_bf16,
+                                        int32_t M, int32_t N, int32_t K, int32_t r, uint16_t *y_bf16,
+                                        void *workspace, size_t workspace_bytes, int32_t schedule,
+                                        hipStream_t stream);
+
 /* Host-only argument check of biloco_gemm_lowrank_sched: returns the status
  * the call would return for these arguments before launching anything.
  * Makes no HIP call (usable without a GPU). */

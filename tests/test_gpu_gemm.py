@@ -158,3 +158,33 @@ def test_bounded_wait_fallback_forced_from_host():
     out = subprocess.run([sys.executable, "-c", _FALLBACK_SCRIPT.format(root=root)], env=env,
                          capture_output=True, text=True, timeout=300)
     assert out.returncode == 0 and "FALLBACK_OK" in out.stdout, out.stdout + out.stderr
+
+
+def _fused_quant_case(d, y_ref, schedules):
+    p = DeviceProblem(d, quantize=False)
+    rc, rs = oracle.quant_act_fp4(d["x"])
+    for s in schedules:
+        p.a_codes.fill_(0x5A)
+        p.a_scales.fill_(0x33)
+        p.y.zero_()
+        p.gemm_quant(s)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(p.a_codes.cpu().numpy(), rc, err_msg=f"schedule {s}")
+        np.testing.assert_array_equal(p.a_scales.cpu().numpy(), rs, err_msg=f"schedule {s}")
+        check_y(p.y_float(), y_ref, f"quantise + product, schedule {s}")
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
+def test_quant_and_product_in_one_call(cfg):
+    # biloco_gemm_lowrank_quant: the activation codes and scales it writes are
+    # the oracle's bit for bit, and y is within tolerance, on every schedule
+    d, y_ref = _case(cfg)
+    _fused_quant_case(d, y_ref, [B.BILOCO_SCHED_AUTO] + _schedules(d))
+
+
+@pytest.mark.parametrize("M,K,N,r", [(2, 1024, 300, 40), (17, 480, 77, 65), (5, 256, 200, 0)])
+def test_quant_and_product_in_one_call_edges(M, K, N, r):
+    d = wl.make_inputs(M, K, N, r, seed=900 + M)
+    y_ref = oracle.gemm_lowrank(d["x"], d["wcode"], d["wscales"], d["g"], d["V"], d["U"],
+                                d["alpha"])
+    _fused_quant_case(d, y_ref, [B.BILOCO_SCHED_AUTO] + _schedules(d))
