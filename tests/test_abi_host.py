@@ -174,3 +174,28 @@ def test_peel_rejects_before_hip():
         assert call(**{k: ok[k] + 8}) == B.BILOCO_ERR_INVALID_VALUE, k
     assert call(wsb=ws - 1) == B.BILOCO_ERR_WORKSPACE_TOO_SMALL
     assert call(R=A + 64) == B.BILOCO_ERR_INVALID_VALUE               # R inside W
+
+
+def test_gemm_quant_rejects_before_hip():
+    L = B.lib()
+    M, N, K, r = 2, 256, 256, 16
+    ws = B.biloco_gemm_workspace_bytes(M, N, K, r)
+    names = ["x", "ac", "as_", "wc", "wsc", "g", "vp", "up", "al", "M", "N", "K", "r", "y", "ws",
+             "wsb", "sched", "stream"]
+    ok = dict(x=A * 3, ac=A * 1, as_=A * 2, wc=A * 4, wsc=A * 5, g=1.0, vp=A * 6, up=A * 7,
+              al=A * 8, M=M, N=N, K=K, r=r, y=A * 10, ws=A * 20, wsb=ws, sched=0, stream=None)
+
+    def call(**kw):
+        args = dict(ok)
+        args.update(kw)
+        return L.biloco_gemm_lowrank_quant(*[args[k] for k in names])
+
+    assert call(x=None) == B.BILOCO_ERR_INVALID_VALUE
+    assert call(x=None, r=0, vp=None, up=None, al=None) == B.BILOCO_ERR_INVALID_VALUE
+    assert call(ac=None) == B.BILOCO_ERR_INVALID_VALUE
+    assert call(M=33) == B.BILOCO_ERR_UNSUPPORTED
+    assert call(wsb=ws - 1) == B.BILOCO_ERR_WORKSPACE_TOO_SMALL
+    assert call(ac=A * 3 + 64) == B.BILOCO_ERR_INVALID_VALUE       # codes inside x
+    assert call(as_=A * 4 + 16) == B.BILOCO_ERR_INVALID_VALUE      # scales inside w_codes
+    assert call(ac=A * 2) == B.BILOCO_ERR_INVALID_VALUE            # codes over scales
+    assert call(sched=9) == B.BILOCO_ERR_INVALID_VALUE
