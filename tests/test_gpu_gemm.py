@@ -188,3 +188,67 @@ def test_quant_and_product_in_one_call_edges(M, K, N, r):
     y_ref = oracle.gemm_lowrank(d["x"], d["wcode"], d["wscales"], d["g"], d["V"], d["U"],
                                 d["alpha"])
     _fused_quant_case(d, y_ref, [B.BILOCO_SCHED_AUTO] + _schedules(d))
+
+
+def _degenerate(d, what):
+    """Degenerate operands of the method: the oracle's y for them has a plain
+    form, checked before the GPU is compared with it."""
+    d = dict(d)
+    if what == "x_zero":
+        d["x"] = np.zeros_like(d["x"])                       # y = 0 exactly
+    elif what == "r_codes_zero":
+        d["wcode"] = np.zeros_like(d["wcode"])               # y = correction only
+        d["wcodes_packed"] = wl.pack_nibbles(d["wcode"])
+    elif what == "alpha_zero":
+        d["alpha"] = np.zeros_like(d["alpha"])               # y = FP4 product only
+    elif what == "signs_plus":
+        d["U"] = np.ones_like(d["U"])                        # C = (sum alpha)(sum_k x)
+        d["V"] = np.ones_like(d["V"])
+    elif what == "negative_zero_codes":
+        d["wcode"] = np.where(d["wcode"] == 0, 8, d["wcode"]).astype(np.uint8)   # -0 codes
+        d["wcodes_packed"] = wl.pack_nibbles(d["wcode"])
+    return d
+
+
+@pytest.mark.parametrize("what", ["x_zero", "r_codes_zero", "alpha_zero", "signs_plus",
+                                  "negative_zero_codes"])
+@pytest.mark.parametrize("M", [1, 2, 8, 32])
+def test_degenerate_operands(what, M):
+    base = wl.make_inputs(M, 1024, 520, 96, seed=70 + M)
+    d = _degenerate(base, what)
+    y_ref = oracle.gemm_lowrank(d["x"], d["wcode"], d["wscales"], d["g"], d["V"], d["U"],
+                                d["alpha"])
+    parts = oracle.gemm_lowrank(d["x"], d["wcode"], d["wscales"], d["g"], d["V"], d["U"],
+                                d["alpha"], parts=True)
+    if what == "x_zero":
+        assert not np.any(y_ref)
+    elif what == "r_codes_zero":
+        assert not np.any(parts["G"])
+    elif what == "alpha_zero":
+        assert not np.any(parts["C"])
+    elif what == "signs_plus":
+        xs = wl.bf16_bits_to_f32(d["x"]).astype(np.float64).sum(axis=1)
+        al = wl.bf16_bits_to_f32(d["alpha"]).astype(np.float64).sum()
+        np.testing.assert_allclose(parts["C"], np.outer(xs * al, np.ones(d["N"])), rtol=1e-12,
+                                   atol=1e-12)
+    p = DeviceProblem(d)
+    for s in _schedules(d):
+        y, _ = _run(d, s, p)
+        if what == "x_zero":
+            assert not np.any(y), f"schedule {s}: y not exactly zero"
+        else:
+            check_y(y, y_ref, f"{what} M={M} schedule {s}")
+
+
+@pytest.mark.parametrize("M,r", [(1, 1500), (3, 1500), (32, 2048)])
+def test_rank_above_1024(M, r):
+    # ranks the pages do not reach: the schedules that take them must stay exact
+    d = wl.make_inputs(M, 512, 300, r, seed=5 + r)
+    y_ref = oracle.gemm_lowrank(d["x"], d["wcode"], d["wscales"], d["g"], d["V"], d["U"],
+                                d["alpha"])
+    p = DeviceProblem(d)
+    scheds = _schedules(d)
+    assert scheds, "no schedule takes this shape"
+    for s in scheds:
+        y, _ = _run(d, s, p)
+        check_y(y, y_ref, f"M={M} r={r} schedule {s}")
