@@ -13,10 +13,10 @@
 // then one pass over the read-only fp32 W (row products for R v, column
 // products for R^T u) plus small kernels, and W stays the only large array.
 //
-// Per step of term i: coef (beta_j = alpha_j (v_j . v)), row (s = R v),
-// pack (u = sign(s), gamma_j = alpha_j (u_j . u)), col (K-slice partials of
-// W^T u), colfin (t = R^T u, v = sign(t)); after the T steps one
-// term-finishing launch.  At the end: the Gram matrix of the sign terms, a
+// Per step of term i: coef (beta_j = alpha_j (v_j . v)), row (R v and
+// u = sign(R v) by atomic or), coef (gamma_j = alpha_j (u_j . u)), col
+// (K-slice partials of W^T u), colfin (t = R^T u, v = sign(t)); the two coef
+// launches only when i > 0; after the T steps one term-finishing launch.  At the end: the Gram matrix of the sign terms, a
 // blocked Cholesky solve of the normal equations, and R = W - U diag(alpha)
 // V^T with 4-bit lookup tables of the coefficients.
 //
@@ -38,7 +38,7 @@ constexpr int kColUnroll = 8;          // rows in flight per thread in the colum
 struct PeelLayout {
     int64_t m, n;
     int r, Wm, Wn, RW, S, rows_per_slice, NBf;
-    size_t ubits, vbits, ucur, vcur, s, coef, ag, tpart, red, bvec, gram, sol, bad, total;
+    size_t ubits, vbits, ucur, vcur, coef, ag, tpart, red, bvec, gram, sol, bad, total;
 };
 
 size_t al256(size_t x) { return (x + 255) / 256 * 256; }
@@ -63,7 +63,6 @@ PeelLayout peel_layout(int64_t m, int64_t n, int r) {
     L.vbits = take((size_t)r * L.Wn * 4);
     L.ucur = take((size_t)L.Wm * 4);
     L.vcur = take((size_t)L.Wn * 4);
-    L.s = take((size_t)m * 4);
     L.coef = take((size_t)r * 4);
     L.ag = take((size_t)r * 4);
     L.tpart = take((size_t)L.S * (size_t)n * 4);
@@ -78,7 +77,7 @@ PeelLayout peel_layout(int64_t m, int64_t n, int r) {
 
 struct PeelPtrs {
     uint32_t *ubits, *vbits, *ucur, *vcur;
-    float *s, *coef, *ag, *tpart, *red;
+    float *coef, *ag, *tpart, *red;
     double *bvec, *gram, *sol;
     int *bad;
 };
@@ -87,7 +86,7 @@ PeelPtrs peel_ptrs(const PeelLayout &L, void *ws) {
     char *b = static_cast<char *>(ws);
     return PeelPtrs{reinterpret_cast<uint32_t *>(b + L.ubits), reinterpret_cast<uint32_t *>(b + L.vbits),
                     reinterpret_cast<uint32_t *>(b + L.ucur),  reinterpret_cast<uint32_t *>(b + L.vcur),
-                    reinterpret_cast<float *>(b + L.s),        reinterpret_cast<float *>(b + L.coef),
+                    reinterpret_cast<float *>(b + L.coef),
                     reinterpret_cast<float *>(b + L.ag),       reinterpret_cast<float *>(b + L.tpart),
                     reinterpret_cast<float *>(b + L.red),      reinterpret_cast<double *>(b + L.bvec),
                     reinterpret_cast<double *>(b + L.gram),    reinterpret_cast<double *>(b + L.sol),
@@ -111,43 +110,12 @@ __device__ __forceinline__ int wave_isum(int v) {
 // ---------------------------------------------------------------------------
 // coef: one wave per earlier term j < i:
 //   coef[j] = alpha_j * (len - 2 popcount(rows[j] ^ cur))       (= alpha_j (x_j . x))
-// With src_f set, cur is first built in LDS as the sign bits of src_f (bit =
-// src_f < 0), and workgroup 0 also stores it at cur_out.
+// cur (the current u or v words, bits past len cleared) is staged in LDS.
 __global__ void __launch_bounds__(kPeelThreads)
-peel_coef_kernel(const uint32_t *__restrict__ rows, const uint32_t *__restrict__ cur_in,
-                 const float *__restrict__ src_f, uint32_t *__restrict__ cur_out, int words,
+peel_coef_kernel(const uint32_t *__restrict__ rows, const uint32_t *__restrict__ cur_in, int words,
                  int64_t len, int i, const float *__restrict__ ag, float *__restrict__ coef) {
     extern __shared__ uint32_t cur[];
-    if (src_f) {
-        // each wave packs 64 consecutive signs per round by ballot; the loads
-        // of 8 rounds are issued before their ballots
-        constexpr int kRounds = 8;
-        const int lane = threadIdx.x & 63;
-        const int64_t total = (int64_t)words * 32;
-        for (int64_t base0 = (int64_t)(threadIdx.x >> 6) * 64; base0 < total;
-             base0 += (int64_t)kPeelThreads * kRounds) {
-            float x[kRounds];
-#pragma unroll
-            for (int u = 0; u < kRounds; ++u) {
-                const int64_t k = base0 + (int64_t)kPeelThreads * u + lane;
-                x[u] = k < len ? src_f[k] : 0.0f;
-            }
-#pragma unroll
-            for (int u = 0; u < kRounds; ++u) {
-                const int64_t base = base0 + (int64_t)kPeelThreads * u;
-                if (base >= total) break;              // uniform over the wave
-                const uint64_t bal = __ballot(x[u] < 0.0f);
-                const int w = (int)(base >> 5);
-                if (lane == 0) cur[w] = (uint32_t)bal;
-                if (lane == 32 && w + 1 < words) cur[w + 1] = (uint32_t)(bal >> 32);
-            }
-        }
-    } else {
-        for (int w = threadIdx.x; w < words; w += kPeelThreads) cur[w] = cur_in[w] & valid_mask(w, len);
-    }
-    __syncthreads();
-    if (cur_out && blockIdx.x == 0)
-        for (int w = threadIdx.x; w < words; w += kPeelThreads) cur_out[w] = cur[w];
+    for (int w = threadIdx.x; w < words; w += kPeelThreads) cur[w] = cur_in[w] & valid_mask(w, len);
     __syncthreads();
     const int j = blockIdx.x * (kPeelThreads / 64) + (threadIdx.x >> 6), lane = threadIdx.x & 63;
     if (j >= i) return;
@@ -159,12 +127,13 @@ peel_coef_kernel(const uint32_t *__restrict__ rows, const uint32_t *__restrict__
 
 // ---------------------------------------------------------------------------
 // row: one wave per row a (4 rows per workgroup):
-//   s[a] = sum_k W[a][k] v_k  -  sum_{j<i} coef[j] u_j[a]
-// v from its packed bits (LDS); u_j[a] from the row-major packed U words.
+//   s_a = sum_k W[a][k] v_k  -  sum_{j<i} coef[j] u_j[a],  u_a = sign(s_a)
+// v from its packed bits (LDS); u_j[a] from the row-major packed U words;
+// u's bit goes into ucur by an atomic or (ucur cleared before the launch).
 __global__ void __launch_bounds__(kPeelThreads)
 peel_row_kernel(const float4 *__restrict__ W, int64_t m, int64_t n4, const uint32_t *__restrict__ vbits,
                 int Wn, const uint32_t *__restrict__ up, int i, const float *__restrict__ coef,
-                float *__restrict__ s) {
+                uint32_t *__restrict__ ucur) {
     extern __shared__ uint32_t vb[];
     for (int w = threadIdx.x; w < Wn; w += kPeelThreads) vb[w] = vbits[w];
     __syncthreads();
@@ -200,7 +169,10 @@ peel_row_kernel(const float4 *__restrict__ W, int64_t m, int64_t n4, const uint3
         corr += bit ? -coef[j] : coef[j];
     }
     const float tot = wave_sum(acc0 + acc1) - wave_sum(corr);
-    if (lane == 0) s[a] = tot;
+    // u = sign(R v): set the row's bit (the word was cleared before this launch)
+    if (lane == 0 && tot < 0.0f)
+        __hip_atomic_fetch_or(ucur + (a >> 5), 1u << (a & 31), __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------------------
@@ -251,7 +223,12 @@ peel_col_kernel(const float4 *__restrict__ W, int64_t m, int64_t n4, const uint3
 __global__ void __launch_bounds__(kPeelThreads)
 peel_colfin_kernel(const float *__restrict__ tpart, int S, int64_t n, const uint32_t *__restrict__ vp,
                    int i, const float *__restrict__ coef, uint32_t *__restrict__ vcur, int last,
-                   float *__restrict__ red) {
+                   float *__restrict__ red, uint32_t *__restrict__ ucur, int Wm) {
+    // u of this step has been read (coef, col); clear it for the next step's
+    // row launch, except after a term's last step (the term launch reads it)
+    if (!last)
+        for (int w = blockIdx.x * kPeelThreads + threadIdx.x; w < Wm; w += gridDim.x * kPeelThreads)
+            ucur[w] = 0u;
     __shared__ float part[8][32], corr[8][32];
     const int grp = threadIdx.x >> 5, c = threadIdx.x & 31;
     const int64_t k = (int64_t)blockIdx.x * 32 + c;
@@ -299,7 +276,7 @@ peel_colfin_kernel(const float *__restrict__ tpart, int S, int64_t n, const uint
 // row-major packed outputs (cleared before the first term).
 __global__ void __launch_bounds__(1024)
 peel_term_kernel(int i, int64_t m, int64_t n, int NBf, const float *__restrict__ red,
-                 const uint32_t *__restrict__ ucur, const uint32_t *__restrict__ vcur, int Wm, int Wn,
+                 uint32_t *__restrict__ ucur, const uint32_t *__restrict__ vcur, int Wm, int Wn,
                  float *__restrict__ ag, double *__restrict__ bvec, uint32_t *__restrict__ ubits,
                  uint32_t *__restrict__ vbits, uint32_t *__restrict__ up, uint32_t *__restrict__ vp) {
     __shared__ double sa[16], sb[16];
@@ -334,6 +311,8 @@ peel_term_kernel(int i, int64_t m, int64_t n, int NBf, const float *__restrict__
         up[(int64_t)wr * m + x] |= ((ucur[x >> 5] >> (x & 31)) & 1u) << sh;
     for (int64_t x = threadIdx.x; x < n; x += 1024)
         vp[(int64_t)wr * n + x] |= ((vcur[x >> 5] >> (x & 31)) & 1u) << sh;
+    __syncthreads();
+    for (int w = threadIdx.x; w < Wm; w += 1024) ucur[w] = 0u;   // for the next term's first row launch
 }
 
 // zero-fill (no memset node: callers may capture the call in a graph)
@@ -561,6 +540,9 @@ hipError_t launch_peel(const float *W, int64_t m, int64_t n, int r, int T, const
         hipLaunchKernelGGL(peel_zero_kernel, dim3((unsigned)(grid < 4096 ? grid : 4096)),
                            dim3(kPeelThreads), 0, stream, v_packed, (int64_t)L.RW * n);
         PEEL_CHECK();
+        hipLaunchKernelGGL(peel_zero_kernel, dim3(1), dim3(kPeelThreads), 0, stream, P.ucur,
+                           (int64_t)L.Wm);
+        PEEL_CHECK();
     }
     const unsigned row_grid = (unsigned)((m + 3) / 4);
     const dim3 col_grid((unsigned)((n4 + kPeelThreads - 1) / kPeelThreads), (unsigned)L.S);
@@ -571,26 +553,26 @@ hipError_t launch_peel(const float *W, int64_t m, int64_t n, int r, int T, const
             // beta_j = alpha_j (v_j . v)
             if (i > 0) {
                 hipLaunchKernelGGL(peel_coef_kernel, dim3((unsigned)((i + 3) / 4)), dim3(kPeelThreads),
-                                   (size_t)L.Wn * 4, stream, P.vbits, vsrc, nullptr, nullptr, L.Wn, n,
-                                   i, P.ag, P.coef);
+                                   (size_t)L.Wn * 4, stream, P.vbits, vsrc, L.Wn, n, i, P.ag, P.coef);
                 PEEL_CHECK();
             }
             // s = R v
             hipLaunchKernelGGL(peel_row_kernel, dim3(row_grid), dim3(kPeelThreads), (size_t)L.Wn * 4,
-                               stream, W4, m, n4, vsrc, L.Wn, u_packed, i, P.coef, P.s);
+                               stream, W4, m, n4, vsrc, L.Wn, u_packed, i, P.coef, P.ucur);
             PEEL_CHECK();
-            // u = sign(s); gamma_j = alpha_j (u_j . u)
-            hipLaunchKernelGGL(peel_coef_kernel, dim3((unsigned)(i > 0 ? (i + 3) / 4 : 1)),
-                               dim3(kPeelThreads), (size_t)L.Wm * 4, stream, P.ubits, nullptr, P.s,
-                               P.ucur, L.Wm, m, i, P.ag, P.coef);
-            PEEL_CHECK();
+            // gamma_j = alpha_j (u_j . u)
+            if (i > 0) {
+                hipLaunchKernelGGL(peel_coef_kernel, dim3((unsigned)((i + 3) / 4)), dim3(kPeelThreads),
+                                   (size_t)L.Wm * 4, stream, P.ubits, P.ucur, L.Wm, m, i, P.ag, P.coef);
+                PEEL_CHECK();
+            }
             // W^T u in K-slices, then t = R^T u and v = sign(t)
             hipLaunchKernelGGL(peel_col_kernel, col_grid, dim3(kPeelThreads), 0, stream, W4, m, n4,
                                P.ucur, L.rows_per_slice, reinterpret_cast<float4 *>(P.tpart));
             PEEL_CHECK();
             hipLaunchKernelGGL(peel_colfin_kernel, dim3(fin_grid), dim3(kPeelThreads), 0, stream,
                                P.tpart, L.S, n, v_packed, i, P.coef, P.vcur, t == T - 1 ? 1 : 0,
-                               P.red);
+                               P.red, P.ucur, L.Wm);
             PEEL_CHECK();
         }
         hipLaunchKernelGGL(peel_term_kernel, dim3(1), dim3(1024), 0, stream, i, m, n, L.NBf, P.red,
