@@ -58,7 +58,7 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kZThreads = 512;          // z kernel: 8 waves
 constexpr int kZWaves = kZThreads / 64;
-constexpr int kZStepsPerWave = 8;       // K-steps (32 k) per wave in the z kernel
+constexpr int kZStepsPerWave = 4;       // K-steps (32 k) per wave in the z kernel
 constexpr int kPThreads = 512;          // product kernel: 8 waves
 constexpr int kPWaves = kPThreads / 64;
 constexpr int kChunkK = 128;
