@@ -56,11 +56,15 @@ typedef int32_t biloco_status;
  * the fastest mode for batch size and rank, and can list the modes a shape
  * allows).  The modes here are this library's own, designed for gfx950. */
 #define BILOCO_SCHED_AUTO        0  /* pick per shape (biloco_default_schedule) */
-#define BILOCO_SCHED_UNFUSED     1  /* z kernel, then GEMM + epilogue kernel (two launches) */
+#define BILOCO_SCHED_UNFUSED     1  /* two launches: z, then a vector-ALU product kernel that
+                                       adds the correction before the store (the default at
+                                       M <= 2; a plain, slow fallback at larger M) */
 #define BILOCO_SCHED_FUSED_GEMV  2  /* one launch; vector-ALU dot products; M <= 2 */
 #define BILOCO_SCHED_FUSED_MFMA  3  /* matrix-core products for any M <= 32: a z kernel
                                        (skipped when r == 0), then one product kernel whose
-                                       accumulators take the correction before the store */
+                                       accumulators take the correction before the store,
+                                       then (only when K is split over workgroups) a launch
+                                       that sums the K-slices; the default at M >= 3 */
 #define BILOCO_SCHED_COMPOSED    4  /* separate launches: the plain FP4 product (fp32, in the
                                        workspace), z, then y = bf16(product + z . U^T) by
                                        4-bit sign lookup tables: the unfused form the fused
