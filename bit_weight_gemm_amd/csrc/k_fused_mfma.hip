@@ -72,14 +72,18 @@ constexpr int kSumBatch = 8;            // K-slice partials loaded at once by a 
 //              VGPRs, a workgroup covers 8 kCpw chunks of K
 //   kRbw*      row blocks per workgroup: every wave holds kRbw x kCpw 16-byte
 //              code loads in flight at once
-// A wave's scale bytes in a row (kCpw x 8 <= 24) fit a 16-byte-aligned window
-// of three 16-byte pieces.
+//   kCpwWide, kRbwWide   the whole-K variant for M <= 16 (no K split while
+//              8 kCpwWide chunks cover K): fewer row blocks, more chunks
+// A wave's scale bytes in a row (CPW x 8) fit a 16-byte-aligned window of
+// scale_pieces(CPW) 16-byte pieces.
 template <int MB> struct MfmaShape {
     static constexpr int kCpw = 3;
     static constexpr int kRbwSmall = 3;                 // row blocks per workgroup, small variant
     static constexpr int kRbwLarge = MB == 1 ? 8 : 7;   // row blocks per workgroup, large variant
+    static constexpr int kCpwWide = 5;
+    static constexpr int kRbwWide = 4;
 };
-static_assert(MfmaShape<1>::kCpw * 8 + 14 <= 48 && MfmaShape<2>::kCpw * 8 + 14 <= 48, "scale window");
+__host__ __device__ constexpr int scale_pieces(int cpw) { return (cpw * 8 + 14 + 15) / 16; }
 
 struct MfmaParams {
     const uint8_t *a_codes;
@@ -311,14 +315,13 @@ __global__ void __launch_bounds__(kZThreads) mfma_z_kernel(MfmaParams p) {
 // block past the range, chunk past the wave's share) loads zeros through an
 // out-of-range buffer offset, so every path issues the same loads and the
 // hardware wait counts stay exact.
-template <int MB, int RBW>
+template <int MB, int RBW, int CPW>
 __global__ void __launch_bounds__(kPThreads) mfma_product_kernel(MfmaParams p) {
-    using Shape = MfmaShape<MB>;
-    constexpr int CPW = Shape::kCpw;
+    constexpr int PPR = scale_pieces(CPW);              // 16-byte scale pieces per row
     // LDS: the waves' partial sums [wave][row block][mb][64 lanes], then each
-    // wave's block scales of R [wave][row][3 16-byte pieces]
+    // wave's block scales of R [wave][row][PPR 16-byte pieces]
     extern __shared__ float4_t s_part[];
-    constexpr int SCL = (RBW * 16 * 3 + 63) / 64;      // scale loads per lane
+    constexpr int SCL = (RBW * 16 * PPR + 63) / 64;    // scale loads per lane
     u32x4_t *s_sc = reinterpret_cast<u32x4_t *>(s_part + (size_t)kPWaves * RBW * MB * 64);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int col = lane & 15, grp = lane >> 4;
@@ -353,14 +356,14 @@ __global__ void __launch_bounds__(kPThreads) mfma_product_kernel(MfmaParams p) {
         }
 
     // ---- block scales of R for this wave's chunks, every row of the range:
-    // per row the 16-byte-aligned 48-byte window that holds the wave's (at
-    // most 3 x 8) scale bytes; 3 pieces per row, kScLoads 16-byte loads per lane
+    // per row the 16-byte-aligned window of PPR pieces that holds the wave's
+    // (at most CPW x 8) scale bytes; SCL 16-byte loads per lane
     const int pb = rb_begin, nrb = rb_end - rb_begin;     // 1 .. RBW row blocks
     u32x4_t sc_v[SCL];
 #pragma unroll
     for (int t = 0; t < SCL; ++t) {
         const int idx = lane + 64 * t;
-        const int rl = idx / 3, piece = idx - rl * 3;
+        const int rl = idx / PPR, piece = idx - rl * PPR;
         const int n = pb * 16 + rl;
         const bool ok = rl < nrb * 16 && n < p.N && cpw > 0;
         const int a0 = (n * KB + wc0 * 8) & ~15;
@@ -405,18 +408,18 @@ __global__ void __launch_bounds__(kPThreads) mfma_product_kernel(MfmaParams p) {
 
     // ---- this wave's scale windows to its own LDS region (no barrier: only
     // this wave reads them; its scale loads are older than its code loads)
-    u32x4_t *my_sc = s_sc + (size_t)wave * RBW * 16 * 3;
+    u32x4_t *my_sc = s_sc + (size_t)wave * RBW * 16 * PPR;
 #pragma unroll
     for (int t = 0; t < SCL; ++t) {
         const int idx = lane + 64 * t;
-        if (idx < RBW * 16 * 3) my_sc[idx] = sc_v[t];
+        if (idx < RBW * 16 * PPR) my_sc[idx] = sc_v[t];
     }
     // scale pair of chunk c of row block rbl for this lane: bytes 2 grp and
     // 2 grp + 1 of the chunk's 8, shifted by the row's window alignment
     auto scale_pair = [&](int rbl, int c) -> uint32_t {
         const int n = (pb + rbl) * 16 + col;
         const int delta = (n * KB + wc0 * 8) & 15;
-        const int byte = (rbl * 16 + col) * 48 + delta + c * 8 + grp * 2;
+        const int byte = (rbl * 16 + col) * (16 * PPR) + delta + c * 8 + grp * 2;
         return *reinterpret_cast<const uint16_t *>(reinterpret_cast<const uint8_t *>(my_sc) + byte);
     };
 
@@ -562,7 +565,7 @@ __global__ void __launch_bounds__(256) mfma_epilogue_kernel(MfmaParams p) {
 // =====================================================================
 namespace {
 struct MfmaPlan {
-    int mb, W, zs, zsteps, chunks, S, cps, RB, Gs, grid, rbw;
+    int mb, W, zs, zsteps, chunks, S, cps, RB, Gs, grid, rbw, cpw;
     size_t lds;
     // workspace offsets inside the matrix-core area
     size_t off_zpart, off_zcnt, off_za, off_ypart, bytes;
@@ -583,17 +586,21 @@ MfmaPlan mfma_plan(int M, int N, int K, int r) {
         q.zs = (steps + q.zsteps - 1) / q.zsteps;
     }
     // product: the fewest K-slices whose chunks the 8 waves' activation
-    // tiles cover
+    // tiles cover; for one m-block, the whole-K variant when its wider tiles
+    // take K in one slice and the narrow ones would not
     q.chunks = (K + kChunkK - 1) / kChunkK;
-    const int cps_max = kPWaves * (q.mb == 1 ? MfmaShape<1>::kCpw : MfmaShape<2>::kCpw);
+    q.cpw = q.mb == 1 ? MfmaShape<1>::kCpw : MfmaShape<2>::kCpw;
+    const bool wide = q.mb == 1 && q.chunks > kPWaves * q.cpw && q.chunks <= kPWaves * MfmaShape<1>::kCpwWide;
+    if (wide) q.cpw = MfmaShape<1>::kCpwWide;
+    const int cps_max = kPWaves * q.cpw;
     q.S = (q.chunks + cps_max - 1) / cps_max;
     q.cps = (q.chunks + q.S - 1) / q.S;
     q.S = (q.chunks + q.cps - 1) / q.cps;
     q.RB = (N + 15) / 16;
     // row groups per slice: one workgroup per CU when the range of each fits
     // the large variant, more workgroups (several rounds) otherwise
-    const int small = q.mb == 1 ? MfmaShape<1>::kRbwSmall : MfmaShape<2>::kRbwSmall;
-    const int large = q.mb == 1 ? MfmaShape<1>::kRbwLarge : MfmaShape<2>::kRbwLarge;
+    const int small = wide ? MfmaShape<1>::kRbwWide : q.mb == 1 ? MfmaShape<1>::kRbwSmall : MfmaShape<2>::kRbwSmall;
+    const int large = wide ? MfmaShape<1>::kRbwWide : q.mb == 1 ? MfmaShape<1>::kRbwLarge : MfmaShape<2>::kRbwLarge;
     q.Gs = kGridTarget / q.S;
     if (q.Gs < 1) q.Gs = 1;
     if (q.Gs < (q.RB + large - 1) / large) q.Gs = (q.RB + large - 1) / large;
@@ -601,7 +608,7 @@ MfmaPlan mfma_plan(int M, int N, int K, int r) {
     q.grid = q.Gs * q.S;
     const int rb_wg = (q.RB + q.Gs - 1) / q.Gs;
     q.rbw = rb_wg <= small ? small : large;
-    q.lds = (size_t)kPWaves * q.rbw * q.mb * 64 * 16 + (size_t)kPWaves * q.rbw * 16 * 48;
+    q.lds = (size_t)kPWaves * q.rbw * q.mb * 64 * 16 + (size_t)kPWaves * q.rbw * 16 * 16 * scale_pieces(q.cpw);
     // workspace
     size_t off = 0;
     q.off_zpart = off;
@@ -617,12 +624,12 @@ MfmaPlan mfma_plan(int M, int N, int K, int r) {
 }
 
 // Dynamic LDS above 64 KiB must be allowed once per kernel.
-template <int MB, int RBW>
+template <int MB, int RBW, int CPW>
 hipError_t allow_lds() {
     static std::once_flag once;
     static hipError_t err = hipSuccess;
     std::call_once(once, [] {
-        err = hipFuncSetAttribute(reinterpret_cast<const void *>(&mfma_product_kernel<MB, RBW>),
+        err = hipFuncSetAttribute(reinterpret_cast<const void *>(&mfma_product_kernel<MB, RBW, CPW>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsLimit);
     });
     return err;
@@ -708,20 +715,25 @@ hipError_t launch_gemm_mfma(const GemmArgs &a, hipStream_t stream) {
         if (e != hipSuccess) return e;
     }
     const dim3 grid(q.grid), block(kPThreads);
+    constexpr int c1 = MfmaShape<1>::kCpw, c2 = MfmaShape<2>::kCpw;
     constexpr int s1 = MfmaShape<1>::kRbwSmall, l1 = MfmaShape<1>::kRbwLarge;
     constexpr int s2 = MfmaShape<2>::kRbwSmall, l2 = MfmaShape<2>::kRbwLarge;
-    if (q.mb == 1 && q.rbw == s1) {
-        e = allow_lds<1, s1>();
-        if (e == hipSuccess) hipLaunchKernelGGL((mfma_product_kernel<1, s1>), grid, block, q.lds, stream, p);
+    constexpr int cw = MfmaShape<1>::kCpwWide, rw = MfmaShape<1>::kRbwWide;
+    if (q.mb == 1 && q.cpw == cw) {
+        e = allow_lds<1, rw, cw>();
+        if (e == hipSuccess) hipLaunchKernelGGL((mfma_product_kernel<1, rw, cw>), grid, block, q.lds, stream, p);
+    } else if (q.mb == 1 && q.rbw == s1) {
+        e = allow_lds<1, s1, c1>();
+        if (e == hipSuccess) hipLaunchKernelGGL((mfma_product_kernel<1, s1, c1>), grid, block, q.lds, stream, p);
     } else if (q.mb == 1) {
-        e = allow_lds<1, l1>();
-        if (e == hipSuccess) hipLaunchKernelGGL((mfma_product_kernel<1, l1>), grid, block, q.lds, stream, p);
+        e = allow_lds<1, l1, c1>();
+        if (e == hipSuccess) hipLaunchKernelGGL((mfma_product_kernel<1, l1, c1>), grid, block, q.lds, stream, p);
     } else if (q.rbw == s2) {
-        e = allow_lds<2, s2>();
-        if (e == hipSuccess) hipLaunchKernelGGL((mfma_product_kernel<2, s2>), grid, block, q.lds, stream, p);
+        e = allow_lds<2, s2, c2>();
+        if (e == hipSuccess) hipLaunchKernelGGL((mfma_product_kernel<2, s2, c2>), grid, block, q.lds, stream, p);
     } else {
-        e = allow_lds<2, l2>();
-        if (e == hipSuccess) hipLaunchKernelGGL((mfma_product_kernel<2, l2>), grid, block, q.lds, stream, p);
+        e = allow_lds<2, l2, c2>();
+        if (e == hipSuccess) hipLaunchKernelGGL((mfma_product_kernel<2, l2, c2>), grid, block, q.lds, stream, p);
     }
     if (e != hipSuccess) return e;
     e = hipGetLastError();

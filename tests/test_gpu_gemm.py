@@ -79,7 +79,12 @@ def test_every_batch_size_ragged(M):
                                      # several passes and two K-slices (batch of 32 rows)
                                      (17, 4096, 33000, 64),
                                      # many K-slices with a ragged last one
-                                     (32, 13856, 40, 100)])
+                                     (32, 13856, 40, 100),
+                                     # one m-block, K of 25 .. 40 chunks in one slice of
+                                     # the wide tiles: just past the narrow tiles' reach,
+                                     # a K tail inside a chunk, several passes
+                                     (16, 3200, 50, 1), (9, 4000, 1000, 70),
+                                     (3, 5120, 70000, 33)])
 def test_edge_shapes(M, K, N, r):
     d = wl.make_inputs(M, K, N, r, seed=M * 1000 + N)
     y_ref = oracle.gemm_lowrank(d["x"], d["wcode"], d["wscales"], d["g"], d["V"], d["U"],
