@@ -34,6 +34,9 @@ struct GemmArgs {
 //   [64 KiB, ...)     z as (fp32 value | 32-bit epoch tag << 32) pairs [M][Rpad]
 //   then              z as plain fp32 [M][Rpad] for the two-launch schedule (a
 //                     separate area, so plain floats are never read as tags)
+//   then (M <= 2)     the vector-ALU product's correction operands: z split
+//                     into bf16 high and low parts, laid out per lane
+//                     [M][ceil(Rpad / 512)][64 lanes][4][high, low] (bf16 pairs)
 //   then (256-aligned) the matrix-core schedule's area: z slice partials,
 //                     per-word counters, z/g operands, K-slice partials of y
 //                     and per-row-block counters (sized by mfma_ws_bytes)
@@ -41,15 +44,20 @@ struct GemmArgs {
 //                     and its r = 0 product's split-K partials
 constexpr int kGemvMaxWorkgroups = 8192;
 constexpr size_t kWsHeaderBytes = 64 * 1024;
-inline int rpad32(int r) { return (r + 31) / 32 * 32; }
+__host__ __device__ inline int rpad32(int r) { return (r + 31) / 32 * 32; }
 inline size_t ws_epoch_offset() { return 0; }
 inline size_t ws_seen_offset() { return 256; }
 inline size_t ws_zt_offset() { return kWsHeaderBytes; }
 inline size_t ws_zt_bytes(int M, int r) { return (size_t)8 * (size_t)M * (size_t)rpad32(r); }
 inline size_t ws_zf_offset(int M, int r) { return ws_zt_offset() + ws_zt_bytes(M, r); }
 inline size_t ws_zf_bytes(int M, int r) { return (size_t)4 * (size_t)M * (size_t)rpad32(r); }
+inline size_t ws_zop_offset(int M, int r) { return ws_zf_offset(M, r) + ws_zf_bytes(M, r); }
+__host__ __device__ inline int zop_rounds(int r) { return (rpad32(r) + 511) / 512; }
+inline size_t ws_zop_bytes(int M, int r) {
+    return M <= 2 ? (size_t)M * (size_t)zop_rounds(r) * 2048 : 0;
+}
 inline size_t ws_mfma_offset(int M, int r) {
-    return r > 0 ? (ws_zf_offset(M, r) + ws_zf_bytes(M, r) + 255) / 256 * 256 : 0;
+    return r > 0 ? (ws_zop_offset(M, r) + ws_zop_bytes(M, r) + 255) / 256 * 256 : 0;
 }
 bool mfma_supported(int M, int N, int K, int r);     // shapes the matrix-core schedule handles
 size_t mfma_ws_bytes(int M, int N, int K, int r);    // its workspace area (0 if none is needed)

@@ -32,6 +32,8 @@
 //    reduction per row and m;
 //  * a consumer's wait for z is bounded: when it runs out the consumer
 //    computes the z values itself, so the kernel ends whatever else runs.
+#include <type_traits>
+
 #include "biloco_device.h"
 #include "biloco_internal.h"
 
@@ -62,6 +64,10 @@ struct GemvParams {
     uint64_t *zt;           // z as (value | tag << 32), [M][rpad]  (one launch)
     const float *zf;        // z as plain fp32 [M][rpad] from the z kernel (two launches)
     float *zf_out;          // the same area, written by the z kernel
+    // z / correction operands per lane, [M][ceil(rpad / 512)][64][4][hi, lo]
+    // bf16 pairs (two launches): written by the z kernel when set
+    uint32_t *zop_out;
+    const uint32_t *zop;
     float g;
     int N, K, r, rpad;
     int rows_per_wg;
@@ -232,12 +238,19 @@ __host__ __device__ constexpr int gemv_rows_per_wave(int kbl, int mm) {
          : ((200 - 8 * kbl * mm) / (3 * kbl + 4) <= 1 ? 1 : (200 - 8 * kbl * mm) / (3 * kbl + 4));
 }
 
-// Correction of the wave's rows: bit pairs (pb, pb + 16), pb = lane / 16 + 4 j,
-// of the lane's U words (lane % 16) + 16 q, against z (LDS, [MM][rpad]) split
-// into bf16 high + bf16 low parts; added to the per-lane row sums.
-template <int MM, int R, int QMAX>
+// z in LDS: value (m, i) at m (rpad + rpad / 16) + i + 2 (i / 32).  The two
+// spare floats per 32 put the values one read of the correction takes (16
+// words apart by 32 indices, 4 lane groups apart by 1) on distinct banks.
+__device__ __forceinline__ int zslot(const GemvParams &p, int m, int i) {
+    return m * (p.rpad + (p.rpad >> 4)) + i + 2 * (i >> 5);
+}
+
+// Correction of the wave's first NR rows: bit pairs (pb, pb + 16),
+// pb = lane / 16 + 4 j, of the lane's U words (lane % 16) + 16 q, against z
+// (LDS) split into bf16 high + bf16 low parts; added to the per-lane row sums.
+template <int MM, int NR, int R, int QMAX>
 __device__ __forceinline__ void add_correction(const GemvParams &p, const float *s_z,
-                                               const uint32_t (&uw)[QMAX][R],
+                                               const uint32_t (&ul)[QMAX],
                                                float (&part)[R][MM]) {
     const int lane = threadIdx.x & 63;
     const int W = p.rpad >> 5;
@@ -246,6 +259,10 @@ __device__ __forceinline__ void add_correction(const GemvParams &p, const float 
         if (16 * q >= W) break;
         const int w = (lane & 15) + 16 * q;
         const bool wok = w < W;
+        // word w of row rr, from lane 16 rr + w % 16 (which loaded it)
+        uint32_t uw[NR];
+#pragma unroll
+        for (int rr = 0; rr < NR; ++rr) uw[rr] = __shfl(ul[q], 16 * rr + (lane & 15), 64);
         uint32_t zhi[4][MM], zlo[4][MM];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -253,8 +270,8 @@ __device__ __forceinline__ void add_correction(const GemvParams &p, const float 
 #pragma unroll
             for (int m = 0; m < MM; ++m) {
                 const int i0 = 32 * w + pb, i1 = i0 + 16;
-                const float z0 = (wok && i0 < p.r) ? s_z[m * p.rpad + i0] : 0.0f;
-                const float z1 = (wok && i1 < p.r) ? s_z[m * p.rpad + i1] : 0.0f;
+                const float z0 = (wok && i0 < p.r) ? s_z[zslot(p, m, i0)] : 0.0f;
+                const float z1 = (wok && i1 < p.r) ? s_z[zslot(p, m, i1)] : 0.0f;
                 const uint32_t h0 = __float_as_uint(z0) & 0xFFFF0000u;
                 const uint32_t h1 = __float_as_uint(z1) & 0xFFFF0000u;
                 const uint32_t l0 = __float_as_uint(z0 - __uint_as_float(h0));
@@ -264,14 +281,45 @@ __device__ __forceinline__ void add_correction(const GemvParams &p, const float 
             }
         }
 #pragma unroll
-        for (int rr = 0; rr < R; ++rr) {
+        for (int rr = 0; rr < NR; ++rr) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const uint32_t sg = signs_bf16x2(uw[q][rr], (lane >> 4) + 4 * j);
+                const uint32_t sg = signs_bf16x2(uw[rr], (lane >> 4) + 4 * j);
 #pragma unroll
                 for (int m = 0; m < MM; ++m) {
                     part[rr][m] = dot2_bf16(sg, zhi[j][m], part[rr][m]);
                     part[rr][m] = dot2_bf16(sg, zlo[j][m], part[rr][m]);
+                }
+            }
+        }
+    }
+}
+
+// The same correction with the operands in registers (two launches): zo[q][m]
+// holds, for j = 0 .. 3, the high and low bf16 pairs of z at the lane's
+// indices (i, i + 16), i = 32 w + lane / 16 + 4 j.
+template <int MM, int NR, int R, int QMAX>
+__device__ __forceinline__ void add_correction_ops(const GemvParams &p, const uint32_t (&ul)[QMAX],
+                                                   const u32x4_t (&zo)[QMAX][MM][2],
+                                                   float (&part)[R][MM]) {
+    const int lane = threadIdx.x & 63;
+    const int W = p.rpad >> 5;
+#pragma unroll
+    for (int q = 0; q < QMAX; ++q) {
+        if (16 * q >= W) break;
+        uint32_t uw[NR];
+#pragma unroll
+        for (int rr = 0; rr < NR; ++rr) uw[rr] = __shfl(ul[q], 16 * rr + (lane & 15), 64);
+#pragma unroll
+        for (int rr = 0; rr < NR; ++rr) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t sg = signs_bf16x2(uw[rr], (lane >> 4) + 4 * j);
+#pragma unroll
+                for (int m = 0; m < MM; ++m) {
+                    const u32x4_t &v = zo[q][m][j >> 1];
+                    part[rr][m] = dot2_bf16(sg, v[2 * (j & 1)], part[rr][m]);
+                    part[rr][m] = dot2_bf16(sg, v[2 * (j & 1) + 1], part[rr][m]);
                 }
             }
         }
@@ -284,6 +332,7 @@ __device__ __forceinline__ void add_correction(const GemvParams &p, const float 
 template <int MM, int KBL, int ZMODE>
 __global__ void __launch_bounds__(kGemvThreads) fused_gemv_kernel(GemvParams p) {
     constexpr int R = gemv_rows_per_wave(KBL, MM);
+    static_assert(R >= 1 && R <= 4, "the row-count switch covers 1 .. 4 rows per wave");
     constexpr bool has_z = ZMODE != 0;
     constexpr int QMAX = 2;                    // r <= 1024: two rounds of 16 words
     constexpr int ZP = 2 * MM;                 // z values per thread (MM * r <= MM * 1024)
@@ -292,7 +341,8 @@ __global__ void __launch_bounds__(kGemvThreads) fused_gemv_kernel(GemvParams p) 
     __shared__ uint32_t s_bcast;
     extern __shared__ uint32_t s_dyn[];   // activation f16 pairs [MM][KB][8], then z [MM][rpad]
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // the wave index as a scalar, so that the row count below is one too
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int KB = p.K >> 4, KH = p.K >> 1;
     uint32_t *s_act = s_dyn;
     float *s_z = reinterpret_cast<float *>(s_dyn + (size_t)MM * KB * 8);
@@ -327,30 +377,38 @@ __global__ void __launch_bounds__(kGemvThreads) fused_gemv_kernel(GemvParams p) 
     ZInputs<MM> zin;
     if (z_wg) z_prefetch<MM>(p, blockIdx.x, zin);
     const int nz = MM * p.r;
-    float zpre[ZP];
-    if (ZMODE == 2) {
+    // two launches: this lane's correction operands (z split into bf16 high
+    // and low parts, two dwords per j) for each round of 16 words, rounds
+    // past the last clamped to it; no wait until the correction
+    u32x4_t zo[QMAX][MM][2];
+    if constexpr (ZMODE == 2) {
 #pragma unroll
-        for (int j = 0; j < ZP; ++j) {
-            const int idx = threadIdx.x + kGemvThreads * j;
-            const int ic = idx < nz ? idx : nz - 1;
-            const int m = ic / p.r, i = ic - m * p.r;
-            zpre[j] = p.zf[(int64_t)m * p.rpad + i];
+        for (int q = 0; q < QMAX; ++q)
+#pragma unroll
+            for (int m = 0; m < MM; ++m) {
+                const int qc = min(q, zop_rounds(p.r) - 1);
+                const u32x4_t *src = reinterpret_cast<const u32x4_t *>(
+                    p.zop + (((int64_t)m * zop_rounds(p.r) + qc) * 64 + lane) * 8);
+                zo[q][m][0] = src[0];
+                zo[q][m][1] = src[1];
+            }
+    }
+    // 3. U's words for these rows, one load per round of 16 words: lane
+    // 16 rr + c fetches word c + 16 q of row rr (clamped to a row and word
+    // that exist; such values are never used).  No branch: the waits below
+    // for the activation and z then count these loads exactly and leave them
+    // in flight; the correction shuffles the words to their lanes.
+    uint32_t ul[QMAX];
+#pragma unroll
+    for (int q = 0; q < QMAX; ++q) {
+        ul[q] = 0u;
+        if constexpr (has_z) {
+            const int W = p.rpad >> 5;
+            const int w = min((lane & 15) + 16 * q, W - 1);
+            const int n = min(row0 + min(lane >> 4, max(nrows - 1, 0)), p.N - 1);
+            ul[q] = p.u[(int64_t)w * p.N + n];
         }
     }
-    // 3. U's words for these rows: lane covers word (lane % 16) + 16 q
-    const int W = p.rpad >> 5;
-    uint32_t uw[QMAX][R];
-#pragma unroll
-    for (int q = 0; q < QMAX; ++q)
-#pragma unroll
-        for (int rr = 0; rr < R; ++rr) {
-            uw[q][rr] = 0u;
-            if (has_z && 16 * q < W && rr < nrows) {
-                int w = (lane & 15) + 16 * q;
-                w = w < W ? w : W - 1;
-                uw[q][rr] = p.u[(int64_t)w * p.N + row0 + rr];
-            }
-        }
     __builtin_amdgcn_sched_barrier(0);
 
     // 4. decode the activation into LDS: [m][block][8 f16 pairs], exact values;
@@ -374,16 +432,6 @@ __global__ void __launch_bounds__(kGemvThreads) fused_gemv_kernel(GemvParams p) 
             uint4 *dst = reinterpret_cast<uint4 *>(s_act + (size_t)ai * 8);
             dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
             dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
-        }
-    }
-    if (ZMODE == 2) {
-#pragma unroll
-        for (int j = 0; j < ZP; ++j) {
-            const int idx = threadIdx.x + kGemvThreads * j;
-            if (idx < nz) {
-                const int m = idx / p.r, i = idx - m * p.r;
-                s_z[m * p.rpad + i] = zpre[j];
-            }
         }
     }
     __syncthreads();
@@ -417,36 +465,36 @@ __global__ void __launch_bounds__(kGemvThreads) fused_gemv_kernel(GemvParams p) 
         if (threadIdx.x == 0 && blockIdx.x > 0) st_u32(p.seen + blockIdx.x, ep + 1u);
     }
 
-    // 6. the rows of R
-    u32x2_t codes[R][KBL];
-    uint32_t sc[R][KBL];
-#pragma unroll
-    for (int rr = 0; rr < R; ++rr) {
-        if (rr >= nrows) continue;
-        const int n = row0 + rr;
-#pragma unroll
-        for (int t = 0; t < KBL; ++t) {
-            // blocks past the row end load a valid block; they are zeroed at use
-            const int b = lane + 64 * t, bc = b < KB ? b : KB - 1;
-            codes[rr][t] = __builtin_nontemporal_load(
-                reinterpret_cast<const u32x2_t *>(p.w_codes + (int64_t)n * KH + bc * 8));
-            sc[rr][t] = __builtin_nontemporal_load(p.w_scales + (int64_t)n * KB + bc);
-        }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-
-    // 7. two launches: the correction while the rows stream in
+    // 6-8. the rows of R, the FP4 product of every row, times g, onto the
+    // per-lane sums, then the correction (two launches).
+    // The body is specialised on the wave's row count (a scalar), so every
+    // load it issues is one it needs and the wait before each row's
+    // arithmetic counts exactly the loads issued after that row: no row
+    // waits for a later one.  No barrier inside.
     float part[R][MM];
 #pragma unroll
     for (int rr = 0; rr < R; ++rr)
 #pragma unroll
         for (int m = 0; m < MM; ++m) part[rr][m] = 0.0f;
-    if (ZMODE == 2) add_correction<MM, R, QMAX>(p, s_z, uw, part);
-
-    // 8. the FP4 product of every row, times g, onto the per-lane sums
+    auto rows = [&](auto nr_c) {
+        constexpr int NR = decltype(nr_c)::value;
+        u32x2_t codes[NR][KBL];
+        uint32_t sc[NR][KBL];
 #pragma unroll
-    for (int rr = 0; rr < R; ++rr) {
-        if (rr < nrows) {
+        for (int rr = 0; rr < NR; ++rr) {
+            const int n = row0 + rr;
+#pragma unroll
+            for (int t = 0; t < KBL; ++t) {
+                // blocks past the row end load a valid block; they are zeroed at use
+                const int b = lane + 64 * t, bc = b < KB ? b : KB - 1;
+                codes[rr][t] = __builtin_nontemporal_load(
+                    reinterpret_cast<const u32x2_t *>(p.w_codes + (int64_t)n * KH + bc * 8));
+                sc[rr][t] = __builtin_nontemporal_load(p.w_scales + (int64_t)n * KB + bc);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int rr = 0; rr < NR; ++rr) {
             float gacc[MM];
 #pragma unroll
             for (int m = 0; m < MM; ++m) gacc[m] = 0.0f;
@@ -472,7 +520,20 @@ __global__ void __launch_bounds__(kGemvThreads) fused_gemv_kernel(GemvParams p) 
             }
 #pragma unroll
             for (int m = 0; m < MM; ++m) part[rr][m] = __builtin_fmaf(p.g, gacc[m], part[rr][m]);
+            // keep each row's decoding next to its products (hoisted, it
+            // would wait for every row's loads)
+            __builtin_amdgcn_sched_barrier(0);
         }
+        // the correction last: U's scattered words come back while the rows
+        // are consumed, so no row waits for them
+        if constexpr (ZMODE == 2) add_correction_ops<MM, NR, R, QMAX>(p, ul, zo, part);
+    };
+    switch (nrows) {
+        case 1: rows(std::integral_constant<int, 1>{}); break;
+        case 2: if constexpr (R >= 2) rows(std::integral_constant<int, 2>{}); break;
+        case 3: if constexpr (R >= 3) rows(std::integral_constant<int, 3>{}); break;
+        case 4: if constexpr (R >= 4) rows(std::integral_constant<int, 4>{}); break;
+        default: break;   // no rows: nothing is stored
     }
 
     // 9. one launch: z of this call into LDS (every thread requests its z
@@ -503,12 +564,12 @@ __global__ void __launch_bounds__(kGemvThreads) fused_gemv_kernel(GemvParams p) 
                     a = ld_tagged(src);
                     ++spins;
                 }
-                s_z[m * p.rpad + i] = (uint32_t)(a >> 32) == tag ? __uint_as_float((uint32_t)a)
+                s_z[zslot(p, m, i)] = (uint32_t)(a >> 32) == tag ? __uint_as_float((uint32_t)a)
                                                                  : z_local(p, m, i);
             }
         }
         __syncthreads();
-        add_correction<MM, R, QMAX>(p, s_z, uw, part);
+        add_correction<MM, R, R, QMAX>(p, s_z, ul, part);
     }
 
     // 10. one reduction per row and m, then the bf16 (or fp32) store
@@ -534,9 +595,24 @@ __global__ void __launch_bounds__(kGemvThreads) fused_gemv_kernel(GemvParams p) 
     }
 }
 
+// z[m][i] into its correction operand slot: index i = 32 w + 16 h + 4 j + g
+// (w = 16 q + c) is half h of the high and low dwords j of lane c + 16 g in
+// round q.  High part: the top 16 bits of z; low part: the top 16 bits of
+// the remainder (z minus the high part), as the correction has always split z.
+__device__ __forceinline__ void put_zop(const GemvParams &p, int m, int i, float z) {
+    const uint32_t hi = __float_as_uint(z) & 0xFFFF0000u;
+    const uint32_t lo = __float_as_uint(z - __uint_as_float(hi));
+    const int w = i >> 5, h = (i >> 4) & 1, j = (i >> 2) & 3, g = i & 3;
+    const int lane = (w & 15) + 16 * g;
+    const int64_t dw = (((int64_t)m * zop_rounds(p.r) + (w >> 4)) * 64 + lane) * 8 + 2 * j;
+    uint16_t *half = reinterpret_cast<uint16_t *>(p.zop_out + dw) + h;
+    half[0] = (uint16_t)(hi >> 16);
+    half[2] = (uint16_t)(lo >> 16);
+}
+
 // z of the two-launch schedule: one workgroup per z item (kZI indices i over
-// all of K), plain fp32 stores; the product kernel that follows on the same
-// stream reads z complete.
+// all of K), plain fp32 stores (and the product's operand halves); the
+// product kernel that follows on the same stream reads z complete.
 template <int MM>
 __global__ void __launch_bounds__(kGemvThreads) z_kernel(GemvParams p) {
     __shared__ float s_red[8];
@@ -568,14 +644,23 @@ __global__ void __launch_bounds__(kGemvThreads) z_kernel(GemvParams p) {
 #pragma unroll
         for (int m = 0; m < MM; ++m) {
             const int ii = i0 + i;
-            if ((int)threadIdx.x == 64 * i + m && ii < p.r)
-                p.zf_out[(int64_t)m * p.rpad + ii] = zs[i][m] * bf16_to_f32(zin.al[i]);
+            if ((int)threadIdx.x == 64 * i + m && ii < p.r) {
+                const float zv = zs[i][m] * bf16_to_f32(zin.al[i]);
+                p.zf_out[(int64_t)m * p.rpad + ii] = zv;
+                if (p.zop_out) put_zop(p, m, ii, zv);
+            }
         }
+    // the operand slots of the padding indices r .. 512 ceil(rpad / 512) hold 0
+    if (p.zop_out && blockIdx.x == 0) {
+        const int span = zop_rounds(p.r) * 512 - p.r;
+        for (int t = threadIdx.x; t < MM * span; t += kGemvThreads)
+            put_zop(p, t / span, p.r + t % span, 0.0f);
+    }
 }
 
 namespace {
 size_t gemv_lds_bytes(int M, int K, int rpad) {
-    return (size_t)M * (size_t)(K / 16) * 32 + (size_t)M * (size_t)rpad * 4;
+    return (size_t)M * (size_t)(K / 16) * 32 + (size_t)M * (size_t)(rpad + rpad / 16) * 4;
 }
 
 template <int MM, int KBL, int ZMODE>
@@ -687,6 +772,10 @@ hipError_t launch_gemv(const GemmArgs &a, bool two_launch, hipStream_t stream) {
         p.zt = reinterpret_cast<uint64_t *>(ws + ws_zt_offset());
         p.zf_out = reinterpret_cast<float *>(ws + ws_zf_offset(a.M, a.r));
         p.zf = p.zf_out;
+        if (two_launch) {
+            p.zop_out = reinterpret_cast<uint32_t *>(ws + ws_zop_offset(a.M, a.r));
+            p.zop = p.zop_out;
+        }
         zmode = two_launch ? 2 : 1;
     } else {
         // no correction: the kernel still reads one epoch word and one U word
