@@ -378,35 +378,38 @@ __global__ void __launch_bounds__(kGemvThreads) fused_gemv_kernel(GemvParams p) 
     if (z_wg) z_prefetch<MM>(p, blockIdx.x, zin);
     const int nz = MM * p.r;
     // two launches: this lane's correction operands (z split into bf16 high
-    // and low parts, two dwords per j) for each round of 16 words, rounds
-    // past the last clamped to it; no wait until the correction
+    // and low parts, two dwords per j) for each round of 16 words; a round
+    // past the last reads zeros through the offset kOob (no memory access,
+    // exact wait counts); no wait until the correction
     u32x4_t zo[QMAX][MM][2];
     if constexpr (ZMODE == 2) {
+        const int QW = zop_rounds(p.r);
+        const __amdgpu_buffer_rsrc_t r_zo = buffer_of(p.zop, (int64_t)MM * QW * 2048);
 #pragma unroll
         for (int q = 0; q < QMAX; ++q)
 #pragma unroll
             for (int m = 0; m < MM; ++m) {
-                const int qc = min(q, zop_rounds(p.r) - 1);
-                const u32x4_t *src = reinterpret_cast<const u32x4_t *>(
-                    p.zop + (((int64_t)m * zop_rounds(p.r) + qc) * 64 + lane) * 8);
-                zo[q][m][0] = src[0];
-                zo[q][m][1] = src[1];
+                const int off = ((m * QW + q) * 64 + lane) * 32;
+                zo[q][m][0] = load16(r_zo, opaque(q < QW ? off : kOob));
+                zo[q][m][1] = load16(r_zo, opaque(q < QW ? off + 16 : kOob));
             }
     }
     // 3. U's words for these rows, one load per round of 16 words: lane
     // 16 rr + c fetches word c + 16 q of row rr (clamped to a row and word
-    // that exist; such values are never used).  No branch: the waits below
-    // for the activation and z then count these loads exactly and leave them
-    // in flight; the correction shuffles the words to their lanes.
+    // that exist; such values are never used; a round past the last reads
+    // zeros through kOob).  No branch: the waits below for the activation
+    // and z then count these loads exactly and leave them in flight; the
+    // correction shuffles the words to their lanes.
     uint32_t ul[QMAX];
 #pragma unroll
     for (int q = 0; q < QMAX; ++q) {
         ul[q] = 0u;
         if constexpr (has_z) {
             const int W = p.rpad >> 5;
+            const __amdgpu_buffer_rsrc_t r_u = buffer_of(p.u, (int64_t)W * p.N * 4);
             const int w = min((lane & 15) + 16 * q, W - 1);
             const int n = min(row0 + min(lane >> 4, max(nrows - 1, 0)), p.N - 1);
-            ul[q] = p.u[(int64_t)w * p.N + n];
+            ul[q] = __builtin_amdgcn_raw_buffer_load_b32(r_u, opaque(16 * q < W ? (w * p.N + n) * 4 : kOob), 0, 0);
         }
     }
     __builtin_amdgcn_sched_barrier(0);
