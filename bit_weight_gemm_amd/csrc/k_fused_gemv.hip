@@ -619,18 +619,23 @@ __device__ __forceinline__ void put_zop(const GemvParams &p, int m, int i, float
 template <int MM>
 __global__ void __launch_bounds__(kGemvThreads) z_kernel(GemvParams p) {
     __shared__ float s_red[8];
-    // the activation's FP4 quantisation rides along (read by the product)
-    if (p.qa_codes) {
+    // The activation's FP4 quantisation rides along (read by the product) in
+    // the first zq workgroups, one block per thread, dispatched first, so no
+    // z item waits for it.
+    const int zq = (int)gridDim.x - p.z_items;
+    if ((int)blockIdx.x < zq) {
         const int64_t nb = (int64_t)MM * (p.K >> 4);
         for (int64_t blk = (int64_t)blockIdx.x * kGemvThreads + threadIdx.x; blk < nb;
-             blk += (int64_t)gridDim.x * kGemvThreads)
+             blk += (int64_t)zq * kGemvThreads)
             quant_act_block(p.x, blk, p.qa_codes, p.qa_scales);
+        return;
     }
-    // Workgroups are dispatched to the 8 XCDs in turn (b % 8).  The items of
-    // one V word (32 / kZI consecutive items) are mapped to workgroups of one
-    // XCD, so that word's column of V is fetched into one L2 only.  The map
-    // is a permutation of [0, z_items) whatever the dispatch does.
-    const int b = blockIdx.x, G = p.z_items, x = b & 7, q = G >> 3, rem = G & 7;
+    // Workgroups are dispatched to the 8 XCDs in turn.  The items of one V
+    // word (32 / kZI consecutive items) are mapped to workgroups whose index
+    // b (counted after the quantisation workgroups) agrees mod 8, that is to
+    // one XCD, so that word's column of V is fetched into one L2 only.  The
+    // map is a permutation of [0, z_items) whatever the dispatch does.
+    const int b = blockIdx.x - zq, G = p.z_items, x = b & 7, q = G >> 3, rem = G & 7;
     const int item = x * q + (x < rem ? x : rem) + (b >> 3);
     ZInputs<MM> zin;
     z_prefetch<MM>(p, item, zin);
@@ -654,7 +659,7 @@ __global__ void __launch_bounds__(kGemvThreads) z_kernel(GemvParams p) {
             }
         }
     // the operand slots of the padding indices r .. 512 ceil(rpad / 512) hold 0
-    if (p.zop_out && blockIdx.x == 0) {
+    if (p.zop_out && b == 0) {
         const int span = zop_rounds(p.r) * 512 - p.r;
         for (int t = threadIdx.x; t < MM * span; t += kGemvThreads)
             put_zop(p, t / span, p.r + t % span, 0.0f);
@@ -789,10 +794,12 @@ hipError_t launch_gemv(const GemmArgs &a, bool two_launch, hipStream_t stream) {
     static const uint32_t spin = spin_limit_default();
     p.spin_limit = spin;
     if (zmode == 2) {
+        // the quantisation workgroups (if any), then the z items
+        const int zq = a.qa_codes ? (a.M * (a.K / 16) + kGemvThreads - 1) / kGemvThreads : 0;
         if (a.M == 1)
-            hipLaunchKernelGGL(z_kernel<1>, dim3(p.z_items), dim3(kGemvThreads), 0, stream, p);
+            hipLaunchKernelGGL(z_kernel<1>, dim3(p.z_items + zq), dim3(kGemvThreads), 0, stream, p);
         else
-            hipLaunchKernelGGL(z_kernel<2>, dim3(p.z_items), dim3(kGemvThreads), 0, stream, p);
+            hipLaunchKernelGGL(z_kernel<2>, dim3(p.z_items + zq), dim3(kGemvThreads), 0, stream, p);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
