@@ -377,11 +377,16 @@ __global__ void __launch_bounds__(kGemvThreads) fused_gemv_kernel(GemvParams p) 
     ZInputs<MM> zin;
     if (z_wg) z_prefetch<MM>(p, blockIdx.x, zin);
     const int nz = MM * p.r;
-    // two launches: this lane's correction operands (z split into bf16 high
+    // Correction inputs, requested once the activation is decoded, just ahead
+    // of the rows of R (they are needed only at the end; requested with the
+    // activation, they would hold it up).
+    // Two launches: this lane's correction operands (z split into bf16 high
     // and low parts, two dwords per j) for each round of 16 words; a round
     // past the last reads zeros through the offset kOob (no memory access,
     // exact wait counts); no wait until the correction
     u32x4_t zo[QMAX][MM][2];
+    uint32_t ul[QMAX];
+    auto request_correction_inputs = [&]() {
     if constexpr (ZMODE == 2) {
         const int QW = zop_rounds(p.r);
         const __amdgpu_buffer_rsrc_t r_zo = buffer_of(p.zop, (int64_t)MM * QW * 2048);
@@ -394,13 +399,11 @@ __global__ void __launch_bounds__(kGemvThreads) fused_gemv_kernel(GemvParams p) 
                 zo[q][m][1] = load16(r_zo, opaque(q < QW ? off + 16 : kOob));
             }
     }
-    // 3. U's words for these rows, one load per round of 16 words: lane
+    // U's words for these rows, one load per round of 16 words: lane
     // 16 rr + c fetches word c + 16 q of row rr (clamped to a row and word
     // that exist; such values are never used; a round past the last reads
-    // zeros through kOob).  No branch: the waits below for the activation
-    // and z then count these loads exactly and leave them in flight; the
-    // correction shuffles the words to their lanes.
-    uint32_t ul[QMAX];
+    // zeros through kOob).  No branch, so the waits for the rows count these
+    // loads exactly; the correction shuffles the words to their lanes.
 #pragma unroll
     for (int q = 0; q < QMAX; ++q) {
         ul[q] = 0u;
@@ -412,7 +415,7 @@ __global__ void __launch_bounds__(kGemvThreads) fused_gemv_kernel(GemvParams p) 
             ul[q] = __builtin_amdgcn_raw_buffer_load_b32(r_u, opaque(16 * q < W ? (w * p.N + n) * 4 : kOob), 0, 0);
         }
     }
-    __builtin_amdgcn_sched_barrier(0);
+    };
 
     // 4. decode the activation into LDS: [m][block][8 f16 pairs], exact values;
     // z (two launches) into its own LDS area
@@ -531,6 +534,8 @@ __global__ void __launch_bounds__(kGemvThreads) fused_gemv_kernel(GemvParams p) 
         // are consumed, so no row waits for them
         if constexpr (ZMODE == 2) add_correction_ops<MM, NR, R, QMAX>(p, ul, zo, part);
     };
+    request_correction_inputs();
+    __builtin_amdgcn_sched_barrier(0);
     switch (nrows) {
         case 1: rows(std::integral_constant<int, 1>{}); break;
         case 2: if constexpr (R >= 2) rows(std::integral_constant<int, 2>{}); break;
