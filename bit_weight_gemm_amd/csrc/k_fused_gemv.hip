@@ -166,7 +166,7 @@ __device__ __forceinline__ void z_prefetch(const GemvParams &p, int item, ZInput
 
 // The sign-by-x products of one z item, summed per thread.
 template <int MM>
-__device__ void z_accumulate(const GemvParams &p, int item, ZInputs<MM> &in, float (&acc)[kZI][MM]) {
+__device__ __forceinline__ void z_accumulate(const GemvParams &p, int item, ZInputs<MM> &in, float (&acc)[kZI][MM]) {
     const int i0 = item * kZI, o = i0 & 31;
     const int s = o & 15;                 // bit offset inside the 16-bit half
     const bool high = o >= 16;
@@ -198,7 +198,7 @@ __device__ void z_accumulate(const GemvParams &p, int item, ZInputs<MM> &in, flo
 // epoch + 1: all sums first, then the kZI * MM stores from as many threads,
 // with no wait behind them (a store would otherwise hold up the next wait).
 template <int MM>
-__device__ void z_publish(const GemvParams &p, int item, const ZInputs<MM> &in,
+__device__ __forceinline__ void z_publish(const GemvParams &p, int item, const ZInputs<MM> &in,
                           float (&acc)[kZI][MM], uint32_t epoch, float *red) {
     const int i0 = item * kZI;
     float zs[kZI][MM];
@@ -215,6 +215,64 @@ __device__ void z_publish(const GemvParams &p, int item, const ZInputs<MM> &in,
             if ((int)threadIdx.x == 64 * i + m && ii < p.r)
                 st_tagged(p.zt + (int64_t)m * p.rpad + ii, zs[i][m] * bf16_to_f32(in.al[i]), tag);
         }
+}
+
+// The same item with no barrier (one launch, inside a wave's row section):
+// only the first round of inputs (K <= 2 kGemvThreads kZU), each wave's sums
+// go to its LDS slot, then a workgroup-scope counter; the wave that arrives
+// last adds the slots in wave order (so the result does not depend on the
+// order of arrival), publishes, and resets the counter.
+template <int MM>
+__device__ __forceinline__ void z_item_waves(const GemvParams &p, int item, const ZInputs<MM> &in, uint32_t epoch,
+                             float (*slots)[kZI * MM], uint32_t *cnt) {
+    const int i0 = item * kZI, o = i0 & 31;
+    const int s = o & 15;
+    const bool high = o >= 16;
+    float acc[kZI][MM];
+#pragma unroll
+    for (int i = 0; i < kZI; ++i)
+#pragma unroll
+        for (int m = 0; m < MM; ++m) acc[i][m] = 0.0f;
+    const int KP = p.K / 2;
+#pragma unroll
+    for (int u = 0; u < kZU; ++u) {
+        const bool valid = (int)threadIdx.x + kGemvThreads * u < KP;
+        const uint32_t t = high ? __builtin_amdgcn_perm(in.vv[u].y, in.vv[u].x, 0x07060302u)
+                                : __builtin_amdgcn_perm(in.vv[u].y, in.vv[u].x, 0x05040100u);
+#pragma unroll
+        for (int i = 0; i < kZI; ++i) {
+            const uint32_t sg = signs_bf16x2(t, s + i);
+#pragma unroll
+            for (int m = 0; m < MM; ++m) acc[i][m] = dot2_bf16(sg, valid ? in.xp[u][m] : 0u, acc[i][m]);
+        }
+    }
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    float v[kZI * MM];
+#pragma unroll
+    for (int i = 0; i < kZI; ++i)
+#pragma unroll
+        for (int m = 0; m < MM; ++m) v[i * MM + m] = wave_sum_dpp(acc[i][m]);
+    uint32_t old = 0;
+    if (lane == 0) {
+#pragma unroll
+        for (int j = 0; j < kZI * MM; ++j) slots[wave][j] = v[j];
+        old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    old = __builtin_amdgcn_readfirstlane(old);
+    if (old != (uint32_t)(kGemvThreads / 64 - 1)) return;
+    if (lane < kZI * MM) {
+        float sum = 0.0f;
+#pragma unroll
+        for (int q = 0; q < kGemvThreads / 64; ++q) sum += slots[q][lane];
+        const int i = lane / MM, m = lane - i * MM, ii = i0 + i;
+        // alpha of index i, selected with constant indices (a register array
+        // indexed by a lane-dependent value would go to scratch memory)
+        uint32_t al = in.al[0];
+#pragma unroll
+        for (int c = 1; c < kZI; ++c) al = i == c ? in.al[c] : al;
+        if (ii < p.r) st_tagged(p.zt + (int64_t)m * p.rpad + ii, sum * bf16_to_f32(al), epoch + 1u);
+    }
+    if (lane == 0) *cnt = 0u;
 }
 
 // Fallback: z[m][i] for one index, computed by one thread alone (slow; used
@@ -339,6 +397,8 @@ __global__ void __launch_bounds__(kGemvThreads) fused_gemv_kernel(GemvParams p) 
     constexpr int AMAX = (MM * KBL * 64 + kGemvThreads - 1) / kGemvThreads;  // blocks per thread
     __shared__ float s_red[8];
     __shared__ uint32_t s_bcast;
+    __shared__ float s_zslots[kGemvThreads / 64][kZI * MM];   // one launch: per-wave z item sums
+    __shared__ uint32_t s_zcnt;
     extern __shared__ uint32_t s_dyn[];   // activation f16 pairs [MM][KB][8], then z [MM][rpad]
 
     // the wave index as a scalar, so that the row count below is one too
@@ -347,8 +407,11 @@ __global__ void __launch_bounds__(kGemvThreads) fused_gemv_kernel(GemvParams p) 
     uint32_t *s_act = s_dyn;
     float *s_z = reinterpret_cast<float *>(s_dyn + (size_t)MM * KB * 8);
 
-    // the call's epoch (one launch): a plain device-scope load by every thread
-    const uint32_t ep = ZMODE == 1 ? ld_u32(p.epoch) : 0u;
+    // the call's epoch (one launch): a device-scope load by every thread,
+    // requested with the correction inputs (first, it would hold up the
+    // activation: the word was last written on another XCD)
+    uint32_t ep = 0u;
+    if (ZMODE == 1 && threadIdx.x == 0) s_zcnt = 0u;   // ordered by the activation's barrier
 
     // rows of this workgroup, spread over its 8 waves (the first get one more)
     const int wg_row0 = blockIdx.x * p.rows_per_wg;
@@ -374,8 +437,12 @@ __global__ void __launch_bounds__(kGemvThreads) fused_gemv_kernel(GemvParams p) 
     }
     // 2. a z item's inputs (one launch) or the finished z (two launches)
     const bool z_wg = ZMODE == 1 && (int)blockIdx.x < p.z_items;
+    // the z item published early (inside the row section, no barrier) when
+    // its inputs fit beside the rows' registers: KBL MM <= 8, which also
+    // bounds K by 8192, one round of inputs; otherwise after the rows
+    constexpr bool z_early = KBL * MM <= 8;
+    static_assert(!z_early || 64 * KBL * 16 <= 2 * kGemvThreads * kZU, "one round of z inputs");
     ZInputs<MM> zin;
-    if (z_wg) z_prefetch<MM>(p, blockIdx.x, zin);
     const int nz = MM * p.r;
     // Correction inputs, requested once the activation is decoded, just ahead
     // of the rows of R (they are needed only at the end; requested with the
@@ -387,6 +454,13 @@ __global__ void __launch_bounds__(kGemvThreads) fused_gemv_kernel(GemvParams p) 
     u32x4_t zo[QMAX][MM][2];
     uint32_t ul[QMAX];
     auto request_correction_inputs = [&]() {
+    // one launch: the epoch and this workgroup's z item's inputs
+    // (unconditionally, the index clamped, so the waits for the rows stay
+    // exact)
+    if constexpr (ZMODE == 1) {
+        ep = ld_u32(p.epoch);
+        if constexpr (z_early) z_prefetch<MM>(p, min((int)blockIdx.x, p.z_items - 1), zin);
+    }
     if constexpr (ZMODE == 2) {
         const int QW = zop_rounds(p.r);
         const __amdgpu_buffer_rsrc_t r_zo = buffer_of(p.zop, (int64_t)MM * QW * 2048);
@@ -454,23 +528,6 @@ __global__ void __launch_bounds__(kGemvThreads) fused_gemv_kernel(GemvParams p) 
         }
     }
 
-    // 5. one launch: a z item is computed and published before the rows of R
-    // are requested, so that z is out long before any workgroup needs it;
-    // every other workgroup records that it has read the epoch
-    if (ZMODE == 1) {
-        if (z_wg) {
-            float zacc[kZI][MM];
-            z_accumulate<MM>(p, blockIdx.x, zin, zacc);
-            z_publish<MM>(p, blockIdx.x, zin, zacc, ep, s_red);
-            for (int it = blockIdx.x + gridDim.x; it < p.z_items; it += gridDim.x) {
-                z_prefetch<MM>(p, it, zin);
-                z_accumulate<MM>(p, it, zin, zacc);
-                z_publish<MM>(p, it, zin, zacc, ep, s_red);
-            }
-        }
-        if (threadIdx.x == 0 && blockIdx.x > 0) st_u32(p.seen + blockIdx.x, ep + 1u);
-    }
-
     // 6-8. the rows of R, the FP4 product of every row, times g, onto the
     // per-lane sums, then the correction (two launches).
     // The body is specialised on the wave's row count (a scalar), so every
@@ -499,6 +556,10 @@ __global__ void __launch_bounds__(kGemvThreads) fused_gemv_kernel(GemvParams p) 
             }
         }
         __builtin_amdgcn_sched_barrier(0);
+        // one launch: the z item, published while the rows stream in
+        if constexpr (ZMODE == 1 && z_early) {
+            if (z_wg) z_item_waves<MM>(p, blockIdx.x, zin, ep, s_zslots, &s_zcnt);
+        }
 #pragma unroll
         for (int rr = 0; rr < NR; ++rr) {
             float gacc[MM];
@@ -541,7 +602,32 @@ __global__ void __launch_bounds__(kGemvThreads) fused_gemv_kernel(GemvParams p) 
         case 2: if constexpr (R >= 2) rows(std::integral_constant<int, 2>{}); break;
         case 3: if constexpr (R >= 3) rows(std::integral_constant<int, 3>{}); break;
         case 4: if constexpr (R >= 4) rows(std::integral_constant<int, 4>{}); break;
-        default: break;   // no rows: nothing is stored
+        default:   // no rows: nothing is stored
+            if constexpr (ZMODE == 1 && z_early) {
+                if (z_wg) z_item_waves<MM>(p, blockIdx.x, zin, ep, s_zslots, &s_zcnt);
+            }
+            break;
+    }
+
+    // one launch: the z item, computed and published once the rows are done
+    // (its inputs came in ahead of them); computed before the rows, it held
+    // up every workgroup's stream.  Every other workgroup then records that
+    // it has read the epoch.
+    if (ZMODE == 1) {
+        if (z_wg) {
+            float zacc[kZI][MM];
+            if constexpr (!z_early) {
+                z_prefetch<MM>(p, blockIdx.x, zin);
+                z_accumulate<MM>(p, blockIdx.x, zin, zacc);
+                z_publish<MM>(p, blockIdx.x, zin, zacc, ep, s_red);
+            }
+            for (int it = blockIdx.x + gridDim.x; it < p.z_items; it += gridDim.x) {
+                z_prefetch<MM>(p, it, zin);
+                z_accumulate<MM>(p, it, zin, zacc);
+                z_publish<MM>(p, it, zin, zacc, ep, s_red);
+            }
+        }
+        if (threadIdx.x == 0 && blockIdx.x > 0) st_u32(p.seen + blockIdx.x, ep + 1u);
     }
 
     // 9. one launch: z of this call into LDS (every thread requests its z
