@@ -65,7 +65,8 @@ constexpr int kChunkK = 128;
 constexpr int kGridTarget = 256;        // one workgroup per CU
 constexpr size_t kLdsLimit = 160 * 1024 - 1024;
 
-constexpr int kSumBatch = 8;            // K-slice partials loaded at once by a last arrival
+constexpr int kSumBatch = 8;            // K-slice partials of y loaded at once by the epilogue
+constexpr int kZSplitMinSlices = 12;    // z slices from which the exchange gets a launch of its own
 
 // Per batch-tile-height tuning (MB m-blocks of 16 rows):
 //   kCpw       128-k chunks per wave: the activation tile takes 16 kCpw MB
@@ -107,6 +108,7 @@ struct MfmaParams {
     uint8_t *qa_codes;          // if set: the z kernel also quantises x (codes, scales)
     uint8_t *qa_scales;
     int rpad;
+    int zsplit;                 // 1: the z launch stores its slice partials only, a reduce launch finishes
     // product kernel
     int S, cps, chunks, RB, Gs;
     float *ypart;               // [S][RB][MB][64 lanes][4] (D layout)
@@ -162,6 +164,48 @@ __device__ __forceinline__ float get(const float *p) {
 __device__ __forceinline__ void stores_done() { __builtin_amdgcn_s_waitcnt(0); }
 __device__ __forceinline__ uint32_t arrive(uint32_t *cnt) {
     return __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The slices' sum for word w times alpha_i / g as bf16 high + low parts into
+// the correction operand (and plain fp32 z into zf when asked).  Thread
+// (mb, l, j) sums one value; lanes j and j + 4 of a group of 8 threads form
+// the (index, index + 16) pair of dword j & 3.  COHERENT: the partials were
+// written in the same launch (relaxed agent-scope loads); else after a launch
+// boundary (plain loads).
+constexpr int kZSumBatch = 16;          // slice partials loaded at once
+template <int MB, bool COHERENT>
+__device__ __forceinline__ void z_finish(const MfmaParams &p, int w) {
+    const float ginv = 1.0f / p.g;
+    for (int idx = threadIdx.x; idx < MB * 64 * 8; idx += kZThreads) {
+        const int j = idx & 7, l = (idx >> 3) & 63, mb = idx >> 9;
+        const int m = 16 * mb + (l & 15), q = l >> 4;
+        float sum = 0.0f;
+        for (int t0 = 0; t0 < p.zs; t0 += kZSumBatch) {
+            float part_v[kZSumBatch];
+#pragma unroll
+            for (int tt = 0; tt < kZSumBatch; ++tt) {
+                const int t = min(t0 + tt, p.zs - 1);
+                const float *src = p.zpart + ((int64_t)t * p.W + w) * MB * 64 * 8 + idx;
+                part_v[tt] = COHERENT ? get(src) : *src;
+            }
+#pragma unroll
+            for (int tt = 0; tt < kZSumBatch; ++tt)
+                if (t0 + tt < p.zs) sum += part_v[tt];
+        }
+        const int i = 32 * w + 4 * q + (j & 3) + 16 * (j >> 2);
+        const float al = bf16_to_f32(p.alpha[i < p.r ? i : p.r - 1]);
+        const float zz = (i < p.r && m < p.M) ? sum * al * ginv : 0.0f;
+        if (p.zf && i < p.r && m < p.M) p.zf[(int64_t)m * p.rpad + i] = sum * al;
+        const uint32_t zh = f32_to_bf16_rne(zz);
+        const uint32_t zl = f32_to_bf16_rne(zz - bf16_to_f32(zh));
+        // pair with the partner thread (j ^ 4) of the same 8-thread group
+        const uint32_t oh = __shfl_xor(zh, 4, 64), ol = __shfl_xor(zl, 4, 64);
+        if (j < 4) {
+            uint16_t *dst = reinterpret_cast<uint16_t *>(p.zA + ((((int64_t)w * MB + mb) * 2) * 64 + l) * 4 + j);
+            reinterpret_cast<uint32_t *>(dst)[0] = zh | (oh << 16);
+            reinterpret_cast<uint32_t *>(dst)[64 * 4] = zl | (ol << 16);
+        }
+    }
 }
 
 // =====================================================================
@@ -254,8 +298,17 @@ __global__ void __launch_bounds__(kZThreads) mfma_z_kernel(MfmaParams p) {
         for (int e = 0; e < 4; ++e) s_t[16 * mb + 4 * (l >> 4) + e][16 * ib + (l & 15)] = v[e];
     }
     __syncthreads();
-    // this slice's partial in the operand layout: thread (mb, l, j)
+    // this slice's partial in the operand layout: thread (mb, l, j); with a
+    // reduce launch to follow, plain stores and nothing more
     float *part = p.zpart + ((int64_t)s * p.W + w) * MB * 64 * 8;
+    if (p.zsplit) {
+        for (int idx = threadIdx.x; idx < MB * 64 * 8; idx += kZThreads) {
+            const int j = idx & 7, l = (idx >> 3) & 63, mb = idx >> 9;
+            const int m = 16 * mb + (l & 15), q = l >> 4;
+            part[idx] = s_t[m][4 * q + (j & 3) + 16 * (j >> 2)];
+        }
+        return;
+    }
     for (int idx = threadIdx.x; idx < MB * 64 * 8; idx += kZThreads) {
         const int j = idx & 7, l = (idx >> 3) & 63, mb = idx >> 9;
         const int m = 16 * mb + (l & 15), q = l >> 4;
@@ -266,40 +319,14 @@ __global__ void __launch_bounds__(kZThreads) mfma_z_kernel(MfmaParams p) {
     if (threadIdx.x == 0) s_last = arrive(p.zcnt + w) == (uint32_t)(p.zs - 1);
     __syncthreads();
     if (!s_last) return;
-    // Last arrival for word w: the slices' sum times alpha_i / g as bf16 high
-    // + low parts.  Thread (mb, l, j) sums one value; lanes j and j + 4 of a
-    // group of 8 threads form the (index, index + 16) pair of dword j & 3.
-    const float ginv = 1.0f / p.g;
-    for (int idx = threadIdx.x; idx < MB * 64 * 8; idx += kZThreads) {
-        const int j = idx & 7, l = (idx >> 3) & 63, mb = idx >> 9;
-        const int m = 16 * mb + (l & 15), q = l >> 4;
-        float sum = 0.0f;
-        for (int t0 = 0; t0 < p.zs; t0 += kSumBatch) {
-            float part_v[kSumBatch];
-#pragma unroll
-            for (int tt = 0; tt < kSumBatch; ++tt) {
-                const int t = min(t0 + tt, p.zs - 1);
-                part_v[tt] = get(p.zpart + ((int64_t)t * p.W + w) * MB * 64 * 8 + idx);
-            }
-#pragma unroll
-            for (int tt = 0; tt < kSumBatch; ++tt)
-                if (t0 + tt < p.zs) sum += part_v[tt];
-        }
-        const int i = 32 * w + 4 * q + (j & 3) + 16 * (j >> 2);
-        const float al = bf16_to_f32(p.alpha[i < p.r ? i : p.r - 1]);
-        const float zz = (i < p.r && m < p.M) ? sum * al * ginv : 0.0f;
-        if (p.zf && i < p.r && m < p.M) p.zf[(int64_t)m * p.rpad + i] = sum * al;
-        const uint32_t zh = f32_to_bf16_rne(zz);
-        const uint32_t zl = f32_to_bf16_rne(zz - bf16_to_f32(zh));
-        // pair with the partner thread (j ^ 4) of the same 8-thread group
-        const uint32_t oh = __shfl_xor(zh, 4, 64), ol = __shfl_xor(zl, 4, 64);
-        if (j < 4) {
-            uint16_t *dst = reinterpret_cast<uint16_t *>(p.zA + ((((int64_t)w * MB + mb) * 2) * 64 + l) * 4 + j);
-            reinterpret_cast<uint32_t *>(dst)[0] = zh | (oh << 16);
-            reinterpret_cast<uint32_t *>(dst)[64 * 4] = zl | (ol << 16);
-        }
-    }
+    z_finish<MB, true>(p, w);
     if (threadIdx.x == 0) p.zcnt[w] = 0u;   // ready for the next call on this workspace
+}
+
+// The reduce launch: workgroup w finishes word w from the slice partials.
+template <int MB>
+__global__ void __launch_bounds__(kZThreads) mfma_zreduce_kernel(MfmaParams p) {
+    z_finish<MB, false>(p, blockIdx.x);
 }
 
 // =====================================================================
@@ -704,15 +731,24 @@ hipError_t launch_z_mfma(const GemmArgs &a, float *zf, hipStream_t stream) {
 hipError_t launch_gemm_mfma(const GemmArgs &a, hipStream_t stream) {
     if (!mfma_supported(a.M, a.N, a.K, a.r)) return hipErrorNotSupported;
     MfmaPlan q;
-    const MfmaParams p = mfma_params(a, q);
+    MfmaParams p = mfma_params(a, q);
     hipError_t e = hipSuccess;
     if (a.r > 0) {
-        if (q.mb == 1)
+        // With many K-slices, the z slices store partials only and a reduce
+        // launch finishes each word: there a launch boundary costs less than
+        // the exchange of partials through a counter inside one launch
+        // (measured: 14 slices gain, 5 and 8 lose).
+        p.zsplit = q.zs >= kZSplitMinSlices ? 1 : 0;
+        if (q.mb == 1) {
             hipLaunchKernelGGL(mfma_z_kernel<1>, dim3(q.W * q.zs), dim3(kZThreads), 0, stream, p);
-        else
+            if (p.zsplit) hipLaunchKernelGGL(mfma_zreduce_kernel<1>, dim3(q.W), dim3(kZThreads), 0, stream, p);
+        } else {
             hipLaunchKernelGGL(mfma_z_kernel<2>, dim3(q.W * q.zs), dim3(kZThreads), 0, stream, p);
+            if (p.zsplit) hipLaunchKernelGGL(mfma_zreduce_kernel<2>, dim3(q.W), dim3(kZThreads), 0, stream, p);
+        }
         e = hipGetLastError();
         if (e != hipSuccess) return e;
+        p.zsplit = 0;
     }
     const dim3 grid(q.grid), block(kPThreads);
     constexpr int c1 = MfmaShape<1>::kCpw, c2 = MfmaShape<2>::kCpw;
