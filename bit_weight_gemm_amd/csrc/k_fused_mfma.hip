@@ -75,6 +75,8 @@ constexpr int kZSplitMinSlices = 12;    // z slices from which the exchange gets
 //              code loads in flight at once
 //   kCpwWide, kRbwWide   the whole-K variant for M <= 16 (no K split while
 //              8 kCpwWide chunks cover K): fewer row blocks, more chunks
+//   kPipe      row blocks whose code loads are in flight ahead of the one
+//              being computed
 // A wave's scale bytes in a row (CPW x 8) fit a 16-byte-aligned window of
 // scale_pieces(CPW) 16-byte pieces.
 template <int MB> struct MfmaShape {
@@ -83,6 +85,9 @@ template <int MB> struct MfmaShape {
     static constexpr int kRbwLarge = MB == 1 ? 8 : 7;   // row blocks per workgroup, large variant
     static constexpr int kCpwWide = 5;
     static constexpr int kRbwWide = 4;
+    // row blocks of code loads requested ahead of the arithmetic (measured
+    // best: 1 for one m-block, 2 for two; all at once was slower for both)
+    static constexpr int kPipe = MB == 1 ? 1 : 2;
 };
 __host__ __device__ constexpr int scale_pieces(int cpw) { return (cpw * 8 + 14 + 15) / 16; }
 
@@ -336,15 +341,16 @@ __global__ void __launch_bounds__(kZThreads) mfma_zreduce_kernel(MfmaParams p) {
 // [q ncs / 8, (q + 1) ncs / 8) of the slice for every row block of the range:
 // its activation tile (those chunks, every K-step, every m-block) lives in
 // registers for the whole launch, so the stream of R meets no LDS read.
-// The range is at most RBW row blocks.  The wave issues every load it needs
-// (RBW x CPW 16-byte code loads and their scales) before computing anything,
-// then consumes the row blocks in issue order.  A slot with no work (row
-// block past the range, chunk past the wave's share) loads zeros through an
-// out-of-range buffer offset, so every path issues the same loads and the
-// hardware wait counts stay exact.
+// The range is at most RBW row blocks.  The wave requests its activation and
+// scales first, then its code loads of R kPipe row blocks ahead of the row
+// block it computes (CPW 16-byte loads per row block).  A slot with no work
+// (row block past the range, chunk past the wave's share) loads zeros
+// through an out-of-range buffer offset, so every path issues the same loads
+// and the hardware wait counts stay exact.
 template <int MB, int RBW, int CPW>
 __global__ void __launch_bounds__(kPThreads) mfma_product_kernel(MfmaParams p) {
     constexpr int PPR = scale_pieces(CPW);              // 16-byte scale pieces per row
+    constexpr int kPipe = MfmaShape<MB>::kPipe;
     // LDS: the waves' partial sums [wave][row block][mb][64 lanes], then each
     // wave's block scales of R [wave][row][PPR 16-byte pieces]
     extern __shared__ float4_t s_part[];
@@ -419,10 +425,15 @@ __global__ void __launch_bounds__(kPThreads) mfma_product_kernel(MfmaParams p) {
     const bool has_corr = wave < nws;
     if (has_corr) corr_load(wave);
 
-    // ---- every code load of R for this workgroup
+    // ---- code loads of R: the first kPipe row blocks now, each further one
+    // once the row block kPipe before it is done.  Issued all at once, the
+    // last of them went out only after several microseconds (the memory
+    // system takes new requests as old ones return) and no arithmetic could
+    // start before; this way the wave computes while its later row blocks
+    // are still being requested.  Every index is a constant, so each wait
+    // counts exactly the loads issued after the ones it needs.
     u32x4_t cw[RBW][CPW];
-#pragma unroll
-    for (int rbl = 0; rbl < RBW; ++rbl) {
+    auto load_rb = [&](int rbl) {
         const int n = (pb + rbl) * 16 + col;
 #pragma unroll
         for (int c = 0; c < CPW; ++c) {
@@ -430,7 +441,10 @@ __global__ void __launch_bounds__(kPThreads) mfma_product_kernel(MfmaParams p) {
             const bool ok = rbl < nrb && n < p.N && c < cpw && gc * kChunkK + grp * 32 < p.K;
             cw[rbl][c] = load16(r_wc, opaque(ok ? n * KH + gc * 64 + grp * 16 : kOob));
         }
-    }
+    };
+#pragma unroll
+    for (int rbl = 0; rbl < RBW; ++rbl)
+        if (rbl < kPipe) load_rb(rbl);
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- this wave's scale windows to its own LDS region (no barrier: only
@@ -506,6 +520,8 @@ __global__ void __launch_bounds__(kPThreads) mfma_product_kernel(MfmaParams p) {
             for (int mb = 0; mb < MB; ++mb) mine[(rbl * MB + mb) * 64] = acc[mb][0] + acc[mb][1];
         }
         // keep each row block's dequantisation next to its MFMAs
+        __builtin_amdgcn_sched_barrier(0);
+        if (rbl + kPipe < RBW) load_rb(rbl + kPipe);
         __builtin_amdgcn_sched_barrier(0);
     }
     // further correction words of this wave (more than 8 per slice)
