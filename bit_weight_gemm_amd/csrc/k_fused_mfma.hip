@@ -66,7 +66,7 @@ constexpr int kGridTarget = 256;        // one workgroup per CU
 constexpr size_t kLdsLimit = 160 * 1024 - 1024;
 
 constexpr int kSumBatch = 8;            // K-slice partials of y loaded at once by the epilogue
-constexpr int kZSplitMinSlices = 12;    // z slices from which the exchange gets a launch of its own
+constexpr int kZSplitMinSlices = 8;     // z slices from which the exchange gets a launch of its own
 
 // Per batch-tile-height tuning (MB m-blocks of 16 rows):
 //   kCpw       128-k chunks per wave: the activation tile takes 16 kCpw MB
@@ -179,9 +179,9 @@ __device__ __forceinline__ uint32_t arrive(uint32_t *cnt) {
 // boundary (plain loads).
 constexpr int kZSumBatch = 16;          // slice partials loaded at once
 template <int MB, bool COHERENT>
-__device__ __forceinline__ void z_finish(const MfmaParams &p, int w) {
+__device__ __forceinline__ void z_finish(const MfmaParams &p, int w, int first = 0, int step = kZThreads) {
     const float ginv = 1.0f / p.g;
-    for (int idx = threadIdx.x; idx < MB * 64 * 8; idx += kZThreads) {
+    for (int idx = first + (int)threadIdx.x; idx < MB * 64 * 8; idx += step) {
         const int j = idx & 7, l = (idx >> 3) & 63, mb = idx >> 9;
         const int m = 16 * mb + (l & 15), q = l >> 4;
         float sum = 0.0f;
@@ -328,10 +328,14 @@ __global__ void __launch_bounds__(kZThreads) mfma_z_kernel(MfmaParams p) {
     if (threadIdx.x == 0) p.zcnt[w] = 0u;   // ready for the next call on this workspace
 }
 
-// The reduce launch: workgroup w finishes word w from the slice partials.
+// The reduce launch: workgroup (w, part) finishes the kZrThreads values
+// [part kZrThreads, (part + 1) kZrThreads) of word w's operand from the
+// slice partials, one value per thread.
+constexpr int kZrThreads = 256;
 template <int MB>
-__global__ void __launch_bounds__(kZThreads) mfma_zreduce_kernel(MfmaParams p) {
-    z_finish<MB, false>(p, blockIdx.x);
+__global__ void __launch_bounds__(kZrThreads) mfma_zreduce_kernel(MfmaParams p) {
+    constexpr int parts = MB * 64 * 8 / kZrThreads;
+    z_finish<MB, false>(p, blockIdx.x / parts, (blockIdx.x % parts) * kZrThreads, MB * 64 * 8);
 }
 
 // =====================================================================
@@ -753,14 +757,14 @@ hipError_t launch_gemm_mfma(const GemmArgs &a, hipStream_t stream) {
         // With many K-slices, the z slices store partials only and a reduce
         // launch finishes each word: there a launch boundary costs less than
         // the exchange of partials through a counter inside one launch
-        // (measured: 14 slices gain, 5 and 8 lose).
+        // (measured: 8 and 14 slices gain, 5 loses).
         p.zsplit = q.zs >= kZSplitMinSlices ? 1 : 0;
         if (q.mb == 1) {
             hipLaunchKernelGGL(mfma_z_kernel<1>, dim3(q.W * q.zs), dim3(kZThreads), 0, stream, p);
-            if (p.zsplit) hipLaunchKernelGGL(mfma_zreduce_kernel<1>, dim3(q.W), dim3(kZThreads), 0, stream, p);
+            if (p.zsplit) hipLaunchKernelGGL(mfma_zreduce_kernel<1>, dim3(q.W * 2), dim3(kZrThreads), 0, stream, p);
         } else {
             hipLaunchKernelGGL(mfma_z_kernel<2>, dim3(q.W * q.zs), dim3(kZThreads), 0, stream, p);
-            if (p.zsplit) hipLaunchKernelGGL(mfma_zreduce_kernel<2>, dim3(q.W), dim3(kZThreads), 0, stream, p);
+            if (p.zsplit) hipLaunchKernelGGL(mfma_zreduce_kernel<2>, dim3(q.W * 4), dim3(kZrThreads), 0, stream, p);
         }
         e = hipGetLastError();
         if (e != hipSuccess) return e;
