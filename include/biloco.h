@@ -61,7 +61,8 @@ typedef int32_t biloco_status;
                                        M <= 2; a plain, slow fallback at larger M) */
 #define BILOCO_SCHED_FUSED_GEMV  2  /* one launch; vector-ALU dot products; M <= 2 */
 #define BILOCO_SCHED_FUSED_MFMA  3  /* matrix-core products for any M <= 32: a z kernel
-                                       (skipped when r == 0), then one product kernel whose
+                                       (skipped when r == 0; from K >= 8192 a second launch
+                                       sums its K-slices), then one product kernel whose
                                        accumulators take the correction before the store,
                                        then (only when K is split over workgroups) a launch
                                        that sums the K-slices; the default at M >= 3 */
@@ -199,8 +200,8 @@ biloco_status biloco_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K, int32
  * Limits: 1 <= M <= 32; N >= 1; K >= 32 and K % 32 == 0; r >= 0.
  * With r == 0, x_bf16, v_packed, u_packed and alpha_bf16 may be NULL.
  * Accuracy: y is within 8e-3*|y_ref| + 1e-3*rms(y_ref) of the exact value
- * (fp32 accumulation, bf16 output rounding).  One or two launches on
- * `stream`, depending on the schedule. */
+ * (fp32 accumulation, bf16 output rounding).  One to four launches on
+ * `stream`, depending on the schedule and the shape. */
 biloco_status biloco_gemm_lowrank(const uint8_t *a_codes, const uint8_t *a_scales,
                                   const uint16_t *x_bf16,
                                   const uint8_t *w_codes, const uint8_t *w_scales,
