@@ -61,7 +61,7 @@ typedef int32_t biloco_status;
                                        M <= 2; a plain, slow fallback at larger M) */
 #define BILOCO_SCHED_FUSED_GEMV  2  /* one launch; vector-ALU dot products; M <= 2 */
 #define BILOCO_SCHED_FUSED_MFMA  3  /* matrix-core products for any M <= 32: a z kernel
-                                       (skipped when r == 0; from K >= 8192 a second launch
+                                       (skipped when r == 0; for K > 7168 a second launch
                                        sums its K-slices), then one product kernel whose
                                        accumulators take the correction before the store,
                                        then (only when K is split over workgroups) a launch
