@@ -424,16 +424,40 @@ __global__ void __launch_bounds__(kGemvThreads) fused_gemv_kernel(GemvParams p) 
     // ---- small inputs first.  Requested behind the stream of R, scattered
     // reads come back only once the stream has drained; requested first, they
     // are in hand before any row of R is asked for.
-    // 1. the FP4 activation blocks this thread decodes (clamped addresses)
+    // 1. the FP4 activation.  Two launches and r = 0 (lane_act): each lane
+    // loads the codes and scales of its own blocks (lane + 64 t) and decodes
+    // them in registers once the rows of R are requested, so no barrier and
+    // no LDS stand between the start and the stream.  One launch: the blocks
+    // this thread decodes into LDS for the workgroup (clamped addresses).
+    constexpr bool lane_act = ZMODE != 1 && KBL * MM <= 8;   // (beyond: too many registers)
     const int nact = MM * KB;
     uint2 ac[AMAX];
     uint32_t asb[AMAX];
+    uint2 lac[lane_act ? KBL : 1][MM];
+    uint32_t las[lane_act ? KBL : 1][MM];
+    if constexpr (lane_act) {
+        // scales as the aligned 4-byte word holding the lane's byte (a byte
+        // load's widening would be placed, and waited for, right here); the
+        // last word may cover up to 3 bytes past the array, inside the
+        // 16-byte block that holds its last byte, and those bytes are unused
+        const __amdgpu_buffer_rsrc_t r_as = buffer_of(p.a_scales, ((int64_t)MM * KB + 3) & ~(int64_t)3);
 #pragma unroll
-    for (int a = 0; a < AMAX; ++a) {
-        const int ai = threadIdx.x + kGemvThreads * a, aic = ai < nact ? ai : nact - 1;
-        const int m = aic / KB, b = aic - m * KB;
-        ac[a] = *reinterpret_cast<const uint2 *>(p.a_codes + (int64_t)m * KH + b * 8);
-        asb[a] = p.a_scales[(int64_t)m * KB + b];
+        for (int t = 0; t < KBL; ++t) {
+            const int b = lane + 64 * t, bc = b < KB ? b : KB - 1;
+#pragma unroll
+            for (int m = 0; m < MM; ++m) {
+                lac[t][m] = *reinterpret_cast<const uint2 *>(p.a_codes + (int64_t)m * KH + bc * 8);
+                las[t][m] = __builtin_amdgcn_raw_buffer_load_b32(r_as, (m * KB + bc) & ~3, 0, 0);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int a = 0; a < AMAX; ++a) {
+            const int ai = threadIdx.x + kGemvThreads * a, aic = ai < nact ? ai : nact - 1;
+            const int m = aic / KB, b = aic - m * KB;
+            ac[a] = *reinterpret_cast<const uint2 *>(p.a_codes + (int64_t)m * KH + b * 8);
+            asb[a] = p.a_scales[(int64_t)m * KB + b];
+        }
     }
     // 2. a z item's inputs (one launch) or the finished z (two launches)
     const bool z_wg = ZMODE == 1 && (int)blockIdx.x < p.z_items;
@@ -493,6 +517,22 @@ __global__ void __launch_bounds__(kGemvThreads) fused_gemv_kernel(GemvParams p) 
 
     // 4. decode the activation into LDS: [m][block][8 f16 pairs], exact values;
     // z (two launches) into its own LDS area
+    // exact f16 values of one block's 16 codes (8 pairs) under scale byte sb
+    auto decode_block = [&](uint2 c, uint32_t sb, uint32_t (&o)[8]) {
+        const float sa = __builtin_amdgcn_cvt_f32_fp8(sb, 0);
+        const _Float16 mh = (_Float16)scale_mant(sa);
+        const half2_t mm2 = {mh, mh};
+        const uint32_t raw[8] = {
+            fp4x2_to_f16x2<0>(c.x, sa), fp4x2_to_f16x2<1>(c.x, sa),
+            fp4x2_to_f16x2<2>(c.x, sa), fp4x2_to_f16x2<3>(c.x, sa),
+            fp4x2_to_f16x2<0>(c.y, sa), fp4x2_to_f16x2<1>(c.y, sa),
+            fp4x2_to_f16x2<2>(c.y, sa), fp4x2_to_f16x2<3>(c.y, sa)};
+#pragma unroll
+        for (int d = 0; d < 8; ++d)
+            o[d] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, raw[d]) * mm2);
+    };
+    uint32_t act[KBL][MM][8];
+    if constexpr (!lane_act) {
 #pragma unroll
     for (int a = 0; a < AMAX; ++a) {
         const int ai = threadIdx.x + kGemvThreads * a;
@@ -515,7 +555,6 @@ __global__ void __launch_bounds__(kGemvThreads) fused_gemv_kernel(GemvParams p) 
         }
     }
     __syncthreads();
-    uint32_t act[KBL][MM][8];
 #pragma unroll
     for (int t = 0; t < KBL; ++t) {
         const int b = lane + 64 * t, bc = b < KB ? b : KB - 1;
@@ -526,6 +565,7 @@ __global__ void __launch_bounds__(kGemvThreads) fused_gemv_kernel(GemvParams p) 
             act[t][m][0] = lo.x; act[t][m][1] = lo.y; act[t][m][2] = lo.z; act[t][m][3] = lo.w;
             act[t][m][4] = hi.x; act[t][m][5] = hi.y; act[t][m][6] = hi.z; act[t][m][7] = hi.w;
         }
+    }
     }
 
     // 6-8. the rows of R, the FP4 product of every row, times g, onto the
@@ -556,6 +596,21 @@ __global__ void __launch_bounds__(kGemvThreads) fused_gemv_kernel(GemvParams p) 
             }
         }
         __builtin_amdgcn_sched_barrier(0);
+        // the lane's activation, decoded while the rows stream in (its words
+        // pass an empty asm here, so that neither the decode nor its wait is
+        // hoisted out of this row-count case to before the rows' loads)
+        if constexpr (lane_act) {
+#pragma unroll
+            for (int t = 0; t < KBL; ++t)
+#pragma unroll
+                for (int m = 0; m < MM; ++m) {
+                    const uint2 c = make_uint2((uint32_t)opaque((int)lac[t][m].x),
+                                               (uint32_t)opaque((int)lac[t][m].y));
+                    const int b = lane + 64 * t, bc = b < KB ? b : KB - 1;
+                    const uint32_t sb = ((uint32_t)opaque((int)las[t][m]) >> (8 * ((m * KB + bc) & 3))) & 0xFFu;
+                    decode_block(c, sb, act[t][m]);
+                }
+        }
         // one launch: the z item, published while the rows stream in
         if constexpr (ZMODE == 1 && z_early) {
             if (z_wg) z_item_waves<MM>(p, blockIdx.x, zin, ep, s_zslots, &s_zcnt);
