@@ -411,7 +411,11 @@ __global__ void __launch_bounds__(kGemvThreads) fused_gemv_kernel(GemvParams p) 
     // requested with the correction inputs (first, it would hold up the
     // activation: the word was last written on another XCD)
     uint32_t ep = 0u;
-    if (ZMODE == 1 && threadIdx.x == 0) s_zcnt = 0u;   // ordered by the activation's barrier
+    if constexpr (ZMODE == 1) {
+        // the z item's arrival counter, zeroed before any wave can use it
+        if (threadIdx.x == 0) s_zcnt = 0u;
+        __syncthreads();
+    }
 
     // rows of this workgroup, spread over its 8 waves (the first get one more)
     const int wg_row0 = blockIdx.x * p.rows_per_wg;
@@ -424,12 +428,14 @@ __global__ void __launch_bounds__(kGemvThreads) fused_gemv_kernel(GemvParams p) 
     // ---- small inputs first.  Requested behind the stream of R, scattered
     // reads come back only once the stream has drained; requested first, they
     // are in hand before any row of R is asked for.
-    // 1. the FP4 activation.  Two launches and r = 0 (lane_act): each lane
-    // loads the codes and scales of its own blocks (lane + 64 t) and decodes
-    // them in registers once the rows of R are requested, so no barrier and
-    // no LDS stand between the start and the stream.  One launch: the blocks
-    // this thread decodes into LDS for the workgroup (clamped addresses).
-    constexpr bool lane_act = ZMODE != 1 && KBL * MM <= 8;   // (beyond: too many registers)
+    // 1. the FP4 activation.  lane_act: each lane loads the codes and scales
+    // of its own blocks (lane + 64 t) and decodes them in registers once the
+    // rows of R are requested, so no barrier and no LDS stand between the
+    // start and the stream.  Otherwise the blocks this thread decodes into
+    // LDS for the workgroup (clamped addresses).
+    // (beyond these sizes: too many registers; one launch also holds its z
+    // item's inputs)
+    constexpr bool lane_act = KBL * MM <= (ZMODE == 1 ? 6 : 8);
     const int nact = MM * KB;
     uint2 ac[AMAX];
     uint32_t asb[AMAX];
