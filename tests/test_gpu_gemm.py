@@ -87,7 +87,12 @@ def test_every_batch_size_ragged(M):
                                      (3, 5120, 70000, 33),
                                      # z over 7 and 8 K-slices of 1024: the slices'
                                      # exchange in the z launch, and in a launch of its own
-                                     (20, 7168, 200, 33), (5, 8192, 300, 70)])
+                                     (20, 7168, 200, 33), (5, 8192, 300, 70),
+                                     # vector schedules, activation per lane or through
+                                     # LDS (64-block lanes x rows of 6, 8, 12 and 16)
+                                     (2, 3072, 500, 40), (2, 4096, 500, 40),
+                                     (2, 6144, 300, 33), (1, 8192, 300, 100),
+                                     (1, 12288, 200, 64)])
 def test_edge_shapes(M, K, N, r):
     d = wl.make_inputs(M, K, N, r, seed=M * 1000 + N)
     y_ref = oracle.gemm_lowrank(d["x"], d["wcode"], d["wscales"], d["g"], d["V"], d["U"],
