@@ -338,16 +338,24 @@ def main() -> int:
             tcomp = gemm_call_time(pc, B.BILOCO_SCHED_COMPOSED, rc, calls)
             tcm = gemm_call_time(pc, B.BILOCO_SCHED_COMPOSED_MFMA, rc, calls)
             bc = algorithmic_bytes(pc.M, pc.N, pc.K, pc.r)
-            table[f"config{c}"] = {"M": pc.M, "K": pc.K, "N": pc.N, "r": pc.r,
+            del rc, pc
+            torch.cuda.empty_cache()
+            # the same x and R with r = 0, for the correction's cost at this shape
+            pz = DeviceProblem(wl.make_config(c, r=0))
+            rz = Rotation(pz, max(2, int(ROT_BYTES // weight_bytes(pz)) + 1))
+            tz = gemm_call_time(pz, B.biloco_default_schedule(pz.M, pz.N, pz.K, 0), rz, calls)
+            del rz, pz
+            torch.cuda.empty_cache()
+            table[f"config{c}"] = {"M": dc["M"], "K": dc["K"], "N": dc["N"], "r": dc["r"],
                                    "schedule": SCHED_NAMES.get(sc, sc),
                                    "us_per_call": round(tc * 1e6, 3),
                                    "GBps": round(bc / tc / 1e9, 1),
                                    "pct_peak": round(100 * bc / tc / 1e9 / PEAK_HBM_GBS, 2),
+                                   "r0_us_per_call": round(tz * 1e6, 3),
+                                   "correction_overhead": round(tc / tz - 1.0, 4),
                                    "composed_us_per_call": round(tcomp * 1e6, 3),
                                    "composed_mfma_us_per_call": round(tcm * 1e6, 3),
                                    "speedup_vs_composed": round(min(tcomp, tcm) / tc, 3)}
-            del rc, pc
-            torch.cuda.empty_cache()
         out["per_config"] = table
         out["weight_quant"] = weight_quant_table()
         out["decompose"] = decompose_time()
