@@ -41,12 +41,39 @@ def algorithmic_bytes(M: int, N: int, K: int, r: int) -> int:
     return b
 
 
+def code_text(src: str) -> str:
+    """C/C++/HIP source without its comments and with runs of whitespace
+    collapsed: what the compiler sees, so that an edit of a comment leaves
+    the hash of the kernels alone."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":                            # string or character literal
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            out.append(" ")
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def source_hash() -> str:
+    """Hash of the kernel and library sources' code (comments excluded)."""
     h = hashlib.sha256()
     for f in sorted(glob.glob(os.path.join(ROOT, "bit_weight_gemm_amd", "csrc", "*"))):
-        with open(f, "rb") as fh:
+        with open(f, "r", encoding="utf-8") as fh:
             h.update(os.path.basename(f).encode())
-            h.update(fh.read())
+            h.update(code_text(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -1,37 +1,43 @@
-// One-launch product for small decode batches (schedule BILOCO_SCHED_FUSED_GEMV).
+// Vector product for decode batches M <= 2 (schedules
+// BILOCO_SCHED_UNFUSED, the default, and BILOCO_SCHED_FUSED_GEMV).
 //
-// BiLoCo README, section "Kernel": y = FP4(x) FP4(R)^T + sum_i alpha_i (x.v_i) u_i
-// in one launch; side work computes z = alpha (.) (V x) from the packed signs of
-// V while the FP4 product streams R; z values are published with an epoch tag
-// that the output tiles poll; the epilogue expands z through U's packed signs
-// and adds it before the bf16 store.  Designed here for gfx950 and M <= 2,
-// where the product is a matrix-vector stream bound by HBM:
+// BiLoCo README, section "Kernel": y = FP4(x) FP4(R)^T + sum_i alpha_i (x.v_i) u_i;
+// z = alpha (.) (V x) comes from the packed signs of V, and the epilogue
+// expands z through U's packed signs before the bf16 store.  Designed here
+// for gfx950, where at M <= 2 the product is a matrix-vector stream bound
+// by HBM:
 //
 //  * about one workgroup per CU streams R, 8 waves (two per SIMD), every
-//    wave owning up to R whole rows (full K), so no partial sum crosses a
+//    wave owning up to 4 whole rows (full K), so no partial sum crosses a
 //    workgroup; lanes stride over the 16-element NVFP4 blocks of a row;
-//  * the first ceil(r/2) workgroups also produce z, 2 indices i each over
-//    all of K, with their inputs requested before their rows of R: the +-1
-//    signs of two consecutive k come out of one pair of V words as a bf16
-//    pair, so x (bf16) and the signs meet in v_dot2 (bf16) with exact
-//    products;
 //  * R is dequantised in registers: one v_cvt_scalef32_pk_f16_fp4 per code
 //    byte applies the block scale's power of two, the scale's mantissa
-//    (1 + m/8) multiplies the block's fp32 partial sum; the FP4 activation is
-//    decoded once per workgroup into LDS (exact f16) and held in registers;
-//    the products are v_dot2 (f16 x f16 -> fp32);
-//  * each z value is published as one 64-bit word (fp32 value | epoch << 32)
-//    with a relaxed device-scope store and read back with device-scope loads:
-//    data and tag travel together, so no fence is needed;
-//  * the call's epoch is a plain load at start; every workgroup then writes a
-//    "seen" flag, and workgroup 0 advances the epoch at its end once every
-//    flag is in: no counter is hit by all workgroups;
-//  * U's words for the wave's rows are fetched at start; the correction
-//    multiplies U's signs (bf16 pairs) with z split into bf16 high and low
-//    parts (about 16 bits of z) and joins the row sum before the one
-//    reduction per row and m;
-//  * a consumer's wait for z is bounded: when it runs out the consumer
-//    computes the z values itself, so the kernel ends whatever else runs.
+//    (1 + m/8) multiplies the block's fp32 partial sum; the products with
+//    the exact f16 activation are v_dot2 (f16 x f16 -> fp32);
+//  * the FP4 activation is requested first; at small K M every lane loads
+//    and decodes its own blocks once its rows of R are requested (no LDS,
+//    no barrier before the stream), otherwise the workgroup decodes it into
+//    LDS behind one barrier;
+//  * z: v_dot2 (bf16) of x against bf16 pairs of +-1 built from V's words,
+//    exact products, one workgroup per two indices i over all of K;
+//  * the correction multiplies U's signs (bf16 pairs) with z split into bf16
+//    high and low parts (about 16 bits of z) and joins the row sum before
+//    the one reduction per row and m.
+//
+// Two forms of the z hand-off:
+//  * two launches (the default): z_kernel writes z, already split into its
+//    high/low parts in the lane order of the correction, and (in the
+//    quantising call) quantises x in workgroups of its own; the product then
+//    loads those operands straight into registers;
+//  * one launch: the first workgroups also produce z while every workgroup
+//    streams R.  Each z value is published as one 64-bit word (fp32 value |
+//    epoch << 32) with a relaxed device-scope store and read back with
+//    device-scope loads, so data and tag travel together and no fence is
+//    needed.  The call's epoch is a plain load at start; every workgroup
+//    then writes a "seen" flag, and workgroup 0 advances the epoch at its
+//    end once every flag is in.  A consumer's wait for z is bounded: when it
+//    runs out the consumer computes the z values itself, so the kernel ends
+//    whatever else runs.
 #include <type_traits>
 
 #include "biloco_device.h"

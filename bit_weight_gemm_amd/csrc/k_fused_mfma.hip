@@ -5,24 +5,26 @@
 // packed signs, and z is expanded through U's packed signs into the fp32
 // accumulators before the bf16 store.  The pages run the FP4 GEMM on tensor
 // cores with the batch padded to 128 rows.  Here, on gfx950 matrix cores, the
-// batch is padded to 16 rows (M <= 16) or 32 rows.  The work is two or three
+// batch is padded to 16 rows (M <= 16) or 32 rows.  The work is one to four
 // launches on one stream:
 //
 // 1. mfma_z_kernel (r > 0) computes z/g = (alpha/g) (.) (x . V+-) with
 //    v_mfma_f32_16x16x32_bf16.  The bf16 activation x is exact as an operand;
 //    the +-1 operand is built in registers from V's sign words.  Workgroups
-//    own (one 32-bit word of V, one K-slice).  The last workgroup to arrive
-//    for a word (a counter, never a wait) sums the slices and stores bf16
-//    high + low parts in the register layout of the correction MFMA.
+//    own (one 32-bit word of V, one K-slice).  With fewer than 8 K-slices the
+//    last workgroup to arrive for a word (a counter, never a wait) sums the
+//    slices and stores bf16 high + low parts in the register layout of the
+//    correction MFMA; from 8 slices on, mfma_zreduce_kernel does that in a
+//    launch of its own.
 //
 // 2. mfma_product_kernel: one workgroup of 8 waves per CU.  Each workgroup
 //    owns one K-slice and a range of 16-row blocks of R.
 //    - Each wave owns up to three 128-k chunks of the slice.  Its activation
 //      tile for them is loaded once and dequantised into registers as exact
 //      f16.
-//    - Every wave issues all of its loads of R (raw buffer loads, zeros for
-//      out-of-range slots) before computing.  Its block scales go through a
-//      wave-private LDS window.
+//    - Every wave requests its loads of R (raw buffer loads, zeros for
+//      out-of-range slots) one or two row blocks ahead of the row block it
+//      computes.  Its block scales go through a wave-private LDS window.
 //    - Codes are dequantised in registers into the B operand of
 //      v_mfma_f32_16x16x32_f16.  One v_cvt_scalef32_pk_f16_fp4 per byte
 //      applies the power of two of the E4M3 block scale, and a packed f16
@@ -33,7 +35,8 @@
 //      workgroup stores y; otherwise it stores its slice's partial sums.
 //
 // 3. mfma_epilogue_kernel (K split in S > 1 slices) sums the slices,
-//    multiplies by g and stores bf16.
+//    multiplies by g and stores bf16 (a launch of its own: summing them in
+//    the product by the last slice to arrive measured slower).
 //
 // MFMA operand layout of the 16x16x32 forms (checked on the device):
 //   A[i][k] sits in lane i + 16 (k / 8), element k % 8.
