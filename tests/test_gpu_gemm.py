@@ -3,7 +3,8 @@
 Every schedule a shape allows is compared element by element with the
 oracle on the same seeded inputs: all five decode workloads at full size,
 the r = 0 plain GEMM, every M in 1..32 on a small ragged shape, partial sign
-words, and repeated calls on one workspace.
+words, repeated calls on one workspace, and the captured-graph form the
+benchmark times (rotated weight copies, several replays).
 """
 import functools
 
@@ -265,3 +266,49 @@ def test_rank_above_1024(M, r):
     for s in scheds:
         y, _ = _run(d, s, p)
         check_y(y, y_ref, f"M={M} r={r} schedule {s}")
+
+
+@pytest.mark.parametrize("cfg,sched", [(1, B.BILOCO_SCHED_AUTO), (2, B.BILOCO_SCHED_AUTO),
+                                      (3, B.BILOCO_SCHED_AUTO), (4, B.BILOCO_SCHED_AUTO),
+                                      (1, B.BILOCO_SCHED_FUSED_GEMV), (1, B.BILOCO_SCHED_FUSED_MFMA)])
+def test_graph_replay_as_timed(cfg, sched):
+    """The form the benchmark times: quantise-and-multiply calls captured once
+    in a graph over rotated copies of the weights, replayed several times with
+    eager work in between.  Every call of every replay gives the eager call's
+    bits (the eager call itself is checked against the oracle), and the
+    activation codes and scales it writes are the oracle's."""
+    d, y_ref = _case(cfg)
+    p = DeviceProblem(d, quantize=False)
+    rc, rs = oracle.quant_act_fp4(d["x"])
+    p.gemm_quant(sched)
+    torch.cuda.synchronize()
+    check_y(p.y_float(), y_ref, f"config {cfg} schedule {sched} eager")
+    y_eager = p.y.clone()
+    n_sets, calls = 3, 6
+    wc = [p.w_codes.clone() for _ in range(n_sets)]
+    ws = [p.w_scales.clone() for _ in range(n_sets)]
+    up = [p.u_packed.clone() for _ in range(n_sets)] if p.r else [None] * n_sets
+    vp = [p.v_packed.clone() for _ in range(n_sets)] if p.r else [None] * n_sets
+    ys = [torch.empty_like(p.y) for _ in range(calls)]
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=st):
+        for i in range(calls):
+            k = i % n_sets
+            p.gemm_quant(sched, stream=st, w_codes=wc[k], w_scales=ws[k], u_packed=up[k],
+                         v_packed=vp[k], y=ys[i])
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in ys:
+            t.fill_(0x3F00 + rep)
+        p.a_codes.fill_(0x5A)
+        p.a_scales.fill_(0x33)
+        torch.cuda.synchronize()
+        print(f"config {cfg} schedule {sched} replay {rep}", flush=True)
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, t in enumerate(ys):
+            assert torch.equal(t, y_eager), f"config {cfg} schedule {sched} replay {rep} call {i}"
+        np.testing.assert_array_equal(p.a_codes.cpu().numpy(), rc, err_msg=f"replay {rep}")
+        np.testing.assert_array_equal(p.a_scales.cpu().numpy(), rs, err_msg=f"replay {rep}")
