@@ -67,6 +67,14 @@ def code_text(src: str) -> str:
     return " ".join("".join(out).split())
 
 
+# the launches of one product call per default schedule; the roofline divides
+# the call's algorithmic bytes by the call's time, which the kernel trace
+# gives as the sum of these kernels' averages
+CALL_KERNELS = {"unfused": "z_kernel + fused_gemv_kernel",
+                "fused_mfma": "mfma_z_kernel + mfma_zreduce_kernel (K > 7168) + "
+                              "mfma_product_kernel + mfma_epilogue_kernel (split K)"}
+
+
 def source_hash() -> str:
     """Hash of the kernel and library sources' code (comments excluded)."""
     h = hashlib.sha256()
@@ -336,7 +344,8 @@ def main() -> int:
         "us_per_call_cache_resident": round(t_warm * 1e6, 3),
         "pct_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
         "step_gpu_us": round(gpu * 1e6 / K_steps, 3),
-        "roofline": {"bound": "hbm", "kernel": f"biloco_gemm_lowrank ({sched_name})",
+        "roofline": {"bound": "hbm", "kernel": f"biloco_gemm_lowrank call ({sched_name}: "
+                                               f"{CALL_KERNELS.get(sched_name, 'its launches')})",
                      "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": traffic, "bytes_per_call": nbytes},
