@@ -37,8 +37,11 @@ biloco_status check_shape(int32_t M, int32_t N, int32_t K, int32_t r) {
     if (K % 16 != 0) return BILOCO_ERR_INVALID_VALUE;   // NVFP4 blocks of 16
     if (M > 32) return BILOCO_ERR_UNSUPPORTED;          // decode batches up to 32
     if (K % 32 != 0 || K < 32) return BILOCO_ERR_UNSUPPORTED;
-    // the kernels address R's codes (N x K/2 bytes) with 32-bit byte offsets
+    // the kernels address R's codes (N x K/2 bytes) and the sign words of U
+    // and V (ceil(r/32) x N or K words) with 32-bit byte offsets
     if ((int64_t)N * (K / 2) > (int64_t)INT32_MAX) return BILOCO_ERR_UNSUPPORTED;
+    const int64_t W = ((int64_t)r + 31) / 32;
+    if (W * 4 * (N > K ? N : K) > (int64_t)INT32_MAX) return BILOCO_ERR_UNSUPPORTED;
     return BILOCO_OK;
 }
 

@@ -198,7 +198,8 @@ biloco_status biloco_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K, int32
  *          used by two calls that can run at the same time (use one per
  *          stream).
  * Limits: 1 <= M <= 32; N >= 1; K >= 32 and K % 32 == 0; r >= 0;
- *   N * K / 2 < 2^31 (the codes of R are addressed with 32-bit byte offsets).
+ *   N * K / 2 < 2^31 and 4 * ceil(r/32) * max(N, K) < 2^31 (R's codes and the
+ *   sign words are addressed with 32-bit byte offsets).
  * With r == 0, x_bf16, v_packed, u_packed and alpha_bf16 may be NULL.
  * Accuracy: y is within 8e-3*|y_ref| + 1e-3*rms(y_ref) of the exact value
  * (fp32 accumulation, bf16 output rounding).  One to four launches on

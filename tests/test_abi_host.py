@@ -59,6 +59,7 @@ def test_check_accepts_valid():
     (dict(K=40), B.BILOCO_ERR_INVALID_VALUE),
     (dict(r=-1), B.BILOCO_ERR_INVALID_VALUE),
     (dict(N=65536, K=65536), B.BILOCO_ERR_UNSUPPORTED),     # R's codes: 2^31 bytes
+    (dict(N=1 << 24, K=32, r=1024), B.BILOCO_ERR_UNSUPPORTED),  # U's words: 2^31 bytes
 ])
 def test_check_rejects_shapes(kw, status):
     args = list(_args(ws_bytes=1 << 20))
