@@ -379,12 +379,13 @@ __global__ void __launch_bounds__(kPThreads) mfma_product_kernel(MfmaParams p) {
     // its last byte; those bytes are never used
     const __amdgpu_buffer_rsrc_t r_ws = buffer_of(p.w_scales, ((int64_t)p.N * KB + 15) & ~(int64_t)15);
     const __amdgpu_buffer_rsrc_t r_ac = buffer_of(p.a_codes, (int64_t)p.M * KH);
-    const __amdgpu_buffer_rsrc_t r_as = buffer_of(p.a_scales, (int64_t)p.M * KB);
+    // (16-byte scale windows, as for R's scales: up to 15 bytes past the
+    // array, inside the 16-byte block that holds its last byte)
+    const __amdgpu_buffer_rsrc_t r_as = buffer_of(p.a_scales, ((int64_t)p.M * KB + 15) & ~(int64_t)15);
 
     // ---- activation tile loads (rows >= M, chunks past the wave's share and
     // the K tail read zeros)
     u32x4_t act_c[CPW][MB];
-    uint32_t act_s[CPW][MB];
 #pragma unroll
     for (int c = 0; c < CPW; ++c)
 #pragma unroll
@@ -392,8 +393,19 @@ __global__ void __launch_bounds__(kPThreads) mfma_product_kernel(MfmaParams p) {
             const int m = 16 * mb + col, gc = wc0 + c;
             const bool ok = m < p.M && c < cpw && gc * kChunkK + grp * 32 < p.K;
             act_c[c][mb] = load16(r_ac, opaque(ok ? m * KH + gc * 64 + grp * 16 : kOob));
-            act_s[c][mb] = load2(r_as, opaque(ok ? m * KB + gc * 8 + grp * 2 : kOob));
         }
+    // its block scales: per m-block one 16-byte load per lane, lane
+    // PPR rl + piece taking piece `piece` of row rl's 16-byte-aligned window
+    // that holds the wave's CPW x 8 scale bytes (2-byte loads per lane
+    // touched 16 rows per instruction for 128 bytes)
+    static_assert(16 * PPR <= 64, "one load per lane covers an m-block's scale windows");
+    u32x4_t act_sw[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        const int rl = lane / PPR, piece = lane - rl * PPR, m = 16 * mb + rl;
+        const bool ok = rl < 16 && m < p.M && cpw > 0;
+        act_sw[mb] = load16(r_as, opaque(ok ? ((m * KB + wc0 * 8) & ~15) + 16 * piece : kOob));
+    }
 
     // ---- block scales of R for this wave's chunks, every row of the range:
     // per row the 16-byte-aligned window of PPR pieces that holds the wave's
@@ -471,15 +483,27 @@ __global__ void __launch_bounds__(kPThreads) mfma_product_kernel(MfmaParams p) {
         return *reinterpret_cast<const uint16_t *>(reinterpret_cast<const uint8_t *>(my_sc) + byte);
     };
 
+    // ---- the activation's scale windows, staged in this wave's partial-sum
+    // slots (first written after its first row block)
+    uint8_t *my_as = reinterpret_cast<uint8_t *>(s_part + (size_t)wave * RBW * MB * 64);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+        if (lane < 16 * PPR) reinterpret_cast<u32x4_t *>(my_as)[mb * 64 + lane] = act_sw[mb];
+
     // ---- dequantise the activation tile (its loads are the oldest in flight)
     u32x4_t act[CPW][4][MB];           // exact f16 A operands, K-step d of chunk c
 #pragma unroll
     for (int c = 0; c < CPW; ++c)
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-            // zero codes (the loads that read nothing) give zero operands
-            const float s_lo = __builtin_amdgcn_cvt_f32_fp8(act_s[c][mb], 0);
-            const float s_hi = __builtin_amdgcn_cvt_f32_fp8(act_s[c][mb], 1);
+            // scale bytes 2 grp and 2 grp + 1 of chunk c of row m; zero where
+            // the codes read nothing (the window may hold any byte there)
+            const int m = 16 * mb + col, gc = wc0 + c;
+            const bool ok = m < p.M && c < cpw && gc * kChunkK + grp * 32 < p.K;
+            const int byte = (mb * 64 + col * PPR) * 16 + ((m * KB + wc0 * 8) & 15) + c * 8 + grp * 2;
+            const uint32_t sp = ok ? *reinterpret_cast<const uint16_t *>(my_as + byte) : 0u;
+            const float s_lo = __builtin_amdgcn_cvt_f32_fp8(sp, 0);
+            const float s_hi = __builtin_amdgcn_cvt_f32_fp8(sp, 1);
             const half2_t m_lo = mantissa_pair(s_lo), m_hi = mantissa_pair(s_hi);
 #pragma unroll
             for (int d = 0; d < 4; ++d)
