@@ -361,7 +361,6 @@ __global__ void __launch_bounds__(kPThreads) mfma_product_kernel(MfmaParams p) {
     // LDS: the waves' partial sums [wave][row block][mb][64 lanes], then each
     // wave's block scales of R [wave][row][PPR 16-byte pieces]
     extern __shared__ float4_t s_part[];
-    constexpr int SCL = (RBW * 16 * PPR + 63) / 64;    // scale loads per lane
     u32x4_t *s_sc = reinterpret_cast<u32x4_t *>(s_part + (size_t)kPWaves * RBW * MB * 64);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int col = lane & 15, grp = lane >> 4;
@@ -407,20 +406,7 @@ __global__ void __launch_bounds__(kPThreads) mfma_product_kernel(MfmaParams p) {
         act_sw[mb] = load16(r_as, opaque(ok ? ((m * KB + wc0 * 8) & ~15) + 16 * piece : kOob));
     }
 
-    // ---- block scales of R for this wave's chunks, every row of the range:
-    // per row the 16-byte-aligned window of PPR pieces that holds the wave's
-    // (at most CPW x 8) scale bytes; SCL 16-byte loads per lane
     const int pb = rb_begin, nrb = rb_end - rb_begin;     // 1 .. RBW row blocks
-    u32x4_t sc_v[SCL];
-#pragma unroll
-    for (int t = 0; t < SCL; ++t) {
-        const int idx = lane + 64 * t;
-        const int rl = idx / PPR, piece = idx - rl * PPR;
-        const int n = pb * 16 + rl;
-        const bool ok = rl < nrb * 16 && n < p.N && cpw > 0;
-        const int a0 = (n * KB + wc0 * 8) & ~15;
-        sc_v[t] = load16(r_ws, opaque(ok ? a0 + 16 * piece : kOob));
-    }
 
     // correction words of this wave: w = s + S (wave + 8 j)
     const int nws = p.W > s ? (p.W - s + p.S - 1) / p.S : 0;
@@ -452,7 +438,16 @@ __global__ void __launch_bounds__(kPThreads) mfma_product_kernel(MfmaParams p) {
     // are still being requested.  Every index is a constant, so each wait
     // counts exactly the loads issued after the ones it needs.
     u32x4_t cw[RBW][CPW];
+    // block scales of R, requested with the row block's codes: per row the
+    // 16-byte-aligned window of PPR pieces that holds the wave's (at most
+    // CPW x 8) scale bytes, lane PPR row + piece
+    u32x4_t scv[RBW];
     auto load_rb = [&](int rbl) {
+        {
+            const int rl = lane / PPR, piece = lane - rl * PPR, nr = (pb + rbl) * 16 + rl;
+            const bool ok = rl < 16 && rbl < nrb && nr < p.N && cpw > 0;
+            scv[rbl] = load16(r_ws, opaque(ok ? ((nr * KB + wc0 * 8) & ~15) + 16 * piece : kOob));
+        }
         const int n = (pb + rbl) * 16 + col;
 #pragma unroll
         for (int c = 0; c < CPW; ++c) {
@@ -466,14 +461,9 @@ __global__ void __launch_bounds__(kPThreads) mfma_product_kernel(MfmaParams p) {
         if (rbl < kPipe) load_rb(rbl);
     __builtin_amdgcn_sched_barrier(0);
 
-    // ---- this wave's scale windows to its own LDS region (no barrier: only
-    // this wave reads them; its scale loads are older than its code loads)
+    // this wave's scale windows go to its own LDS region, row block by row
+    // block (no barrier: only this wave reads them)
     u32x4_t *my_sc = s_sc + (size_t)wave * RBW * 16 * PPR;
-#pragma unroll
-    for (int t = 0; t < SCL; ++t) {
-        const int idx = lane + 64 * t;
-        if (idx < RBW * 16 * PPR) my_sc[idx] = sc_v[t];
-    }
     // scale pair of chunk c of row block rbl for this lane: bytes 2 grp and
     // 2 grp + 1 of the chunk's 8, shifted by the row's window alignment
     auto scale_pair = [&](int rbl, int c) -> uint32_t {
@@ -516,6 +506,7 @@ __global__ void __launch_bounds__(kPThreads) mfma_product_kernel(MfmaParams p) {
     float4_t *mine = s_part + (size_t)wave * RBW * MB * 64 + lane;
 #pragma unroll
     for (int rbl = 0; rbl < RBW; ++rbl) {
+        if (lane < 16 * PPR) my_sc[rbl * 16 * PPR + lane] = scv[rbl];
         if (rbl < nrb) {
             float4_t acc[MB][2];
 #pragma unroll
