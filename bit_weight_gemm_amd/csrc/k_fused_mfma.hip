@@ -348,9 +348,10 @@ __global__ void __launch_bounds__(kZrThreads) mfma_zreduce_kernel(MfmaParams p) 
 // [q ncs / 8, (q + 1) ncs / 8) of the slice for every row block of the range:
 // its activation tile (those chunks, every K-step, every m-block) lives in
 // registers for the whole launch, so the stream of R meets no LDS read.
-// The range is at most RBW row blocks.  The wave requests its activation and
-// scales first, then its code loads of R kPipe row blocks ahead of the row
-// block it computes (CPW 16-byte loads per row block).  A slot with no work
+// The range is at most RBW row blocks.  The wave requests its activation
+// (codes and scales) first, then the code loads and the block-scale window of
+// R kPipe row blocks ahead of the row block it computes (CPW + 1 16-byte
+// loads per row block).  A slot with no work
 // (row block past the range, chunk past the wave's share) loads zeros
 // through an out-of-range buffer offset, so every path issues the same loads
 // and the hardware wait counts stay exact.
