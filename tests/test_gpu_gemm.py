@@ -93,7 +93,11 @@ def test_every_batch_size_ragged(M):
                                      # LDS (64-block lanes x rows of 6, 8, 12 and 16)
                                      (2, 3072, 500, 40), (2, 4096, 500, 40),
                                      (2, 6144, 300, 33), (1, 8192, 300, 100),
-                                     (1, 12288, 200, 64)])
+                                     (1, 12288, 200, 64),
+                                     # matrix cores at tiny K: scale windows reaching past
+                                     # the few scale bytes of each row and of the arrays
+                                     (3, 32, 17, 3), (32, 32, 40, 8), (5, 64, 16, 0),
+                                     (20, 96, 33, 40)])
 def test_edge_shapes(M, K, N, r):
     d = wl.make_inputs(M, K, N, r, seed=M * 1000 + N)
     y_ref = oracle.gemm_lowrank(d["x"], d["wcode"], d["wscales"], d["g"], d["V"], d["U"],
