@@ -26,30 +26,47 @@ struct GemmArgs {
     // a_scales of the same call); only for schedules whose z has a launch
     uint8_t *qa_codes = nullptr;
     uint8_t *qa_scales = nullptr;
+    // if set: ws is the matrix-core area itself (a sub-call of the
+    // separate-launch schedule), not a whole workspace
+    bool ws_is_mfma_area = false;
 };
 
-// Workspace layout (byte offsets).
-//   [0, 4)            epoch of the one-launch schedules (uint32)
-//   [256, 256 + 4 G)  one "seen" flag per workgroup of a one-launch call
-//   [64 KiB, ...)     z as (fp32 value | 32-bit epoch tag << 32) pairs [M][Rpad]
-//   then              z as plain fp32 [M][Rpad] for the two-launch schedule (a
-//                     separate area, so plain floats are never read as tags)
-//   then (M <= 2)     the vector-ALU product's correction operands: z split
-//                     into bf16 high and low parts, laid out per lane
-//                     [M][ceil(Rpad / 512)][64 lanes][4][high, low] (bf16 pairs)
-//   then (256-aligned) the matrix-core schedule's area: z slice partials,
-//                     per-word counters, z/g operands, K-slice partials of y
-//                     and per-row-block counters (sized by mfma_ws_bytes)
-//   then (256-aligned, r > 0) the separate-launch schedule's fp32 product [M][N]
-//                     and its r = 0 product's split-K partials
+// Workspace layout (byte offsets).  The first 192 KiB are fixed for every
+// shape, so that no call of one shape can write over the counters, flags or
+// tagged values another shape relies on (one workspace may serve calls of
+// different shapes, one after the other):
+//   [0, 4)                 epoch of the one-launch schedules (uint32)
+//   [256, 256 + 4 G)       one "seen" flag per workgroup of a one-launch call
+//                          (G <= kGemvMaxWorkgroups + 1)
+//   [kWsZcntOffset, 64 KiB) the matrix-core z launch's per-word arrival
+//                          counters (at most kWsZcntMax words), zero between calls
+//   [64 KiB, 192 KiB)      z as (fp32 value | 32-bit epoch tag << 32) words of
+//                          the one-launch vector schedule: one copy per XCD,
+//                          [8][MM <= 2][rpad <= 1024]
+//   [192 KiB, ...)         the areas of the shape, in this order:
+//     r > 0: z as plain fp32 [M][Rpad] (two-launch schedule)
+//     r > 0, M <= 2: the vector product's correction operands: z split into
+//            bf16 high and low parts, laid out per lane
+//            [M][ceil(Rpad / 512)][64 lanes][4][high, low] (bf16 pairs)
+//     (256-aligned) the matrix-core schedule's area: z slice partials, z
+//            operands, K-slice partials of y (sized by mfma_ws_bytes)
+//     (256-aligned, r > 0) the separate-launch schedule's fp32 product [M][N]
+//            and its r = 0 product's split-K partials
 constexpr int kGemvMaxWorkgroups = 8192;
 constexpr size_t kWsHeaderBytes = 64 * 1024;
+constexpr size_t kWsZcntOffset = 34 * 1024;
+constexpr int kWsZcntMax = (int)((kWsHeaderBytes - kWsZcntOffset) / 4);
+constexpr int kZtCopies = 8;                       // one tagged copy of z per XCD
+constexpr int kZtMaxRows = 2, kZtMaxRank = 1024;
+constexpr size_t kWsZtOffset = kWsHeaderBytes;
+constexpr size_t kWsZtBytes = (size_t)8 * kZtCopies * kZtMaxRows * kZtMaxRank;
+constexpr size_t kWsAreaOffset = kWsZtOffset + kWsZtBytes;    // 192 KiB
+static_assert(256 + 4 * (kGemvMaxWorkgroups + 1) <= kWsZcntOffset, "seen flags fit the header");
 __host__ __device__ inline int rpad32(int r) { return (r + 31) / 32 * 32; }
 inline size_t ws_epoch_offset() { return 0; }
 inline size_t ws_seen_offset() { return 256; }
-inline size_t ws_zt_offset() { return kWsHeaderBytes; }
-inline size_t ws_zt_bytes(int M, int r) { return (size_t)8 * (size_t)M * (size_t)rpad32(r); }
-inline size_t ws_zf_offset(int M, int r) { return ws_zt_offset() + ws_zt_bytes(M, r); }
+inline size_t ws_zt_offset() { return kWsZtOffset; }
+inline size_t ws_zf_offset(int, int) { return kWsAreaOffset; }
 inline size_t ws_zf_bytes(int M, int r) { return (size_t)4 * (size_t)M * (size_t)rpad32(r); }
 inline size_t ws_zop_offset(int M, int r) { return ws_zf_offset(M, r) + ws_zf_bytes(M, r); }
 __host__ __device__ inline int zop_rounds(int r) { return (rpad32(r) + 511) / 512; }
@@ -57,7 +74,7 @@ inline size_t ws_zop_bytes(int M, int r) {
     return M <= 2 ? (size_t)M * (size_t)zop_rounds(r) * 2048 : 0;
 }
 inline size_t ws_mfma_offset(int M, int r) {
-    return r > 0 ? (ws_zop_offset(M, r) + ws_zop_bytes(M, r) + 255) / 256 * 256 : 0;
+    return r > 0 ? (ws_zop_offset(M, r) + ws_zop_bytes(M, r) + 255) / 256 * 256 : kWsAreaOffset;
 }
 bool mfma_supported(int M, int N, int K, int r);     // shapes the matrix-core schedule handles
 size_t mfma_ws_bytes(int M, int N, int K, int r);    // its workspace area (0 if none is needed)
@@ -70,10 +87,12 @@ inline size_t ws_g0_offset(int M, int N, int K, int r) {
     return (ws_yf_offset(M, N, K, r) + (size_t)4 * (size_t)M * (size_t)N + 255) / 256 * 256;
 }
 // Workspace for every schedule of the shape: nothing for r = 0 unless the
-// matrix-core schedule splits K.
+// matrix-core schedule splits K (then the fixed part as well, so that the
+// partials never touch another shape's counters).
 inline size_t ws_total_bytes(int M, int N, int K, int r) {
-    return r > 0 ? ws_g0_offset(M, N, K, r) + mfma_ws_bytes(M, N, K, 0)
-                 : ws_mfma_offset(M, r) + mfma_ws_bytes(M, N, K, r);
+    if (r > 0) return ws_g0_offset(M, N, K, r) + mfma_ws_bytes(M, N, K, 0);
+    const size_t b = mfma_ws_bytes(M, N, K, 0);
+    return b > 0 ? ws_mfma_offset(M, 0) + b : 0;
 }
 
 hipError_t launch_pack_signs(const int8_t *signs, int64_t rows, int64_t cols, uint32_t *packed,

@@ -195,6 +195,7 @@ hipError_t launch_gemm_composed(const GemmArgs &a, bool mfma_correction, hipStre
     if (a.r > 0) {
         g0.ws = static_cast<char *>(a.ws) + ws_g0_offset(a.M, a.N, a.K, a.r);
         g0.ws_bytes = a.ws_bytes - ws_g0_offset(a.M, a.N, a.K, a.r);
+        g0.ws_is_mfma_area = true;
     }
     hipError_t e;
     if (a.M >= 3 && mfma_supported(a.M, a.N, a.K, 0)) {

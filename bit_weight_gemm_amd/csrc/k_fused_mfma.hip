@@ -8,7 +8,7 @@
 // batch is padded to 16 rows (M <= 16) or 32 rows.  The work is one to four
 // launches on one stream:
 //
-// 1. mfma_z_kernel (r > 0) computes z/g = (alpha/g) (.) (x . V+-) with
+// 1. mfma_z_kernel (r > 0) computes z = alpha (.) (x . V+-) with
 //    v_mfma_f32_16x16x32_bf16.  The bf16 activation x is exact as an operand;
 //    the +-1 operand is built in registers from V's sign words.  Workgroups
 //    own (one 32-bit word of V, one K-slice).  With fewer than 8 K-slices the
@@ -29,14 +29,16 @@
 //      v_mfma_f32_16x16x32_f16.  One v_cvt_scalef32_pk_f16_fp4 per byte
 //      applies the power of two of the E4M3 block scale, and a packed f16
 //      multiply applies its mantissa.  Both steps are exact.
-//    - Each wave's share of the correction, (z/g) . U+- over rank words
-//      w = slice, slice + S, ..., initialises its accumulators.
+//    - Each wave's share of the correction, z . U+- over rank words
+//      w = slice, slice + S, ..., goes to accumulators of its own; the
+//      product's accumulators are scaled by g before the two meet (g P + C,
+//      so that y is right for every finite g, g = 0 included).
 //    - The waves' sums meet in per-wave LDS slots.  With one K-slice the
 //      workgroup stores y; otherwise it stores its slice's partial sums.
 //
-// 3. mfma_epilogue_kernel (K split in S > 1 slices) sums the slices,
-//    multiplies by g and stores bf16 (a launch of its own: summing them in
-//    the product by the last slice to arrive measured slower).
+// 3. mfma_epilogue_kernel (K split in S > 1 slices) sums the slices and
+//    stores bf16 (a launch of its own: summing them in the product by the
+//    last slice to arrive measured slower).
 //
 // MFMA operand layout of the 16x16x32 forms (checked on the device):
 //   A[i][k] sits in lane i + 16 (k / 8), element k % 8.
@@ -111,7 +113,7 @@ struct MfmaParams {
     int zs, zsteps;             // K-slices and K-steps per slice
     float *zpart;               // [zs][W][MB][64 lanes][8] (correction A-operand order)
     uint32_t *zcnt;             // [W]
-    uint32_t *zA;               // [W][MB][2 hi/lo][64 lanes][4] bf16 pairs of z / g
+    uint32_t *zA;               // [W][MB][2 hi/lo][64 lanes][4] bf16 pairs of z
     float *zf;                  // if set: plain fp32 z [M][rpad] as well (separate-launch use)
     uint8_t *qa_codes;          // if set: the z kernel also quantises x (codes, scales)
     uint8_t *qa_scales;
@@ -174,7 +176,7 @@ __device__ __forceinline__ uint32_t arrive(uint32_t *cnt) {
     return __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// The slices' sum for word w times alpha_i / g as bf16 high + low parts into
+// The slices' sum for word w times alpha_i as bf16 high + low parts into
 // the correction operand (and plain fp32 z into zf when asked).  Thread
 // (mb, l, j) sums one value; lanes j and j + 4 of a group of 8 threads form
 // the (index, index + 16) pair of dword j & 3.  COHERENT: the partials were
@@ -183,7 +185,6 @@ __device__ __forceinline__ uint32_t arrive(uint32_t *cnt) {
 constexpr int kZSumBatch = 16;          // slice partials loaded at once
 template <int MB, bool COHERENT>
 __device__ __forceinline__ void z_finish(const MfmaParams &p, int w, int first = 0, int step = kZThreads) {
-    const float ginv = 1.0f / p.g;
     for (int idx = first + (int)threadIdx.x; idx < MB * 64 * 8; idx += step) {
         const int j = idx & 7, l = (idx >> 3) & 63, mb = idx >> 9;
         const int m = 16 * mb + (l & 15), q = l >> 4;
@@ -202,7 +203,7 @@ __device__ __forceinline__ void z_finish(const MfmaParams &p, int w, int first =
         }
         const int i = 32 * w + 4 * q + (j & 3) + 16 * (j >> 2);
         const float al = bf16_to_f32(p.alpha[i < p.r ? i : p.r - 1]);
-        const float zz = (i < p.r && m < p.M) ? sum * al * ginv : 0.0f;
+        const float zz = (i < p.r && m < p.M) ? sum * al : 0.0f;
         if (p.zf && i < p.r && m < p.M) p.zf[(int64_t)m * p.rpad + i] = sum * al;
         const uint32_t zh = f32_to_bf16_rne(zz);
         const uint32_t zl = f32_to_bf16_rne(zz - bf16_to_f32(zh));
@@ -217,7 +218,7 @@ __device__ __forceinline__ void z_finish(const MfmaParams &p, int w, int first =
 }
 
 // =====================================================================
-// launch 1: z / g
+// launch 1: z
 // =====================================================================
 // Workgroup (w, s): the 32 indices of word w of V over K-slice s (at most
 // 8 kZStepsPerWave K-steps), every row m.  Wave q takes the slice's K-steps
@@ -228,7 +229,7 @@ __device__ __forceinline__ void z_finish(const MfmaParams &p, int w, int first =
 // z[m][4q + j] (j < 4) and z[m][4q + j - 4 + 16] (j >= 4).  The slice's
 // partial goes to the workspace in that layout; the last workgroup to arrive
 // for the word (a counter, never a wait) sums the slices, scales by
-// alpha_i / g and stores bf16 high and low parts.
+// alpha_i and stores bf16 high and low parts.
 template <int MB>
 __global__ void __launch_bounds__(kZThreads) mfma_z_kernel(MfmaParams p) {
     __shared__ float4_t s_acc[kZWaves][MB * 2][64];
@@ -509,17 +510,18 @@ __global__ void __launch_bounds__(kPThreads) mfma_product_kernel(MfmaParams p) {
     for (int rbl = 0; rbl < RBW; ++rbl) {
         if (lane < 16 * PPR) my_sc[rbl * 16 * PPR + lane] = scv[rbl];
         if (rbl < nrb) {
-            float4_t acc[MB][2];
+            float4_t acc[MB][2], cacc[MB];
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb) acc[mb][0] = acc[mb][1] = float4_t{0.f, 0.f, 0.f, 0.f};
+            for (int mb = 0; mb < MB; ++mb)
+                acc[mb][0] = acc[mb][1] = cacc[mb] = float4_t{0.f, 0.f, 0.f, 0.f};
             if (has_corr) {
                 const uint32_t t = uw[rbl];
                 const u32x4_t bv = {sign_pair_bf16(t, 4 * grp + 0), sign_pair_bf16(t, 4 * grp + 1),
                                     sign_pair_bf16(t, 4 * grp + 2), sign_pair_bf16(t, 4 * grp + 3)};
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb) {
-                    acc[mb][0] = mfma_bf16(zz[mb][0], bv, acc[mb][0]);
-                    acc[mb][1] = mfma_bf16(zz[mb][1], bv, acc[mb][1]);
+                    cacc[mb] = mfma_bf16(zz[mb][0], bv, cacc[mb]);
+                    cacc[mb] = mfma_bf16(zz[mb][1], bv, cacc[mb]);
                 }
             }
 #pragma unroll
@@ -540,7 +542,8 @@ __global__ void __launch_bounds__(kPThreads) mfma_product_kernel(MfmaParams p) {
                 }
             }
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb) mine[(rbl * MB + mb) * 64] = acc[mb][0] + acc[mb][1];
+            for (int mb = 0; mb < MB; ++mb)
+                mine[(rbl * MB + mb) * 64] = p.g * (acc[mb][0] + acc[mb][1]) + cacc[mb];
         }
         // keep each row block's dequantisation next to its MFMAs
         __builtin_amdgcn_sched_barrier(0);
@@ -585,7 +588,7 @@ __global__ void __launch_bounds__(kPThreads) mfma_product_kernel(MfmaParams p) {
             if (n < p.N) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    if (m0 + e < p.M) store_y(p, (int64_t)(m0 + e) * p.N + n, p.g * v[e]);
+                    if (m0 + e < p.M) store_y(p, (int64_t)(m0 + e) * p.N + n, v[e]);
             }
         }
     } else {
@@ -599,7 +602,7 @@ __global__ void __launch_bounds__(kPThreads) mfma_product_kernel(MfmaParams p) {
 }
 
 // =====================================================================
-// launch 3 (K split in S > 1 slices): sum the slices, times g, bf16
+// launch 3 (K split in S > 1 slices): sum the slices, bf16
 // =====================================================================
 // Thread (row block, m-block, lane) holds the D-layout element quadruple
 // (m = 16 mb + 4 (lane / 16) + e, n = 16 rb + lane % 16).
@@ -623,7 +626,7 @@ __global__ void __launch_bounds__(256) mfma_epilogue_kernel(MfmaParams p) {
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-        if (m0 + e < p.M) store_y(p, (int64_t)(m0 + e) * p.N + n, p.g * v[e]);
+        if (m0 + e < p.M) store_y(p, (int64_t)(m0 + e) * p.N + n, v[e]);
 }
 
 // =====================================================================
@@ -634,7 +637,7 @@ struct MfmaPlan {
     int mb, W, zs, zsteps, chunks, S, cps, RB, Gs, grid, rbw, cpw;
     size_t lds;
     // workspace offsets inside the matrix-core area
-    size_t off_zpart, off_zcnt, off_za, off_ypart, bytes;
+    size_t off_zpart, off_za, off_ypart, bytes;
 };
 
 size_t align256(size_t b) { return (b + 255) / 256 * 256; }
@@ -678,9 +681,7 @@ MfmaPlan mfma_plan(int M, int N, int K, int r) {
     // workspace
     size_t off = 0;
     q.off_zpart = off;
-    off += (size_t)q.zs * q.W * q.mb * 64 * 8 * 4;
-    q.off_zcnt = off;
-    off = align256(off + (size_t)q.W * 4);
+    off = align256(off + (size_t)q.zs * q.W * q.mb * 64 * 8 * 4);
     q.off_za = off;
     off += (size_t)q.W * q.mb * 2 * 64 * 16;
     q.off_ypart = off;
@@ -743,12 +744,14 @@ MfmaParams mfma_params(const GemmArgs &a, MfmaPlan &q_out) {
     p.RB = q.RB;
     p.Gs = q.Gs;
     if (q.bytes > 0) {
-        char *ws = static_cast<char *>(a.ws) + ws_mfma_offset(a.M, a.r);
+        char *ws = static_cast<char *>(a.ws) + (a.ws_is_mfma_area ? 0 : ws_mfma_offset(a.M, a.r));
         p.zpart = reinterpret_cast<float *>(ws + q.off_zpart);
-        p.zcnt = reinterpret_cast<uint32_t *>(ws + q.off_zcnt);
         p.zA = reinterpret_cast<uint32_t *>(ws + q.off_za);
         p.ypart = reinterpret_cast<float *>(ws + q.off_ypart);
     }
+    // the z launch's per-word counters sit at a fixed place of the header
+    // (r > 0 calls always get a whole workspace)
+    if (a.r > 0) p.zcnt = reinterpret_cast<uint32_t *>(static_cast<char *>(a.ws) + kWsZcntOffset);
     p.rpad = rpad32(a.r);
     return p;
 }
@@ -777,7 +780,7 @@ hipError_t launch_gemm_mfma(const GemmArgs &a, hipStream_t stream) {
         // launch finishes each word: there a launch boundary costs less than
         // the exchange of partials through a counter inside one launch
         // (measured: 8 and 14 slices gain, 5 loses).
-        p.zsplit = q.zs >= kZSplitMinSlices ? 1 : 0;
+        p.zsplit = (q.zs >= kZSplitMinSlices || q.W > kWsZcntMax) ? 1 : 0;
         if (q.mb == 1) {
             hipLaunchKernelGGL(mfma_z_kernel<1>, dim3(q.W * q.zs), dim3(kZThreads), 0, stream, p);
             if (p.zsplit) hipLaunchKernelGGL(mfma_zreduce_kernel<1>, dim3(q.W * 2), dim3(kZrThreads), 0, stream, p);

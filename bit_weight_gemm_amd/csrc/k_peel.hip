@@ -70,7 +70,7 @@ PeelLayout peel_layout(int64_t m, int64_t n, int r) {
     L.bvec = take((size_t)r * 8);
     L.gram = take((size_t)r * r * 8);
     L.sol = take((size_t)r * 8);
-    L.bad = take(4);
+    L.bad = take((size_t)r * 4);      // one "dropped" flag per coefficient
     L.total = o;
     return L;
 }
@@ -359,15 +359,19 @@ peel_gram_kernel(const uint32_t *__restrict__ ubits, const uint32_t *__restrict_
 // diagonal block in LDS and solves the rows below it (L21 = A21 L11^-T, one
 // thread per row), then a tiled update A22 -= L21 L21^T runs over many
 // workgroups.  A last workgroup solves L y = b, L^T x = y.  A pivot below
-// 1e-6 m n (every diagonal entry of G is m n; the sign terms are linearly
-// dependent) sets a flag, and then alpha keeps the greedy coefficients.
+// 1e-6 m n (every diagonal entry of G is m n) means that term's sign outer
+// product lies in the span of the earlier kept ones (e.g. a term found
+// twice): the term is dropped from the solve (its column of L is zero, its
+// coefficient 0), which leaves the span of the design matrix, and so the
+// least-squares minimum, unchanged -- the refit is still a least-squares
+// minimiser, the one with the dropped coefficients at zero.
 constexpr int kChol = 32;
 
 __global__ void __launch_bounds__(1024)
-peel_chol_panel_kernel(double *__restrict__ G, int r, int k0, double G_diag, int *__restrict__ bad) {
+peel_chol_panel_kernel(double *__restrict__ G, int r, int k0, double G_diag, int *__restrict__ dropped) {
     __shared__ double L[kChol][kChol + 1];
+    __shared__ int s_drop[kChol];
     const int kb = r - k0 < kChol ? r - k0 : kChol;
-    if (k0 == 0 && threadIdx.x == 0) *bad = 0;
     for (int e = threadIdx.x; e < kb * kb; e += 1024) {
         const int a = e / kb, c = e % kb;
         L[a][c] = G[(int64_t)(k0 + a) * r + k0 + c];
@@ -377,11 +381,14 @@ peel_chol_panel_kernel(double *__restrict__ G, int r, int k0, double G_diag, int
         if (threadIdx.x == 0) {
             const double d = L[c][c];
             const bool ok = d > 1e-6 * G_diag;
-            if (!ok) *bad = 1;
+            s_drop[c] = ok ? 0 : 1;
+            dropped[k0 + c] = ok ? 0 : 1;
             L[c][c] = ok ? sqrt(d) : 1.0;
         }
         __syncthreads();
-        for (int a = c + 1 + (int)threadIdx.x; a < kb; a += 1024) L[a][c] /= L[c][c];
+        // a dropped column is zero below the diagonal, so no later column
+        // subtracts anything for it
+        for (int a = c + 1 + (int)threadIdx.x; a < kb; a += 1024) L[a][c] = s_drop[c] ? 0.0 : L[a][c] / L[c][c];
         __syncthreads();
         const int rem = kb - c - 1;
         for (int e = threadIdx.x; e < rem * rem; e += 1024) {
@@ -406,7 +413,7 @@ peel_chol_panel_kernel(double *__restrict__ G, int r, int k0, double G_diag, int
                 double v = x[c];
 #pragma unroll
                 for (int cc = 0; cc < c; ++cc) v -= x[cc] * L[c][cc];
-                x[c] = v / L[c][c];
+                x[c] = s_drop[c] ? 0.0 : v / L[c][c];
             }
         }
 #pragma unroll
@@ -450,25 +457,26 @@ peel_chol_update_kernel(double *__restrict__ G, int r, int k0) {
 // L y = b and L^T x = y (one workgroup), then the outputs.
 __global__ void __launch_bounds__(1024)
 peel_trisolve_kernel(const double *__restrict__ G, const double *__restrict__ b, double *__restrict__ x,
-                     int r, const int *__restrict__ bad, const float *__restrict__ ag,
+                     int r, const int *__restrict__ dropped, const float *__restrict__ ag,
                      float *__restrict__ alpha, float *__restrict__ alpha_greedy) {
     for (int t = threadIdx.x; t < r; t += 1024) x[t] = b[t];
     __syncthreads();
+    // a dropped term's unknown is 0 in both passes (its column of L is zero,
+    // so it never reaches the other unknowns of the forward pass)
     for (int i = 0; i < r; ++i) {
-        if (threadIdx.x == 0) x[i] /= G[(int64_t)i * r + i];
+        if (threadIdx.x == 0) x[i] = dropped[i] ? 0.0 : x[i] / G[(int64_t)i * r + i];
         __syncthreads();
         for (int t = i + 1 + threadIdx.x; t < r; t += 1024) x[t] -= G[(int64_t)t * r + i] * x[i];
         __syncthreads();
     }
     for (int i = r - 1; i >= 0; --i) {
-        if (threadIdx.x == 0) x[i] /= G[(int64_t)i * r + i];
+        if (threadIdx.x == 0) x[i] = dropped[i] ? 0.0 : x[i] / G[(int64_t)i * r + i];
         __syncthreads();
         for (int t = threadIdx.x; t < i; t += 1024) x[t] -= G[(int64_t)i * r + t] * x[i];
         __syncthreads();
     }
-    const bool dependent = *bad != 0;
     for (int i = threadIdx.x; i < r; i += 1024) {
-        alpha[i] = dependent ? ag[i] : (float)x[i];
+        alpha[i] = (float)x[i];
         if (alpha_greedy) alpha_greedy[i] = ag[i];
     }
 }

@@ -161,7 +161,9 @@ biloco_status biloco_quant_weight_workspace_bytes(int64_t N, int64_t K, size_t *
  * decision can differ from another summation order's where |(R v)_a| or
  * |(R^T u)_k| is within rounding of 0.  If the sign terms are linearly
  * dependent (a Cholesky pivot of G falls below 1e-6 m n, e.g. a term found
- * twice), alpha holds the greedy coefficients.
+ * twice), least squares has many minimisers: each term whose outer product
+ * lies in the span of the earlier ones is dropped from the solve (its alpha
+ * is 0) and alpha is the least-squares minimiser of the others.
  * About (5 T + 1) r + 4 launches on `stream`; no two of the output and
  * input arrays may overlap. */
 biloco_status biloco_peel_decompose(const float *W, int64_t m, int64_t n, int32_t r, int32_t T,

@@ -22,9 +22,13 @@ Readings where the pages leave a step open:
     G_ij = (u_i . u_j)(v_i . v_j) and b_i = u_i^T W v_i, and the returned
     residual is W - U diag(a) V^T with the refit coefficients;
   * if the r sign outer products are linearly dependent (G singular, e.g. a
-    term found twice), the refit keeps the greedy coefficients.
+    term found twice), least squares has many minimisers; the oracle returns
+    the one of minimum norm (the pseudo-inverse solution of G a = b, equal to
+    the minimum-norm least-squares solution of the explicit design matrix,
+    since b lies in the range of G).
 
-Matrix products (numpy @) are the only library primitive used.
+Matrix products (numpy @) and the linear solves of the refit (numpy.linalg
+solve, and lstsq for a singular G) are the only library primitives used.
 """
 from __future__ import annotations
 
@@ -85,7 +89,8 @@ def peel(W: np.ndarray, r: int, T: int, v_init: np.ndarray, trace: bool = False)
     G = (U.T @ U) * (V.T @ V)
     b = np.einsum("ai,ai->i", U, Wd @ V)
     if np.linalg.matrix_rank(G) < r:
-        alpha = ag.copy()
+        # singular values below matrix_rank's own tolerance count as zero
+        alpha = np.linalg.lstsq(G, b, rcond=r * np.finfo(np.float64).eps)[0]
     else:
         alpha = np.linalg.solve(G, b)
     out = {"U": U, "V": V, "alpha_greedy": ag, "alpha": alpha,

@@ -2,8 +2,11 @@
 
 Where every sign decision of the oracle's run has a clear margin (planted
 sign structure), the GPU must find the same signs bit for bit and the same
-coefficients and residual to fp32 accuracy, including a run whose terms come
-out dependent (the refit then keeps the greedy coefficients).  On plain
+coefficients and residual to fp32 accuracy.  Where the terms come out
+linearly dependent (a term found twice), least squares has many minimisers:
+the GPU drops the repeated terms from the solve (coefficient 0), the oracle
+returns the minimum-norm minimiser, so the refit is checked for what makes
+it a minimiser (the normal equations and the residual norm).  On plain
 random weights, up to the full decode weight shape, the decisions are not all
 clear, so the GPU result is checked for what defines it, term by term from
 its own earlier terms: each v is the sign of R^T u wherever that is clear of
@@ -62,9 +65,58 @@ def test_planted_exact(case):
     np.testing.assert_array_equal(g["V"], ref["V"])
     scale = np.abs(ref["alpha_greedy"]).max()
     np.testing.assert_allclose(g["alpha_greedy"], ref["alpha_greedy"], rtol=1e-5, atol=1e-6 * scale)
-    np.testing.assert_allclose(g["alpha"], ref["alpha"], rtol=1e-5, atol=1e-6 * scale)
-    tol = 1e-5 * (np.abs(W).max() + np.abs(ref["alpha"]).sum())
-    assert np.abs(g["R"] - ref["R"]).max() <= tol
+    U, V = ref["U"], ref["V"]
+    G = (U.T @ U) * (V.T @ V)
+    if np.linalg.matrix_rank(G) == r:
+        np.testing.assert_allclose(g["alpha"], ref["alpha"], rtol=1e-5, atol=1e-6 * scale)
+        tol = 1e-5 * (np.abs(W).max() + np.abs(ref["alpha"]).sum())
+        assert np.abs(g["R"] - ref["R"]).max() <= tol
+    else:
+        _check_minimiser(W, g, ref)
+
+
+def _check_minimiser(W, g, ref):
+    """The GPU refit is a least-squares minimiser for the fixed signs: it
+    solves the normal equations, its residual norm is the oracle's (the
+    minimum), and the returned residual is W - U diag(alpha) V^T."""
+    Wd = W.astype(np.float64)
+    U, V = ref["U"], ref["V"]
+    G = (U.T @ U) * (V.T @ V)
+    b = np.einsum("ai,ai->i", U, Wd @ V)
+    np.testing.assert_allclose(G @ g["alpha"], b, rtol=1e-5, atol=1e-5 * np.abs(b).max())
+    res_gpu = np.sum((Wd - (U * g["alpha"]) @ V.T) ** 2)
+    res_ref = np.sum(ref["R"] ** 2)
+    assert res_gpu == pytest.approx(res_ref, rel=1e-5, abs=1e-6 * np.sum(Wd ** 2))
+    Rref = Wd - (U * g["alpha"]) @ V.T
+    assert np.abs(g["R"] - Rref).max() <= 1e-5 * (np.abs(W).max() + np.abs(g["alpha"]).sum())
+
+
+def test_repeated_term_golden():
+    """The hand-derived 4 x 4 case whose third term repeats the first: the
+    signs and greedy coefficients are exact; the refit is a minimiser (the
+    GPU drops the repeat: alpha = (33/32, 27/32, 0)); the greedy one is not."""
+    import os
+    vals = {}
+    with open(os.path.join(os.path.dirname(__file__), "golden", "peel_repeated_term.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                k, rest = line.split(None, 1)
+                vals[k] = np.array([float(t) for t in rest.split()])
+    W = vals["W"].reshape(4, 4).astype(np.float32)
+    signs = vals["v_init"].reshape(3, 4)
+    vi = np.zeros((3, 1), np.uint32)
+    for i in range(3):
+        for k in range(4):
+            if signs[i, k] < 0:
+                vi[i, 0] |= np.uint32(1 << k)
+    ref = P.peel(W.astype(np.float64), 3, 2, P.unpack_bits_pm1(vi, 4))
+    g = _gpu_peel(W, 3, 2, vi)
+    np.testing.assert_array_equal(g["U"].T.ravel(), vals["U"])
+    np.testing.assert_array_equal(g["V"].T.ravel(), vals["V"])
+    np.testing.assert_array_equal(g["alpha_greedy"], vals["alpha_greedy"])
+    _check_minimiser(W, g, ref)
+    np.testing.assert_allclose(g["alpha"], [33 / 32, 27 / 32, 0.0], rtol=0, atol=1e-6)
 
 
 def _check_properties(W, r, T, g, terms):
@@ -91,6 +143,8 @@ def _check_properties(W, r, T, g, terms):
     if np.linalg.matrix_rank(G) == r:
         a_ref = np.linalg.solve(G, b)
         np.testing.assert_allclose(al, a_ref, rtol=1e-4, atol=1e-5 * np.abs(a_ref).max())
+    else:
+        np.testing.assert_allclose(G @ al, b, rtol=1e-4, atol=1e-5 * np.abs(b).max())
     rows = np.unique(np.linspace(0, m - 1, min(m, 64)).astype(int))
     Rref = Wd[rows] - (U[rows] * al) @ V.T
     assert np.abs(g["R"][rows] - Rref).max() <= 1e-5 * (np.abs(W).max() + np.abs(al).sum())

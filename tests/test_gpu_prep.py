@@ -190,17 +190,29 @@ def test_wquant_every_block_scale_and_ties():
     _check_wquant(np.stack(rows))
 
 
-def test_wquant_feeds_gemm():
-    # the quantiser's output is the product's residual operand (r = 0 and r > 0)
-    for cfg in (0, 1):
-        d = wl.make_config(cfg)
-        w = wl.make_residual(d["N"], d["K"], seed=11 + cfg)
-        c, s, g = _gpu_wquant(w)
-        d["wcodes_packed"], d["wscales"], d["g"] = c, s, g
-        d["wcode"] = np.stack([c & 15, c >> 4], axis=-1).reshape(d["N"], d["K"])
-        y_ref = oracle.gemm_lowrank(d["x"], d["wcode"], d["wscales"], d["g"], d["V"], d["U"],
-                                    d["alpha"])
-        p = DeviceProblem(d)
-        p.gemm()
+@pytest.mark.parametrize("shape", [("cfg", 0), ("cfg", 1), (8, 5120, 1536, 512),
+                                   (32, 13824, 640, 512), (32, 8192, 1024, 1024)],
+                         ids=["config0", "config1", "M8", "M32-K13824", "M32-r1024"])
+def test_wquant_feeds_gemm(shape):
+    # the quantiser's output (with its small and saturated block scales and
+    # outlier columns) is the product's residual operand, on every schedule:
+    # the vector schedules at M = 1 and the matrix cores at M = 8 and 32
+    if shape[0] == "cfg":
+        d = wl.make_config(shape[1])
+        seed = 11 + shape[1]
+    else:
+        M, K, N, r = shape
+        d = wl.make_inputs(M, K, N, r, seed=K + N)
+        seed = M + K
+    w = wl.make_residual(d["N"], d["K"], seed=seed, outliers=True)
+    c, s, g = _gpu_wquant(w)
+    d["wcodes_packed"], d["wscales"], d["g"] = c, s, g
+    d["wcode"] = np.stack([c & 15, c >> 4], axis=-1).reshape(d["N"], d["K"])
+    y_ref = oracle.gemm_lowrank(d["x"], d["wcode"], d["wscales"], d["g"], d["V"], d["U"],
+                                d["alpha"])
+    p = DeviceProblem(d)
+    for sched in B.biloco_schedules_for(d["M"], d["N"], d["K"], d["r"]):
+        p.y.zero_()
+        p.gemm(sched)
         torch.cuda.synchronize()
-        check_y(p.y_float(), y_ref, f"config {cfg} with quantised R")
+        check_y(p.y_float(), y_ref, f"{shape} schedule {sched} with quantised R")

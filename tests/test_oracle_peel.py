@@ -9,7 +9,10 @@
   Frobenius optimum), so the residual never grows;
 * the refit equals numpy's least-squares solve on the explicit design matrix
   of the r sign outer products, and is never worse than the greedy
-  coefficients.
+  coefficients;
+* with a term found twice (singular normal equations, golden file), the
+  refit is the minimum-norm least-squares minimiser, derived by hand, where
+  the greedy coefficients are not a minimiser at all.
 """
 import itertools
 import os
@@ -22,9 +25,9 @@ from oracle import peel as P
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
-def _golden():
+def _golden(name="peel_two_terms.txt"):
     d = {}
-    with open(os.path.join(GOLDEN, "peel_two_terms.txt")) as f:
+    with open(os.path.join(GOLDEN, name)) as f:
         for line in f:
             line = line.strip()
             if line and not line.startswith("#"):
@@ -126,3 +129,25 @@ def test_unpack_bits():
     assert np.all(s[0, 4:32] == 1) and np.all(s[0, 32:] == 1)
     s2 = P.unpack_bits_pm1(words, 64)
     assert s2[0, 63] == -1
+
+
+def test_repeated_term_refit_is_min_norm_least_squares():
+    g = _golden("peel_repeated_term.txt")
+    W = g["W"].reshape(4, 4)
+    o = P.peel(W, 3, 2, g["v_init"].reshape(3, 4))
+    np.testing.assert_array_equal(o["U"].T.ravel(), g["U"])
+    np.testing.assert_array_equal(o["V"].T.ravel(), g["V"])
+    np.testing.assert_array_equal(o["alpha_greedy"], g["alpha_greedy"])       # dyadic, exact
+    # the design matrix has two equal columns
+    U, V = o["U"], o["V"]
+    A = np.stack([np.outer(U[:, i], V[:, i]).ravel() for i in range(3)], axis=1)
+    assert np.linalg.matrix_rank(A) == 2
+    np.testing.assert_allclose(o["alpha"], g["alpha"], rtol=0, atol=1e-12)
+    # the same through another route: lstsq on the explicit design matrix
+    ref, *_ = np.linalg.lstsq(A, W.ravel(), rcond=None)
+    np.testing.assert_allclose(o["alpha"], ref, rtol=0, atol=1e-12)
+    res_ls = float(np.sum(o["R"] ** 2))
+    res_greedy = float(np.sum((W - (U * o["alpha_greedy"]) @ V.T) ** 2))
+    assert res_ls == pytest.approx(g["resid_ls"][0], rel=0, abs=1e-12)
+    assert res_greedy == pytest.approx(g["resid_greedy"][0], rel=0, abs=1e-12)
+    assert res_ls < res_greedy - 0.5                 # greedy is not a minimiser here
