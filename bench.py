@@ -243,6 +243,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", type=int, default=1, help="workload the step runs (default 1)")
+    ap.add_argument("--rank", type=int, default=None,
+                    help="run the workload at this rank instead of its own (0: the plain FP4 GEMM)")
     ap.add_argument("--schedule", type=int, default=0, help="BILOCO_SCHED_* (0 = auto)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -280,7 +282,7 @@ def main() -> int:
     B.lib()
     src_hash = source_hash()
     cfg = args.config
-    d = wl.make_config(cfg)
+    d = wl.make_config(cfg, r=args.rank)
     prob = DeviceProblem(d)
     M, N, K, r = prob.M, prob.N, prob.K, prob.r
     sched = args.schedule or B.biloco_default_schedule(M, N, K, r)

@@ -45,12 +45,14 @@ biloco_status check_shape(int32_t M, int32_t N, int32_t K, int32_t r) {
     return BILOCO_OK;
 }
 
-// Measured on MI355X: for M <= 2 the two-launch vector-ALU schedule (z
-// kernel, then the product kernel reading z complete) is faster than the
-// one-launch schedule, whose tagged z hand-off waits behind the stream of R
-// in the memory queues.  From M = 3 on, the matrix-core schedule.
+// Measured on MI355X (M = 1, K = N = 5120, r = 512, graph replay): the
+// one-launch vector-ALU schedule (side workgroups compute z while the
+// others stream R) takes 7.3 us per call and 9.1 us per quantising call,
+// against 8.8 and 9.5 us for two launches (z, then the product).  r = 0
+// has one launch either way.  From M = 3 on, the matrix-core schedule.
 int resolve_schedule(int M, int N, int K, int r) {
     if (M >= 3 && mfma_supported(M, N, K, r)) return BILOCO_SCHED_FUSED_MFMA;
+    if (r > 0 && gemv_supported(M, N, K, r)) return BILOCO_SCHED_FUSED_GEMV;
     return BILOCO_SCHED_UNFUSED;
 }
 
@@ -280,10 +282,12 @@ biloco_status biloco_gemm_lowrank_quant(const uint16_t *x_bf16, uint8_t *a_codes
                u_packed, alpha_bf16, M,       N,        K,     r,      y_bf16,
                workspace, workspace_bytes};
     const int s = schedule == BILOCO_SCHED_AUTO ? resolve_schedule(M, N, K, r) : schedule;
-    // the z launch quantises x where the schedule has one; otherwise a launch
-    // of its own comes first
-    const bool in_z = r > 0 && ((s == BILOCO_SCHED_UNFUSED && M <= 2 && gemv_supported(M, N, K, r)) ||
-                                s == BILOCO_SCHED_FUSED_MFMA);
+    // the vector-ALU schedules quantise x in the product launch (or, in the
+    // two-launch form, in the z launch); the matrix-core schedule in its z
+    // launch when r > 0; otherwise a launch of its own comes first
+    const bool gemv = (s == BILOCO_SCHED_UNFUSED && gemv_supported(M, N, K, r)) ||
+                      s == BILOCO_SCHED_FUSED_GEMV;
+    const bool in_z = gemv || (r > 0 && s == BILOCO_SCHED_FUSED_MFMA);
     hipError_t e = hipSuccess;
     if (in_z) {
         a.qa_codes = a_codes;

@@ -69,12 +69,10 @@ __device__ __forceinline__ uint32_t e2m1_mag_code(float a, float s) {
 // magnitudes order like integers), scale = E4M3(amax / 6) with a correctly
 // rounded fp32 division, codes by exact comparisons with the E2M1 midpoints
 // times the scale; one 8-byte store of the codes and one byte of scale.
-__device__ __forceinline__ void quant_act_block(const uint16_t *__restrict__ x, int64_t blk,
-                                                uint8_t *__restrict__ codes,
-                                                uint8_t *__restrict__ scales) {
-    const uint4 *src = reinterpret_cast<const uint4 *>(x + blk * 16);
-    const uint4 v0 = src[0], v1 = src[1];
-    const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+// The arithmetic of one block: its 16 bf16 values (two per dword, element
+// 2j in the low half of w[j]) -> the two dwords of E2M1 codes (element e in
+// nibble e) and the E4M3 scale byte.
+__device__ __forceinline__ uint32_t quant16(const uint32_t (&w)[8], uint32_t &lo, uint32_t &hi) {
     uint32_t amax_bits = 0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -84,7 +82,8 @@ __device__ __forceinline__ void quant_act_block(const uint16_t *__restrict__ x, 
     const float amax = bf16_to_f32(amax_bits);
     const uint32_t sb = f32_to_e4m3_rne(amax / 6.0f);
     const float s = e4m3_to_f32(sb);
-    uint32_t lo = 0, hi = 0;
+    lo = 0;
+    hi = 0;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
         const uint32_t h = (j & 1) ? (w[j >> 1] >> 16) : (w[j >> 1] & 0xFFFFu);
@@ -94,6 +93,63 @@ __device__ __forceinline__ void quant_act_block(const uint16_t *__restrict__ x, 
         if (j < 8) lo |= code << (4 * j);
         else hi |= code << (4 * (j - 8));
     }
+    return sb;
+}
+
+// The same block without a comparison per midpoint: each |x| / s is
+// Markstein's corrected quotient (q0 = |x| r, e = fma(-q0, s, |x|),
+// q = fma(e, r, q0), r = fp32(1 / s)) and the hardware FP4 conversion with
+// unit scale rounds it (nearest, ties to the even code, saturating at 6; the
+// sign of x is put back on q, so that -0 and negatives rounding to 0 keep
+// it).  The codes equal quant16's for every positive bf16 value and every
+// E4M3 scale a block can have (checked exhaustively on the CPU,
+// tests/csrc/act_code_check.c; the conversion's rounding was checked on
+// gfx950 at every E2M1 midpoint and its neighbours).  A zero scale (the
+// block is all zeros, or its amax / 6 rounds to 0) gives signed zeros.
+// elements 2j, 2j + 1 (the halves of wj) -> byte SEL of c
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4_pair(uint32_t c, uint32_t wj, float s, float r) {
+    const uint32_t b[2] = {wj << 16, wj & 0xFFFF0000u};
+    float y[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const float a = __uint_as_float(b[h] & 0x7FFFFFFFu);
+        const float q0 = a * r;
+        const float e = __builtin_fmaf(-q0, s, a);
+        const float q = __builtin_fmaf(e, r, q0);
+        y[h] = __uint_as_float(__float_as_uint(q) | (b[h] & 0x80000000u));
+    }
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, y[0], y[1], 1.0f, SEL);
+}
+__device__ __forceinline__ uint32_t quant16_fast(const uint32_t (&w)[8], uint32_t &lo, uint32_t &hi) {
+    uint32_t amax_bits = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        amax_bits = max(amax_bits, w[j] & 0x7FFFu);
+        amax_bits = max(amax_bits, (w[j] >> 16) & 0x7FFFu);
+    }
+    const uint32_t sb = f32_to_e4m3_rne(bf16_to_f32(amax_bits) / 6.0f);
+    const float s = sb ? e4m3_to_f32(sb) : 1.0f;
+    const float r = sb ? 1.0f / s : 0.0f;
+    lo = fp4_pair<0>(0u, w[0], s, r);
+    lo = fp4_pair<1>(lo, w[1], s, r);
+    lo = fp4_pair<2>(lo, w[2], s, r);
+    lo = fp4_pair<3>(lo, w[3], s, r);
+    hi = fp4_pair<0>(0u, w[4], s, r);
+    hi = fp4_pair<1>(hi, w[5], s, r);
+    hi = fp4_pair<2>(hi, w[6], s, r);
+    hi = fp4_pair<3>(hi, w[7], s, r);
+    return sb;
+}
+
+__device__ __forceinline__ void quant_act_block(const uint16_t *__restrict__ x, int64_t blk,
+                                                uint8_t *__restrict__ codes,
+                                                uint8_t *__restrict__ scales) {
+    const uint4 *src = reinterpret_cast<const uint4 *>(x + blk * 16);
+    const uint4 v0 = src[0], v1 = src[1];
+    const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    uint32_t lo, hi;
+    const uint32_t sb = quant16(w, lo, hi);
     *reinterpret_cast<uint2 *>(codes + blk * 8) = make_uint2(lo, hi);
     scales[blk] = (uint8_t)sb;
 }
@@ -134,6 +190,10 @@ __device__ __forceinline__ uint32_t load1(__amdgpu_buffer_rsrc_t r, int off) {
 // Streaming variants with the non-temporal cache policy (bit 1 of the
 // cache-policy operand on gfx950), for data read once.
 constexpr int kPolicyNt = 2;
+// Loads that bypass the CU's L1 and are served by the XCD's L2 (sc0): how a
+// workgroup reads values another workgroup of the same XCD stored in the
+// same launch.
+constexpr int kPolicySc0 = 1;
 __device__ __forceinline__ u32x2_t load8_nt(__amdgpu_buffer_rsrc_t r, int off) {
     return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kPolicyNt));
 }

@@ -38,6 +38,7 @@
 //    end once every flag is in.  A consumer's wait for z is bounded: when it
 //    runs out the consumer computes the z values itself, so the kernel ends
 //    whatever else runs.
+#include <algorithm>
 #include <type_traits>
 
 #include "biloco_device.h"
@@ -67,7 +68,7 @@ struct GemvParams {
     uint8_t *qa_scales;
     uint32_t *epoch;        // workspace header word 0
     uint32_t *seen;         // workspace header flags, one per workgroup
-    uint64_t *zt;           // z as (value | tag << 32), [M][rpad]  (one launch)
+    uint64_t *zt;           // one launch: z as (value | tag << 32), [MM][rpad]
     const float *zf;        // z as plain fp32 [M][rpad] from the z kernel (two launches)
     float *zf_out;          // the same area, written by the z kernel
     // z / correction operands per lane, [M][ceil(rpad / 512)][64][4][hi, lo]
@@ -76,9 +77,11 @@ struct GemvParams {
     const uint32_t *zop;
     float g;
     int N, K, r, rpad;
-    int rows_per_wg;
+    int first_stream;       // workgroups before this one stream no rows (one launch: the
+                            // side workgroups that compute z)
+    int n_stream;           // workgroups that stream rows; rows split evenly over them
     int z_items;            // ceil(r / kZI)
-    uint32_t spin_limit;    // bound of a wait on z; 0 = compute z locally at once
+    uint32_t spin_limit;    // bound of a wait on z, in 100 MHz ticks; 0 = compute z locally
 };
 
 __device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float c) {
@@ -103,13 +106,6 @@ __device__ __forceinline__ float scale_mant(float s) {
     return __uint_as_float((__float_as_uint(s) & 0x007FFFFFu) | 0x3F800000u);
 }
 
-__device__ __forceinline__ uint64_t ld_tagged(const uint64_t *p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_tagged(uint64_t *p, float v, uint32_t tag) {
-    const uint64_t w = ((uint64_t)tag << 32) | __float_as_uint(v);
-    __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 __device__ __forceinline__ uint32_t ld_u32(const uint32_t *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -200,85 +196,184 @@ __device__ __forceinline__ void z_accumulate(const GemvParams &p, int item, ZInp
     }
 }
 
-// The workgroup sums of a z item, times alpha_i, published with the call's
-// epoch + 1: all sums first, then the kZI * MM stores from as many threads,
-// with no wait behind them (a store would otherwise hold up the next wait).
-template <int MM>
-__device__ __forceinline__ void z_publish(const GemvParams &p, int item, const ZInputs<MM> &in,
-                          float (&acc)[kZI][MM], uint32_t epoch, float *red) {
-    const int i0 = item * kZI;
-    float zs[kZI][MM];
-#pragma unroll
-    for (int i = 0; i < kZI; ++i)
-#pragma unroll
-        for (int m = 0; m < MM; ++m) zs[i][m] = block_sum8(acc[i][m], red);
-    const uint32_t tag = epoch + 1u;
-#pragma unroll
-    for (int i = 0; i < kZI; ++i)
-#pragma unroll
-        for (int m = 0; m < MM; ++m) {
-            const int ii = i0 + i;
-            if ((int)threadIdx.x == 64 * i + m && ii < p.r)
-                st_tagged(p.zt + (int64_t)m * p.rpad + ii, zs[i][m] * bf16_to_f32(in.al[i]), tag);
-        }
+// ---- z of the one-launch form: side workgroups ------------------------
+// The first workgroups of the launch (dispatched first) stream no rows: each
+// computes items of 16 ranks (half a V word) of z over all of K from x and V
+// alone, so its inputs come back ahead of the stream of R, and publishes
+// them as 64-bit words (fp32 value | the call's epoch + 1 << 32) with
+// agent-scope stores, which go past the XCD's L2.  Data and tag travel in
+// one word, so no fence is needed.  A streaming workgroup requests z with
+// agent-scope loads right after its first row: the reads queue behind its
+// own loads of R and return with them, by when the side workgroups have
+// long published.  A value whose tag is not yet this call's is re-read
+// within a bounded time and computed locally if still missing.
+constexpr int kZXR = 16;      // ranks per side item: half of one 32-bit V word
+constexpr int kSideWorkgroups = 32;   // side workgroups per launch (at most)
+constexpr int kZXU = 3;       // k-quads per thread per round of side inputs
+
+__device__ __forceinline__ void st_tagged(uint64_t *p, float v, uint32_t tag) {
+    const uint64_t w = ((uint64_t)tag << 32) | __float_as_uint(v);
+    __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// agent-scope load (sc1) through a buffer resource, an ordinary vector load
+// for the wait counters
+constexpr int kPolicySc1 = 16;
+__device__ __forceinline__ uint64_t ld_tagged(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kPolicySc1));
 }
 
-// The same item with no barrier (one launch, inside a wave's row section):
-// only the first round of inputs (K <= 2 kGemvThreads kZU), each wave's sums
-// go to its LDS slot, then a workgroup-scope counter; the wave that arrives
-// last adds the slots in wave order (so the result does not depend on the
-// order of arrival), publishes, and resets the counter.
 template <int MM>
-__device__ __forceinline__ void z_item_waves(const GemvParams &p, int item, const ZInputs<MM> &in, uint32_t epoch,
-                             float (*slots)[kZI * MM], uint32_t *cnt) {
-    const int i0 = item * kZI, o = i0 & 31;
-    const int s = o & 15;
-    const bool high = o >= 16;
-    float acc[kZI][MM];
+struct ZXInputs {
+    u32x4_t v[kZXU];          // V words of k = 4q .. 4q + 3
+    u32x2_t x[kZXU][MM];      // x[m][4q .. 4q + 3] (bf16)
+};
+
+// One round of an item's inputs: k-quad q = (round kZXU + u) 512 + thread;
+// quads past K read zeros through the offset kOob (zero x adds nothing).
+template <int MM>
+__device__ __forceinline__ void zx_load(const GemvParams &p, int item, int round, ZXInputs<MM> &in) {
+    const __amdgpu_buffer_rsrc_t rv = buffer_of(p.v + (int64_t)(item >> 1) * p.K, (int64_t)p.K * 4);
+    const __amdgpu_buffer_rsrc_t rx = buffer_of(p.x, (int64_t)MM * p.K * 2);
+    const int KQ = p.K >> 2;
 #pragma unroll
-    for (int i = 0; i < kZI; ++i)
+    for (int u = 0; u < kZXU; ++u) {
+        const int q = (round * kZXU + u) * kGemvThreads + (int)threadIdx.x;
+        const bool ok = q < KQ;
+        in.v[u] = load16(rv, opaque(ok ? q * 16 : kOob));
 #pragma unroll
-        for (int m = 0; m < MM; ++m) acc[i][m] = 0.0f;
-    const int KP = p.K / 2;
+        for (int m = 0; m < MM; ++m) in.x[u][m] = load8(rx, opaque(ok ? (m * p.K + 4 * q) * 2 : kOob));
+    }
+}
+
+// The sign-by-x products of one round, per thread, for the 16 ranks of the
+// item's half word: the 16 sign bits of k and k + 1 go to the low and high
+// halves of one dword, each rank's pair of signs becomes a bf16 pair of +-1,
+// and v_dot2 (exact products, fp32 sums) adds sign_k x_k + sign_k+1 x_k+1.
+template <int MM>
+__device__ __forceinline__ void zx_accumulate(const ZXInputs<MM> &in, int half, float (&acc)[kZXR][MM]) {
+    const uint32_t sel = half ? 0x07060302u : 0x05040100u;
 #pragma unroll
-    for (int u = 0; u < kZU; ++u) {
-        const bool valid = (int)threadIdx.x + kGemvThreads * u < KP;
-        const uint32_t t = high ? __builtin_amdgcn_perm(in.vv[u].y, in.vv[u].x, 0x07060302u)
-                                : __builtin_amdgcn_perm(in.vv[u].y, in.vv[u].x, 0x05040100u);
+    for (int u = 0; u < kZXU; ++u) {
+        const uint32_t t01 = __builtin_amdgcn_perm(in.v[u][1], in.v[u][0], sel);
+        const uint32_t t23 = __builtin_amdgcn_perm(in.v[u][3], in.v[u][2], sel);
 #pragma unroll
-        for (int i = 0; i < kZI; ++i) {
-            const uint32_t sg = signs_bf16x2(t, s + i);
+        for (int i = 0; i < kZXR; ++i) {
+            const uint32_t s01 = signs_bf16x2(t01, i), s23 = signs_bf16x2(t23, i);
 #pragma unroll
-            for (int m = 0; m < MM; ++m) acc[i][m] = dot2_bf16(sg, valid ? in.xp[u][m] : 0u, acc[i][m]);
+            for (int m = 0; m < MM; ++m) {
+                acc[i][m] = dot2_bf16(s01, in.x[u][m][0], acc[i][m]);
+                acc[i][m] = dot2_bf16(s23, in.x[u][m][1], acc[i][m]);
+            }
         }
     }
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int PATTERN>
+__device__ __forceinline__ float swz_f(float v) {
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), PATTERN));
+}
+
+// Sums of 16 values over the 64 lanes of a wave: halving exchanges inside
+// each row of 16 lanes (partners lane ^ 8, ^ 4, ^ 2, ^ 1: each lane keeps the
+// half of its values whose index has its own lane bit, adds the partner's
+// copy of them), then the 4 rows.  Lane l ends with the sum of value l % 16.
+template <int MM>
+__device__ __forceinline__ void zx_wave_reduce(const float (&acc)[kZXR][MM], float (&out)[MM]) {
+    const int lane = threadIdx.x & 63;
+    const bool b3 = lane & 8, b2 = lane & 4, b1 = lane & 2, b0 = lane & 1;
+#pragma unroll
+    for (int m = 0; m < MM; ++m) {
+        float a8[8], a4[4], a2[2];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float keep = b3 ? acc[i + 8][m] : acc[i][m], send = b3 ? acc[i][m] : acc[i + 8][m];
+            a8[i] = keep + dpp_f<0x128>(send);                        // row_ror:8 (lane ^ 8 in a row)
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float keep = b2 ? a8[i + 4] : a8[i], send = b2 ? a8[i] : a8[i + 4];
+            a4[i] = keep + swz_f<0x101F>(send);                       // swizzle: lane ^ 4
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const float keep = b1 ? a4[i + 2] : a4[i], send = b1 ? a4[i] : a4[i + 2];
+            a2[i] = keep + dpp_f<0x4E>(send);                         // quad_perm [2,3,0,1]
+        }
+        float v = (b0 ? a2[1] : a2[0]) + dpp_f<0xB1>(b0 ? a2[0] : a2[1]);   // quad_perm [1,0,3,2]
+        v += swz_f<0x401F>(v);                                        // swizzle: lane ^ 16
+        v += __shfl_xor(v, 32, 64);
+        out[m] = v;
+    }
+}
+
+// One side item: every round of inputs (the first already in `in`), the
+// per-wave sums through LDS, then wave 0 publishes the 16 MM values times
+// alpha_i.
+template <int MM>
+__device__ __forceinline__ void zx_item(const GemvParams &p, int item, ZXInputs<MM> &in,
+                                        uint32_t tag, float (*slots)[kZXR * MM]) {
+    float acc[kZXR][MM];
+#pragma unroll
+    for (int i = 0; i < kZXR; ++i)
+#pragma unroll
+        for (int m = 0; m < MM; ++m) acc[i][m] = 0.0f;
+    const int rounds = ((p.K >> 2) + kZXU * kGemvThreads - 1) / (kZXU * kGemvThreads);
+    for (int rd = 0; rd < rounds; ++rd) {
+        if (rd > 0) zx_load<MM>(p, item, rd, in);
+        zx_accumulate<MM>(in, item & 1, acc);
+    }
+    float v[MM];
+    zx_wave_reduce<MM>(acc, v);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    float v[kZI * MM];
+    __syncthreads();
+    if (lane < kZXR) {
 #pragma unroll
-    for (int i = 0; i < kZI; ++i)
-#pragma unroll
-        for (int m = 0; m < MM; ++m) v[i * MM + m] = wave_sum_dpp(acc[i][m]);
-    uint32_t old = 0;
-    if (lane == 0) {
-#pragma unroll
-        for (int j = 0; j < kZI * MM; ++j) slots[wave][j] = v[j];
-        old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
+        for (int m = 0; m < MM; ++m) slots[wave][lane * MM + m] = v[m];
     }
-    old = __builtin_amdgcn_readfirstlane(old);
-    if (old != (uint32_t)(kGemvThreads / 64 - 1)) return;
-    if (lane < kZI * MM) {
-        float sum = 0.0f;
+    __syncthreads();
+    const int i = kZXR * item + lane;
+    if (wave == 0 && lane < kZXR && i < p.r) {
+        const float al = bf16_to_f32(p.alpha[i]);
 #pragma unroll
-        for (int q = 0; q < kGemvThreads / 64; ++q) sum += slots[q][lane];
-        const int i = lane / MM, m = lane - i * MM, ii = i0 + i;
-        // alpha of index i, selected with constant indices (a register array
-        // indexed by a lane-dependent value would go to scratch memory)
-        uint32_t al = in.al[0];
+        for (int m = 0; m < MM; ++m) {
+            float sum = 0.0f;
 #pragma unroll
-        for (int c = 1; c < kZI; ++c) al = i == c ? in.al[c] : al;
-        if (ii < p.r) st_tagged(p.zt + (int64_t)m * p.rpad + ii, sum * bf16_to_f32(al), epoch + 1u);
+            for (int q = 0; q < kGemvThreads / 64; ++q) sum += slots[q][lane * MM + m];
+            st_tagged(p.zt + (int64_t)m * p.rpad + i, sum * al, tag);
+        }
     }
-    if (lane == 0) *cnt = 0u;
+}
+
+// A side workgroup b (b < first_stream): reads the epoch, records that it
+// has, computes its items b, b + first_stream, ... and publishes them.
+// Workgroup 0 is also the bookkeeper: it advances the epoch once every other
+// workgroup has read it (its flag shows epoch + 1), so that no workgroup of
+// this call can see the next value; the next call starts from epoch + 1.
+// Every workgroup sets its flag right after its first loads,
+// unconditionally, and none waits for the bookkeeper, so this wait ends once
+// all have started.
+template <int MM>
+__device__ void side_workgroup(const GemvParams &p, float (*slots)[kZXR * MM]) {
+    const int b = blockIdx.x, S = p.first_stream;
+    const int items = (p.r + kZXR - 1) / kZXR;
+    ZXInputs<MM> in;
+    const uint32_t ep = ld_u32(p.epoch);
+    zx_load<MM>(p, b < items ? b : items - 1, 0, in);
+    if (threadIdx.x == 0) st_u32(p.seen + b, ep + 1u);
+    for (int it = b; it < items; it += S) {
+        if (it != b) zx_load<MM>(p, it, 0, in);
+        zx_item<MM>(p, it, in, ep + 1u, slots);
+    }
+    if (b == 0) {
+        for (int j = 1 + threadIdx.x; j < (int)gridDim.x; j += kGemvThreads)
+            while (ld_u32(p.seen + j) != ep + 1u) __builtin_amdgcn_s_sleep(2);
+        __syncthreads();
+        if (threadIdx.x == 0) st_u32(p.epoch, ep + 1u);
+    }
 }
 
 // Fallback: z[m][i] for one index, computed by one thread alone (slow; used
@@ -393,7 +488,11 @@ __device__ __forceinline__ void add_correction_ops(const GemvParams &p, const ui
 // ZMODE 0: no correction (r == 0); 1: z produced in this launch by the first
 // workgroups and polled through epoch tags; 2: z complete in the workspace
 // (written by z_kernel earlier on the same stream).
-template <int MM, int KBL, int ZMODE>
+// QA: the launch also quantises x (the activation's FP4 codes and scales are
+// computed here, bit for bit as biloco_quant_act_fp4 computes them, from the
+// bf16 x each lane loads for its own blocks; the first streaming
+// workgroup's first wave also stores them to qa_codes / qa_scales).
+template <int MM, int KBL, int ZMODE, bool QA>
 __global__ void __launch_bounds__(kGemvThreads) fused_gemv_kernel(GemvParams p) {
     constexpr int R = gemv_rows_per_wave(KBL, MM);
     static_assert(R >= 1 && R <= 4, "the row-count switch covers 1 .. 4 rows per wave");
@@ -403,8 +502,7 @@ __global__ void __launch_bounds__(kGemvThreads) fused_gemv_kernel(GemvParams p) 
     constexpr int AMAX = (MM * KBL * 64 + kGemvThreads - 1) / kGemvThreads;  // blocks per thread
     __shared__ float s_red[8];
     __shared__ uint32_t s_bcast;
-    __shared__ float s_zslots[kGemvThreads / 64][kZI * MM];   // one launch: per-wave z item sums
-    __shared__ uint32_t s_zcnt;
+    __shared__ float s_zslots[kGemvThreads / 64][kZXR * MM];  // one launch: side workgroups' sums
     extern __shared__ uint32_t s_dyn[];   // activation f16 pairs [MM][KB][8], then z [MM][rpad]
 
     // the wave index as a scalar, so that the row count below is one too
@@ -418,15 +516,19 @@ __global__ void __launch_bounds__(kGemvThreads) fused_gemv_kernel(GemvParams p) 
     // activation: the word was last written on another XCD)
     uint32_t ep = 0u;
     if constexpr (ZMODE == 1) {
-        // the z item's arrival counter, zeroed before any wave can use it
-        if (threadIdx.x == 0) s_zcnt = 0u;
-        __syncthreads();
+        // the side workgroups (the first of the launch) compute z and end
+        if ((int)blockIdx.x < p.first_stream) {
+            side_workgroup<MM>(p, s_zslots);
+            return;
+        }
     }
 
-    // rows of this workgroup, spread over its 8 waves (the first get one more)
-    const int wg_row0 = blockIdx.x * p.rows_per_wg;
-    int wg_rows = p.N - wg_row0;
-    wg_rows = wg_rows < 0 ? 0 : (wg_rows > p.rows_per_wg ? p.rows_per_wg : wg_rows);
+    // rows of this workgroup: the N rows split evenly over the n_stream
+    // workgroups from first_stream on; spread over its 8 waves (the first get
+    // one more)
+    const int sb = (int)blockIdx.x - p.first_stream;
+    const int wg_row0 = sb < 0 ? p.N : (int)((int64_t)sb * p.N / p.n_stream);
+    const int wg_rows = sb < 0 ? 0 : (int)((int64_t)(sb + 1) * p.N / p.n_stream) - wg_row0;
     const int base = wg_rows >> 3, extra = wg_rows & 7;
     const int nrows = base + (wave < extra ? 1 : 0);
     const int row0 = wg_row0 + wave * base + (wave < extra ? wave : extra);
@@ -443,11 +545,29 @@ __global__ void __launch_bounds__(kGemvThreads) fused_gemv_kernel(GemvParams p) 
     // item's inputs)
     constexpr bool lane_act = KBL * MM <= (ZMODE == 1 ? 6 : 8);
     const int nact = MM * KB;
+    // QA: this workgroup stores the codes and scales (its first wave, whose
+    // lanes' blocks lane + 64 t cover every block; through LDS, all threads)
+    const bool qa_writer = QA && (int)blockIdx.x == p.first_stream;
     uint2 ac[AMAX];
     uint32_t asb[AMAX];
     uint2 lac[lane_act ? KBL : 1][MM];
     uint32_t las[lane_act ? KBL : 1][MM];
-    if constexpr (lane_act) {
+    // QA: this wave's share of the blocks to quantise for the workgroup:
+    // blocks w S8 + lane + 64 j (j < QB) of the MM KB blocks, S8 = their
+    // count over 8; past the share, the offset kOob reads nothing
+    constexpr int QB = (8 * KBL * MM + 63) / 64;
+    const int S8 = (nact + 7) >> 3;
+    u32x4_t qx[QA ? QB : 1][2];
+    if constexpr (QA) {
+        const __amdgpu_buffer_rsrc_t r_x = buffer_of(p.x, (int64_t)nact * 32);
+#pragma unroll
+        for (int j = 0; j < QB; ++j) {
+            const int ai = wave * S8 + lane + 64 * j;
+            const bool ok = lane + 64 * j < S8 && ai < nact;
+            qx[j][0] = load16(r_x, opaque(ok ? ai * 32 : kOob));
+            qx[j][1] = load16(r_x, opaque(ok ? ai * 32 + 16 : kOob));
+        }
+    } else if constexpr (lane_act) {
         // scales as the aligned 4-byte word holding the lane's byte (a byte
         // load's widening would be placed, and waited for, right here); the
         // last word may cover up to 3 bytes past the array, inside the
@@ -471,15 +591,30 @@ __global__ void __launch_bounds__(kGemvThreads) fused_gemv_kernel(GemvParams p) 
             asb[a] = p.a_scales[(int64_t)m * KB + b];
         }
     }
-    // 2. a z item's inputs (one launch) or the finished z (two launches)
-    const bool z_wg = ZMODE == 1 && (int)blockIdx.x < p.z_items;
-    // the z item published early (inside the row section, no barrier) when
-    // its inputs fit beside the rows' registers: KBL MM <= 8, which also
-    // bounds K by 8192, one round of inputs; otherwise after the rows
-    constexpr bool z_early = KBL * MM <= 8;
-    static_assert(!z_early || 64 * KBL * 16 <= 2 * kGemvThreads * kZU, "one round of z inputs");
-    ZInputs<MM> zin;
+    (void)qx;
+    // 2. one launch: this thread's z values, requested behind the rows' loads
     const int nz = MM * p.r;
+    // one launch: this thread's z values (requested after the first row)
+    // Two reads of each value: the first right behind the first row's loads
+    // (it returns with the stream when it reaches memory after the side
+    // workgroups have published), the second after the first row's
+    // arithmetic, for values the first one found not yet published.
+    uint64_t zv[ZP], zv2[ZP];
+    const __amdgpu_buffer_rsrc_t r_zt = buffer_of(p.zt, (int64_t)MM * p.rpad * 8);
+    auto z_request = [&](uint64_t (&dst)[ZP]) {
+#pragma unroll
+        for (int j = 0; j < ZP; ++j) {
+            const int idx = threadIdx.x + kGemvThreads * j;
+            const int ic = idx < nz ? idx : nz - 1;
+            const int m = ic / p.r, i = ic - m * p.r;
+            dst[j] = ld_tagged(r_zt, opaque((m * p.rpad + i) * 8));
+        }
+    };
+    // one launch: the epoch has been read (the bookkeeper may advance it once
+    // every workgroup has)
+    auto z_produce = [&]() {
+        if (threadIdx.x == 0) st_u32(p.seen + blockIdx.x, ep + 1u);
+    };
     // Correction inputs, requested once the activation is decoded, just ahead
     // of the rows of R (they are needed only at the end; requested with the
     // activation, they would hold it up).
@@ -495,7 +630,6 @@ __global__ void __launch_bounds__(kGemvThreads) fused_gemv_kernel(GemvParams p) 
     // exact)
     if constexpr (ZMODE == 1) {
         ep = ld_u32(p.epoch);
-        if constexpr (z_early) z_prefetch<MM>(p, min((int)blockIdx.x, p.z_items - 1), zin);
     }
     if constexpr (ZMODE == 2) {
         const int QW = zop_rounds(p.r);
@@ -544,7 +678,46 @@ __global__ void __launch_bounds__(kGemvThreads) fused_gemv_kernel(GemvParams p) 
             o[d] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, raw[d]) * mm2);
     };
     uint32_t act[KBL][MM][8];
-    if constexpr (!lane_act) {
+    // QA: quantise this wave's share of the blocks (bit for bit as
+    // biloco_quant_act_fp4: quant16_fast) and store the exact f16 values to
+    // LDS (the first streaming workgroup also stores codes and scales);
+    // after a barrier, qa_fetch takes this lane's blocks from LDS.
+    auto qa_share = [&]() {
+#pragma unroll
+        for (int j = 0; j < QB; ++j) {
+            const int ai = wave * S8 + lane + 64 * j;
+            if (lane + 64 * j < S8 && ai < nact) {
+                const uint32_t w[8] = {qx[j][0][0], qx[j][0][1], qx[j][0][2], qx[j][0][3],
+                                       qx[j][1][0], qx[j][1][1], qx[j][1][2], qx[j][1][3]};
+                uint32_t lo, hi;
+                const uint32_t sb = quant16_fast(w, lo, hi);
+                if (qa_writer) {
+                    const int m = ai / KB, b = ai - m * KB;
+                    *reinterpret_cast<uint2 *>(p.qa_codes + (int64_t)m * KH + b * 8) = make_uint2(lo, hi);
+                    p.qa_scales[(int64_t)m * KB + b] = (uint8_t)sb;
+                }
+                uint32_t o[8];
+                decode_block(make_uint2(lo, hi), sb, o);
+                uint4 *dst = reinterpret_cast<uint4 *>(s_act + (size_t)ai * 8);
+                dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+                dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+            }
+        }
+    };
+    auto qa_fetch = [&]() {
+#pragma unroll
+        for (int t = 0; t < KBL; ++t) {
+            const int b = lane + 64 * t, bc = b < KB ? b : KB - 1;
+#pragma unroll
+            for (int m = 0; m < MM; ++m) {
+                const uint4 *src = reinterpret_cast<const uint4 *>(s_act + ((size_t)m * KB + bc) * 8);
+                const uint4 lo = src[0], hi = src[1];
+                act[t][m][0] = lo.x; act[t][m][1] = lo.y; act[t][m][2] = lo.z; act[t][m][3] = lo.w;
+                act[t][m][4] = hi.x; act[t][m][5] = hi.y; act[t][m][6] = hi.z; act[t][m][7] = hi.w;
+            }
+        }
+    };
+    if constexpr (!lane_act && !QA) {
 #pragma unroll
     for (int a = 0; a < AMAX; ++a) {
         const int ai = threadIdx.x + kGemvThreads * a;
@@ -595,8 +768,7 @@ __global__ void __launch_bounds__(kGemvThreads) fused_gemv_kernel(GemvParams p) 
         constexpr int NR = decltype(nr_c)::value;
         u32x2_t codes[NR][KBL];
         uint32_t sc[NR][KBL];
-#pragma unroll
-        for (int rr = 0; rr < NR; ++rr) {
+        auto load_row = [&](int rr) {
             const int n = row0 + rr;
 #pragma unroll
             for (int t = 0; t < KBL; ++t) {
@@ -606,12 +778,25 @@ __global__ void __launch_bounds__(kGemvThreads) fused_gemv_kernel(GemvParams p) 
                     reinterpret_cast<const u32x2_t *>(p.w_codes + (int64_t)n * KH + bc * 8));
                 sc[rr][t] = __builtin_nontemporal_load(p.w_scales + (int64_t)n * KB + bc);
             }
-        }
+        };
+        // one launch: the first row's loads, then the epoch's flag (the
+        // epoch was requested before them, so it waits for no row), then the
+        // others
+        load_row(0);
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (ZMODE == 1) z_request(zv);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (ZMODE == 1) z_produce();
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int rr = 1; rr < NR; ++rr) load_row(rr);
+        __builtin_amdgcn_sched_barrier(0);
+
         // the lane's activation, decoded while the rows stream in (its words
         // pass an empty asm here, so that neither the decode nor its wait is
         // hoisted out of this row-count case to before the rows' loads)
-        if constexpr (lane_act) {
+        if constexpr (QA) {
+        } else if constexpr (lane_act) {
 #pragma unroll
             for (int t = 0; t < KBL; ++t)
 #pragma unroll
@@ -622,10 +807,6 @@ __global__ void __launch_bounds__(kGemvThreads) fused_gemv_kernel(GemvParams p) 
                     const uint32_t sb = ((uint32_t)opaque((int)las[t][m]) >> (8 * ((m * KB + bc) & 3))) & 0xFFu;
                     decode_block(c, sb, act[t][m]);
                 }
-        }
-        // one launch: the z item, published while the rows stream in
-        if constexpr (ZMODE == 1 && z_early) {
-            if (z_wg) z_item_waves<MM>(p, blockIdx.x, zin, ep, s_zslots, &s_zcnt);
         }
 #pragma unroll
         for (int rr = 0; rr < NR; ++rr) {
@@ -657,11 +838,26 @@ __global__ void __launch_bounds__(kGemvThreads) fused_gemv_kernel(GemvParams p) 
             // keep each row's decoding next to its products (hoisted, it
             // would wait for every row's loads)
             __builtin_amdgcn_sched_barrier(0);
+            if constexpr (ZMODE == 1) {
+                if (rr == 0) z_request(zv2);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
         // the correction last: U's scattered words come back while the rows
         // are consumed, so no row waits for them
         if constexpr (ZMODE == 2) add_correction_ops<MM, NR, R, QMAX>(p, ul, zo, part);
     };
+    // QA: the activation first (the x loads are the oldest in flight): each
+    // wave quantises its share into LDS, one barrier, every lane takes its
+    // blocks; the rows are requested after that.  (Quantised after the rows'
+    // loads were issued, the shares waited for the slowest wave's issue, up
+    // to 3 us under the stream's back-pressure: 7.3 us per quantising r = 0
+    // call against 6.4 us this way, config 1.)
+    if constexpr (QA) {
+        qa_share();
+        __syncthreads();
+        qa_fetch();
+    }
     request_correction_inputs();
     __builtin_amdgcn_sched_barrier(0);
     switch (nrows) {
@@ -670,63 +866,38 @@ __global__ void __launch_bounds__(kGemvThreads) fused_gemv_kernel(GemvParams p) 
         case 3: if constexpr (R >= 3) rows(std::integral_constant<int, 3>{}); break;
         case 4: if constexpr (R >= 4) rows(std::integral_constant<int, 4>{}); break;
         default:   // no rows: nothing is stored
-            if constexpr (ZMODE == 1 && z_early) {
-                if (z_wg) z_item_waves<MM>(p, blockIdx.x, zin, ep, s_zslots, &s_zcnt);
+            if constexpr (ZMODE == 1) {
+                z_request(zv);
+                z_produce();
+                z_request(zv2);
             }
             break;
     }
 
-    // one launch: the z item, computed and published once the rows are done
-    // (its inputs came in ahead of them); computed before the rows, it held
-    // up every workgroup's stream.  Every other workgroup then records that
-    // it has read the epoch.
-    if (ZMODE == 1) {
-        if (z_wg) {
-            float zacc[kZI][MM];
-            if constexpr (!z_early) {
-                z_prefetch<MM>(p, blockIdx.x, zin);
-                z_accumulate<MM>(p, blockIdx.x, zin, zacc);
-                z_publish<MM>(p, blockIdx.x, zin, zacc, ep, s_red);
-            }
-            for (int it = blockIdx.x + gridDim.x; it < p.z_items; it += gridDim.x) {
-                z_prefetch<MM>(p, it, zin);
-                z_accumulate<MM>(p, it, zin, zacc);
-                z_publish<MM>(p, it, zin, zacc, ep, s_red);
-            }
-        }
-        if (threadIdx.x == 0 && blockIdx.x > 0) st_u32(p.seen + blockIdx.x, ep + 1u);
-    }
-
-    // 9. one launch: z of this call into LDS (every thread requests its z
-    // words at once, then re-reads the ones not yet published, bounded), then
-    // the correction
-    if (ZMODE == 1) {
+    // 9. one launch: z into LDS, then the correction.  Values whose tag is not
+    // yet this call's are re-read within a bounded time, and computed here if
+    // still missing.
+    if (ZMODE == 1 && wg_rows > 0) {
         if (threadIdx.x == 0) s_bcast = ep;
         __syncthreads();
         const uint32_t tag = s_bcast + 1u;
-        uint64_t zv[ZP];
-#pragma unroll
-        for (int j = 0; j < ZP; ++j) {
-            const int idx = threadIdx.x + kGemvThreads * j;
-            const int ic = idx < nz ? idx : nz - 1;
-            const int m = ic / p.r, i = ic - m * p.r;
-            zv[j] = ld_tagged(p.zt + (int64_t)m * p.rpad + i);
-        }
 #pragma unroll
         for (int j = 0; j < ZP; ++j) {
             const int idx = threadIdx.x + kGemvThreads * j;
             if (idx < nz) {
                 const int m = idx / p.r, i = idx - m * p.r;
-                const uint64_t *src = p.zt + (int64_t)m * p.rpad + i;
-                uint64_t a = zv[j];
-                uint32_t spins = 0;
-                while ((uint32_t)(a >> 32) != tag && spins < p.spin_limit) {
-                    __builtin_amdgcn_s_sleep(1);
-                    a = ld_tagged(src);
-                    ++spins;
+                uint64_t a = (uint32_t)(zv[j] >> 32) == tag ? zv[j] : zv2[j];
+                if ((uint32_t)(a >> 32) != tag && p.spin_limit) {
+                    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+                    do {
+                        __builtin_amdgcn_s_sleep(1);
+                        a = ld_tagged(r_zt, (m * p.rpad + i) * 8);
+                    } while ((uint32_t)(a >> 32) != tag &&
+                             __builtin_amdgcn_s_memrealtime() - t0 < (uint64_t)p.spin_limit);
                 }
-                s_z[zslot(p, m, i)] = (uint32_t)(a >> 32) == tag ? __uint_as_float((uint32_t)a)
-                                                                 : z_local(p, m, i);
+                s_z[zslot(p, m, i)] = ((uint32_t)(a >> 32) == tag && p.spin_limit)
+                                          ? __uint_as_float((uint32_t)a)
+                                          : z_local(p, m, i);
             }
         }
         __syncthreads();
@@ -744,16 +915,6 @@ __global__ void __launch_bounds__(kGemvThreads) fused_gemv_kernel(GemvParams p) 
                 else p.y[(int64_t)m * p.N + row0 + rr] = f32_to_bf16_rne(sum);
             }
         }
-
-    // 11. one launch: workgroup 0 advances the epoch once every other
-    // workgroup has read it (its flag shows epoch + 1); the next call then
-    // starts from epoch + 1
-    if (ZMODE == 1 && blockIdx.x == 0) {
-        for (int j = 1 + threadIdx.x; j < (int)gridDim.x; j += kGemvThreads)
-            while (ld_u32(p.seen + j) != ep + 1u) __builtin_amdgcn_s_sleep(2);
-        __syncthreads();
-        if (threadIdx.x == 0) st_u32(p.epoch, ep + 1u);
-    }
 }
 
 // z[m][i] into its correction operand slot: index i = 32 w + 16 h + 4 j + g
@@ -831,8 +992,14 @@ size_t gemv_lds_bytes(int M, int K, int rpad) {
 
 template <int MM, int KBL, int ZMODE>
 hipError_t launch_t(const GemvParams &p, int grid, size_t lds, hipStream_t stream) {
-    hipLaunchKernelGGL((fused_gemv_kernel<MM, KBL, ZMODE>), dim3(grid), dim3(kGemvThreads), lds,
-                       stream, p);
+    // the two-launch form quantises x in its z launch; the others in the
+    // product launch itself when asked to
+    if (ZMODE != 2 && p.qa_codes)
+        hipLaunchKernelGGL((fused_gemv_kernel<MM, KBL, ZMODE, ZMODE != 2>), dim3(grid),
+                           dim3(kGemvThreads), lds, stream, p);
+    else
+        hipLaunchKernelGGL((fused_gemv_kernel<MM, KBL, ZMODE, false>), dim3(grid),
+                           dim3(kGemvThreads), lds, stream, p);
     return hipGetLastError();
 }
 
@@ -871,10 +1038,12 @@ hipError_t launch_m(const GemvParams &p, int kbl, int grid, size_t lds, int zmod
 }
 
 uint32_t spin_limit_default() {
-    // debug override (BILOCO_DEBUG_SPIN_LIMIT): shortens the bounded wait on z
-    // so that tests can force the self-computing fallback
+    // the bound of a consumer's wait for a z value, in ticks of the 100 MHz
+    // real-time counter (100 us).  Debug override (BILOCO_DEBUG_SPIN_LIMIT):
+    // 0 makes every consumer compute z itself, so that tests can run the
+    // fallback from the host.
     const char *s = getenv("BILOCO_DEBUG_SPIN_LIMIT");
-    return s ? (uint32_t)strtoul(s, nullptr, 10) : (uint32_t)(1u << 20);
+    return s ? (uint32_t)strtoul(s, nullptr, 10) : 10000u;
 }
 
 int kbl_of(int K) { return (K / 16 + 63) / 64; }
@@ -927,9 +1096,25 @@ hipError_t launch_gemv(const GemmArgs &a, bool two_launch, hipStream_t stream) {
     p.r = a.r;
     p.rpad = rpad32(a.r);
     const int kbl = kbl_of(a.K);
-    int swgs = 0;
-    gemv_grid(a.N, kbl_launch(kbl), a.M, &swgs, &p.rows_per_wg);
+    int swgs = 0, rpg = 0;
+    gemv_grid(a.N, kbl_launch(kbl), a.M, &swgs, &rpg);
+    p.first_stream = 0;
+    p.n_stream = swgs;
     p.z_items = (a.r + kZI - 1) / kZI;
+    int grid = swgs;
+    if (!two_launch && a.r > 0) {
+        // one launch: the first S workgroups are side workgroups (z only,
+        // items of 16 ranks; workgroup 0 is also the bookkeeper), the others
+        // stream the rows.  While the rows fit, the grid is 256 (one per CU:
+        // a kernel of this size holds a CU alone, so a 257th workgroup would
+        // start only once another has ended).
+        const int S = std::min(kSideWorkgroups, (a.r + kZXR - 1) / kZXR);
+        const int cap = 8 * gemv_rows_per_wave(kbl_launch(kbl), a.M);
+        const int need = (a.N + cap - 1) / cap;
+        p.first_stream = S;
+        p.n_stream = need <= 256 - S ? std::min(256 - S, a.N) : need;
+        grid = p.n_stream + S;
+    }
     int zmode = 0;
     if (a.r > 0) {
         char *ws = static_cast<char *>(a.ws);
@@ -963,8 +1148,8 @@ hipError_t launch_gemv(const GemmArgs &a, bool two_launch, hipStream_t stream) {
     }
     const size_t lds = gemv_lds_bytes(a.M, a.K, p.rpad);
     switch (a.M) {
-        case 1: return launch_m<1>(p, kbl, swgs, lds, zmode, stream);
-        case 2: return launch_m<2>(p, kbl, swgs, lds, zmode, stream);
+        case 1: return launch_m<1>(p, kbl, grid, lds, zmode, stream);
+        case 2: return launch_m<2>(p, kbl, grid, lds, zmode, stream);
         default: return hipErrorNotSupported;
     }
 }
