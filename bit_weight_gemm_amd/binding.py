@@ -32,7 +32,11 @@ EXPORTED = ["biloco_status_string", "biloco_pack_signs", "biloco_quant_act_fp4",
             "biloco_gemm_workspace_bytes", "biloco_gemm_lowrank", "biloco_gemm_lowrank_sched",
             "biloco_gemm_check", "biloco_default_schedule", "biloco_schedules_for",
             "biloco_quant_weight_nvfp4", "biloco_quant_weight_workspace_bytes",
-            "biloco_peel_decompose", "biloco_peel_workspace_bytes", "biloco_gemm_lowrank_quant"]
+            "biloco_peel_decompose", "biloco_peel_workspace_bytes", "biloco_gemm_lowrank_quant",
+            "biloco_gemm_lowrank_quant_noalloc"]
+
+# size of the device array biloco_gemm_lowrank_quant_noalloc works in
+BILOCO_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 _lib = None
 
@@ -77,6 +81,9 @@ def lib() -> ctypes.CDLL:
         L.biloco_gemm_lowrank_quant.restype = st
         L.biloco_gemm_lowrank_quant.argtypes = [p, p, p, p, p, ctypes.c_float, p, p, p, i32, i32, i32,
                                                 i32, p, p, sz, i32, p]
+        L.biloco_gemm_lowrank_quant_noalloc.restype = st
+        L.biloco_gemm_lowrank_quant_noalloc.argtypes = [p, p, p, p, p, ctypes.c_float, p, p, p, i32,
+                                                        i32, i32, i32, p, i32, p]
         L.biloco_gemm_check.restype = st
         L.biloco_gemm_check.argtypes = [p, p, p, p, p, p, p, p, i32, i32, i32, i32, p, p, sz, i32]
         L.biloco_default_schedule.restype = i32
@@ -222,6 +229,19 @@ def biloco_gemm_lowrank(a_codes, a_scales, x_bf16, w_codes, w_scales, w_global_s
         _p(v_packed), _p(u_packed), _p(alpha_bf16), M, N, K, r, _p(y), _p(workspace),
         int(workspace_bytes), _stream(stream))
     _ok(st, "biloco_gemm_lowrank")
+    return y
+
+
+def biloco_gemm_lowrank_quant_noalloc(x_bf16, a_codes, a_scales, w_codes, w_scales,
+                                      w_global_scale, v_packed, u_packed, alpha_bf16, M, N, K, r, y,
+                                      schedule=BILOCO_SCHED_AUTO, stream=None):
+    """biloco_gemm_lowrank_quant in the library's own per-GPU scratch array
+    (no workspace argument; nothing is allocated)."""
+    st = lib().biloco_gemm_lowrank_quant_noalloc(
+        _p(x_bf16), _p(a_codes), _p(a_scales), _p(w_codes), _p(w_scales), float(w_global_scale),
+        _p(v_packed), _p(u_packed), _p(alpha_bf16), M, N, K, r, _p(y), int(schedule),
+        _stream(stream))
+    _ok(st, "biloco_gemm_lowrank_quant_noalloc")
     return y
 
 

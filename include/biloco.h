@@ -246,6 +246,27 @@ biloco_status biloco_gemm_lowrank_quant(const uint16_t *x_bf16, uint8_t *a_codes
                                         void *workspace, size_t workspace_bytes, int32_t schedule,
                                         hipStream_t stream);
 
+/* For callers that cannot allocate (code under graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): biloco_gemm_lowrank_quant without
+ * a workspace argument.  The workspace is a device array of
+ * BILOCO_NOALLOC_SCRATCH_BYTES inside the library, one copy per GPU (each
+ * GPU the call runs on holds its copy until the process ends); the call
+ * allocates nothing.  The array is used on the current device (hipGetDevice),
+ * so `stream` must belong to it.  Every call on one GPU shares that GPU's
+ * array: calls that can run at the same time on one GPU (other streams,
+ * other threads) race and give wrong results; calls ordered on one stream
+ * are safe.  A shape whose workspace (biloco_gemm_workspace_bytes) exceeds
+ * the array returns BILOCO_ERR_UNSUPPORTED before any HIP call; otherwise
+ * the arguments, results and errors are those of biloco_gemm_lowrank_quant. */
+#define BILOCO_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+biloco_status biloco_gemm_lowrank_quant_noalloc(const uint16_t *x_bf16, uint8_t *a_codes,
+                                                uint8_t *a_scales, const uint8_t *w_codes,
+                                                const uint8_t *w_scales, float w_global_scale,
+                                                const uint32_t *v_packed, const uint32_t *u_packed,
+                                                const uint16_t *alpha_bf16, int32_t M, int32_t N,
+                                                int32_t K, int32_t r, uint16_t *y_bf16,
+                                                int32_t schedule, hipStream_t stream);
+
 /* Host-only argument check of biloco_gemm_lowrank_sched: returns the status
  * the call would return for these arguments before launching anything.
  * Makes no HIP call (usable without a GPU). */
