@@ -216,6 +216,45 @@ def decompose_time(m: int = 5120, n: int = 5120, r: int = 512, T: int = 5) -> di
             "bytes": nbytes}
 
 
+def stream_floor(configs=(1, 2, 3, 4), calls: int = 200) -> dict:
+    """The floors a product call is compared with, in the same graph-replay
+    form the product is timed in: one launch that only reads the config's
+    algorithmic byte count from HBM (a plain 16-byte-per-lane read kernel,
+    buffers rotated over >= 1.2 GB so that the Infinity Cache cannot serve
+    them), and one empty launch."""
+    import ctypes
+    import math
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "bit_weight_gemm_amd", "libbiloco_floor.so"))
+    lib.biloco_floor_read.restype = ctypes.c_int
+    lib.biloco_floor_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                      ctypes.c_int32, ctypes.c_void_p]
+    lib.biloco_floor_empty.restype = ctypes.c_int
+    lib.biloco_floor_empty.argtypes = [ctypes.c_void_p]
+    from bit_weight_gemm_amd import workloads as wl
+    out = torch.zeros(1 << 16, dtype=torch.int32, device="cuda")
+    res = {}
+    for c in configs:
+        cf = wl.CONFIGS[c]
+        nb = algorithmic_bytes(cf["M"], cf["N"], cf["K"], cf["r"])
+        n_sets = max(2, math.ceil(ROT_BYTES / nb))
+        bufs = [torch.ones(nb, dtype=torch.uint8, device="cuda") for _ in range(n_sets)]
+        torch.cuda.synchronize()
+
+        def step(i, st, bufs=bufs, nb=nb):
+            assert lib.biloco_floor_read(bufs[i % len(bufs)].data_ptr(), nb, out.data_ptr(), 256,
+                                         st.cuda_stream) == 0
+        t, _ = time_graph(step, calls)
+        res[f"config{c}"] = {"bytes": nb, "us_per_call": round(t * 1e6, 3),
+                             "GBps": round(nb / t / 1e9, 1),
+                             "pct_peak": round(100 * nb / t / 1e9 / PEAK_HBM_GBS, 2)}
+        del bufs
+        torch.cuda.empty_cache()
+    t, _ = time_graph(lambda i, st: lib.biloco_floor_empty(st.cuda_stream), calls)
+    res["empty_launch_us"] = round(t * 1e6, 3)
+    return res
+
+
 def cpu_baseline(cfg: int, seconds: float):
     import numpy as np
     import oracle
@@ -231,10 +270,41 @@ def cpu_baseline(cfg: int, seconds: float):
             break
     dt = (time.perf_counter() - t0) / n
     nb = algorithmic_bytes(d["M"], d["N"], d["K"], d["r"])
-    return {"value": round(nb / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
-            "kind": "oracle", "us_per_call": round(dt * 1e6, 1),
-            "sample": f"{n} full calls of the config-{cfg} product on the host (quantise x, then "
-                      f"y in fp64 over all M*N outputs), same seeded inputs as the GPU"}
+    res = {"value": round(nb / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
+           "kind": "oracle", "us_per_call": round(dt * 1e6, 1),
+           "sample": f"{n} full calls of the config-{cfg} product on the host (quantise x, then "
+                     f"y in fp64 over all M*N outputs), same seeded inputs as the GPU"}
+    # the same on one thread (a bounded sample: whole calls for about a
+    # fifth of the time above)
+    threads = oracle.num_threads()
+    oracle.set_num_threads(1)
+    n1, t1 = 0, time.perf_counter()
+    while True:
+        oracle.quant_act_fp4(d["x"])
+        oracle.gemm_lowrank(d["x"], d["wcode"], d["wscales"], d["g"], d["V"], d["U"], d["alpha"])
+        n1 += 1
+        if time.perf_counter() - t1 >= seconds / 5:
+            break
+    oracle.set_num_threads(threads)
+    dt1 = (time.perf_counter() - t1) / n1
+    res["one_thread"] = {"value": round(nb / dt1 / 1e9, 4), "unit": "GB/s", "cores": 1,
+                         "us_per_call": round(dt1 * 1e6, 1), "sample": f"{n1} full calls"}
+    # the other workloads, one whole call each on all threads
+    per = {}
+    for c in (1, 2, 3, 4):
+        if c == cfg:
+            continue
+        dc = wl.make_config(c)
+        tc = time.perf_counter()
+        oracle.quant_act_fp4(dc["x"])
+        oracle.gemm_lowrank(dc["x"], dc["wcode"], dc["wscales"], dc["g"], dc["V"], dc["U"],
+                            dc["alpha"])
+        tc = time.perf_counter() - tc
+        bc = algorithmic_bytes(dc["M"], dc["N"], dc["K"], dc["r"])
+        per[f"config{c}"] = {"us_per_call": round(tc * 1e6, 1), "GBps": round(bc / tc / 1e9, 4),
+                             "cores": threads, "sample": "1 full call"}
+    res["per_config"] = per
+    return res
 
 
 def main() -> int:
@@ -255,7 +325,7 @@ def main() -> int:
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no GPU work: turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
                          "this script into profiles/traffic_<schedule>_config<c>.json and .md")
-    ap.add_argument("--only", choices=["weight-quant", "decompose"],
+    ap.add_argument("--only", choices=["weight-quant", "decompose", "stream-floor"],
                     help="time only this NEXT-row operation and print its JSON (for profiling)")
     args = ap.parse_args()
     if args.traffic_summary:
@@ -263,7 +333,8 @@ def main() -> int:
     if args.only:
         import torch
         assert torch.cuda.is_available(), "bench.py needs a GPU"
-        res = weight_quant_table() if args.only == "weight-quant" else decompose_time()
+        res = (weight_quant_table() if args.only == "weight-quant" else
+               decompose_time() if args.only == "decompose" else stream_floor())
         print(json.dumps({args.only: res}), flush=True)
         return 0
 
@@ -354,6 +425,14 @@ def main() -> int:
         "source_hash": src_hash,
     }
 
+    # the floors of this byte count: a launch that only reads it, an empty launch
+    fl = stream_floor(configs=(cfg,), calls=200) if cfg in (1, 2, 3, 4) and args.rank is None else None
+    if fl:
+        out["stream_floor"] = {"read_us_per_call": fl[f"config{cfg}"]["us_per_call"],
+                               "read_GBps": fl[f"config{cfg}"]["GBps"],
+                               "empty_launch_us": fl["empty_launch_us"],
+                               "call_over_read_floor": round(t_call * 1e6 / fl[f"config{cfg}"]["us_per_call"], 3)}
+
     if not args.no_configs:
         table = {}
         # correction overhead at this config: the same x and R with r = 0
@@ -384,7 +463,10 @@ def main() -> int:
             tz = gemm_call_time(pz, B.biloco_default_schedule(pz.M, pz.N, pz.K, 0), rz, calls)
             del rz, pz
             torch.cuda.empty_cache()
+            flc = stream_floor(configs=(c,), calls=100)[f"config{c}"]
             table[f"config{c}"] = {"M": dc["M"], "K": dc["K"], "N": dc["N"], "r": dc["r"],
+                                   "read_floor_us_per_call": flc["us_per_call"],
+                                   "call_over_read_floor": round(tc * 1e6 / flc["us_per_call"], 3),
                                    "schedule": SCHED_NAMES.get(sc, sc),
                                    "us_per_call": round(tc * 1e6, 3),
                                    "GBps": round(bc / tc / 1e9, 1),

@@ -40,6 +40,24 @@ def _compile(src: str) -> str:
     return obj
 
 
+FLOOR_SRC = os.path.join(PKG, "floor", "stream_floor.hip")
+FLOOR_LIB = os.path.join(PKG, "libbiloco_floor.so")
+
+
+def build_floor(verbose: bool = True) -> str:
+    """The measurement-only read/empty kernels bench.py's stream-floor leg
+    times (a library of their own, not part of libbiloco_hip)."""
+    tmp = FLOOR_LIB + ".tmp"
+    cmd = [HIPCC] + COMMON + ["-shared", "-x", "hip", FLOOR_SRC, "-o", tmp]
+    p = subprocess.run(cmd, capture_output=True, text=True)
+    if p.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {FLOOR_SRC}:\n{p.stderr}")
+    os.replace(tmp, FLOOR_LIB)
+    if verbose:
+        print(f"built {FLOOR_LIB}")
+    return FLOOR_LIB
+
+
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
     srcs = [s for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]

@@ -65,6 +65,8 @@ def _load():
                                             i64, i64, i64, i64, p, p, p, p]
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
+        lib.oracle_set_num_threads.restype = None
+        lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
         _lib = lib
     return _lib
 
@@ -168,3 +170,9 @@ def gemm_lowrank(x_bf16, wcode, wscale, g, V, U, alpha_bf16, parts: bool = False
 
 def num_threads() -> int:
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the oracle's parallel loops (timing only; results do not
+    depend on it)."""
+    _load().oracle_set_num_threads(int(n))

@@ -335,3 +335,15 @@ int oracle_num_threads(void)
     return 1;
 #endif
 }
+
+/* Threads of the parallel loops from now on (timing runs: all host cores,
+ * then one).  No effect on any result: every output is computed by one
+ * thread in a fixed order. */
+void oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
