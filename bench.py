@@ -75,25 +75,36 @@ CALL_KERNELS = {"unfused": "z_kernel + fused_gemv_kernel",
                               "mfma_product_kernel + mfma_epilogue_kernel (split K)"}
 
 
-def source_hash() -> str:
-    """Hash of the kernel and library sources' code (comments excluded)."""
+# the sources a schedule's launches are built from (the hash that keys its
+# counter records); other schedules' files may change without voiding them
+SCHED_FILES = {"fused_gemv": ["k_fused_gemv.hip", "biloco_device.h", "biloco_internal.h"],
+               "unfused": ["k_fused_gemv.hip", "biloco_device.h", "biloco_internal.h"],
+               "fused_mfma": ["k_fused_mfma.hip", "biloco_device.h", "biloco_internal.h"]}
+
+
+def source_hash(sched_name: str | None = None) -> str:
+    """Hash of the kernel sources' code (comments excluded): all of csrc/, or
+    only the files of one schedule's kernels."""
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "bit_weight_gemm_amd", "csrc", "*"))):
+    files = sorted(glob.glob(os.path.join(ROOT, "bit_weight_gemm_amd", "csrc", "*")))
+    if sched_name in SCHED_FILES:
+        files = [f for f in files if os.path.basename(f) in SCHED_FILES[sched_name]]
+    for f in files:
         with open(f, "r", encoding="utf-8") as fh:
             h.update(os.path.basename(f).encode())
             h.update(code_text(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(cfg: int, sched_name: str, src_hash: str):
+def measured_traffic(cfg: int, sched_name: str):
     """HBM bytes per call from the committed rocprofv3 --pmc summary, if it was
-    taken on the current kernel sources; else None."""
+    taken on the current sources of the schedule's kernels; else None."""
     path = os.path.join(ROOT, "profiles", f"traffic_{sched_name}_config{cfg}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         d = json.load(f)
-    if d.get("source_hash") != src_hash:
+    if d.get("source_hash") != source_hash(sched_name):
         return None
     return d.get("bytes_per_call")
 
@@ -325,11 +336,16 @@ def main() -> int:
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no GPU work: turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
                          "this script into profiles/traffic_<schedule>_config<c>.json and .md")
+    ap.add_argument("--busy-summary", metavar="PMC_DIR",
+                    help="no GPU work: turn a rocprofv3 --pmc run of BUSY_COUNTERS into "
+                         "profiles/busy_<schedule>_config<c>.json")
     ap.add_argument("--only", choices=["weight-quant", "decompose", "stream-floor"],
                     help="time only this NEXT-row operation and print its JSON (for profiling)")
     args = ap.parse_args()
     if args.traffic_summary:
         return traffic_summary(args)
+    if args.busy_summary:
+        return busy_summary(args)
     if args.only:
         import torch
         assert torch.cuda.is_available(), "bench.py needs a GPU"
@@ -395,7 +411,7 @@ def main() -> int:
     t_call = gemm_call_time(prob, sched, rot, min(K_steps, 400))
     achieved = nbytes / t_call / 1e9
     t_warm = gemm_call_time(prob, sched, None, 200)
-    traffic = measured_traffic(cfg, sched_name, src_hash)
+    traffic = measured_traffic(cfg, sched_name) if args.rank is None else None
 
     out = {
         "metric": METRIC,
@@ -509,6 +525,67 @@ def _pmc_rows(directory: str):
     return rows
 
 
+BUSY_COUNTERS = ["GRBM_GUI_ACTIVE", "GRBM_COUNT", "SQ_BUSY_CU_CYCLES", "SQ_ACTIVE_INST_VALU",
+                 "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_CYCLES"]
+
+
+def busy_summary(args) -> int:
+    """Busy counters per product launch from one rocprofv3 --pmc run of this
+    script (BUSY_COUNTERS, one pass): per kernel, the median over its
+    dispatches of each counter, and three ratios.
+
+    Units as the counters read on MI355X (8 XCDs, 32 CUs and 4 shader engines
+    each): GRBM_GUI_ACTIVE is summed over the XCDs and SQ_CYCLES over the
+    shader engines (it reads 4 GRBM_GUI_ACTIVE for every kernel);
+    SQ_BUSY_CU_CYCLES is clock cycles summed over the 256 CUs;
+    SQ_VALU_MFMA_BUSY_CYCLES is cycles summed over the 1024 SIMDs (a
+    16x16x32 f16 MFMA adds 16); SQ_ACTIVE_INST_VALU is quad-cycles summed
+    over the SIMDs.
+      cu_busy_us  = SQ_BUSY_CU_CYCLES / 256 / 2400 MHz: the time an average
+                    CU had work of the kernel (the profiler's GUI window,
+                    window_us, also holds the dispatch set-up);
+      mfma_frac   = SQ_VALU_MFMA_BUSY_CYCLES / (4 SQ_BUSY_CU_CYCLES): the
+                    matrix cores' share of the SIMD cycles while CUs were busy;
+      valu_frac   = 4 SQ_ACTIVE_INST_VALU / (4 SQ_BUSY_CU_CYCLES): the same
+                    for vector ALU instructions."""
+    import statistics
+    from bit_weight_gemm_amd import workloads as wl
+    from bit_weight_gemm_amd import binding as B
+    directory = args.busy_summary
+    cfg = args.config
+    d = wl.make_config(cfg)
+    sched = args.schedule or B.biloco_default_schedule(d["M"], d["N"], d["K"], d["r"])
+    sched_name = SCHED_NAMES.get(sched, str(sched))
+    per = {}
+    for k, c, v in _pmc_rows(directory):
+        if "biloco::" in k and "quant_act" not in k and "pack_signs" not in k:
+            per.setdefault(k.split("(")[0], {}).setdefault(c, []).append(v)
+    kernels = {}
+    for k, cs in per.items():
+        med = {c: statistics.median(v) for c, v in cs.items()}
+        row = {"counters": med}
+        if med.get("GRBM_GUI_ACTIVE"):
+            row["window_us"] = round(med["GRBM_GUI_ACTIVE"] / 8 / 2400, 3)
+        busy = med.get("SQ_BUSY_CU_CYCLES")
+        if busy:
+            row["cu_busy_us"] = round(busy / 256 / 2400, 3)
+            row["mfma_frac"] = round(med.get("SQ_VALU_MFMA_BUSY_CYCLES", 0) / (4 * busy), 4)
+            row["valu_frac"] = round(med.get("SQ_ACTIVE_INST_VALU", 0) / busy, 4)
+        kernels[k] = row
+    out = {"config": cfg, "schedule": sched_name, "source_hash": source_hash(sched_name),
+           "counters": BUSY_COUNTERS, "kernels": kernels}
+    with open(os.path.join(ROOT, "profiles", f"busy_{sched_name}_config{cfg}.json"), "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+    return 0
+
+
+def _is_step_variant(name: str) -> bool:
+    """fused_gemv_kernel<MM, KBL, ZMODE, true>: the launch that quantises the
+    activation itself (a step), not the product call's kernel."""
+    return "fused_gemv_kernel<" in name and name.rstrip().endswith("true>")
+
+
 def traffic_summary(args) -> int:
     """HBM bytes per product call from rocprofv3 --pmc runs of this script.
 
@@ -539,15 +616,18 @@ def traffic_summary(args) -> int:
             if "biloco::" in k and "quant_act" not in k and "pack_signs" not in k:
                 per_kernel.setdefault(k.split("(")[0], []).append(v)
         kernels = {k: statistics.median(v) * factor for k, v in per_kernel.items()}
+        # the one-launch M <= 2 kernel has a variant that also quantises the
+        # activation (the step's); the call launches the other one
+        call = {k: b for k, b in kernels.items() if not _is_step_variant(k)}
         res[counter] = {"factor_bytes_per_unit": factor, "copy_units_median": kib_copy,
-                        "per_kernel_bytes": kernels, "call_bytes": sum(kernels.values())}
+                        "per_kernel_bytes": kernels, "call_bytes": sum(call.values())}
     bytes_per_call = res["FETCH_SIZE"]["call_bytes"] + res["WRITE_SIZE"]["call_bytes"]
     sched_name = args.sched_name if hasattr(args, "sched_name") else None
     from bit_weight_gemm_amd import binding as B
     sched = args.schedule or B.biloco_default_schedule(d["M"], d["N"], d["K"], d["r"])
     sched_name = SCHED_NAMES.get(sched, str(sched))
     nb = algorithmic_bytes(d["M"], d["N"], d["K"], d["r"])
-    out = {"config": cfg, "schedule": sched_name, "source_hash": source_hash(),
+    out = {"config": cfg, "schedule": sched_name, "source_hash": source_hash(sched_name),
            "bytes_per_call": round(bytes_per_call), "algorithmic_bytes": nb,
            "ratio_to_algorithmic": round(bytes_per_call / nb, 4),
            "fetch": res["FETCH_SIZE"], "write": res["WRITE_SIZE"],
