@@ -27,7 +27,7 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, 10^9 B/s
 ROT_BYTES = 1.2e9              # distinct weight bytes a timed graph walks through
 SCHED_NAMES = {1: "unfused", 2: "fused_gemv", 3: "fused_mfma", 4: "composed",
-               5: "composed_mfma"}
+               5: "composed_mfma", 6: "mfma_allwg"}
 METRIC = "fused GEMM µs/call + effective HBM GB/s (% peak) at M=1..32, r=512"
 
 
@@ -78,6 +78,7 @@ CALL_KERNELS = {"unfused": "z_kernel + fused_gemv_kernel",
 # the sources a schedule's launches are built from (the hash that keys its
 # counter records); other schedules' files may change without voiding them
 SCHED_FILES = {"fused_gemv": ["k_fused_gemv.hip", "biloco_device.h", "biloco_internal.h"],
+               "mfma_allwg": ["k_fused_mfma.hip", "biloco_device.h", "biloco_internal.h"],
                "unfused": ["k_fused_gemv.hip", "biloco_device.h", "biloco_internal.h"],
                "fused_mfma": ["k_fused_mfma.hip", "biloco_device.h", "biloco_internal.h"]}
 
@@ -339,11 +340,19 @@ def main() -> int:
     ap.add_argument("--busy-summary", metavar="PMC_DIR",
                     help="no GPU work: turn a rocprofv3 --pmc run of BUSY_COUNTERS into "
                          "profiles/busy_<schedule>_config<c>.json")
+    ap.add_argument("--timeline", action="store_true",
+                    help="per-wave stamps of one call of --config/--schedule, read from the "
+                         "timeline build (libbiloco_tl.so); writes profiles/timeline_*.md")
+    ap.add_argument("--timeline-r0", action="store_true", help="--timeline with r = 0")
+    ap.add_argument("--timeline-step", action="store_true",
+                    help="--timeline of the quantising call (biloco_gemm_lowrank_quant)")
     ap.add_argument("--only", choices=["weight-quant", "decompose", "stream-floor"],
                     help="time only this NEXT-row operation and print its JSON (for profiling)")
     args = ap.parse_args()
     if args.traffic_summary:
         return traffic_summary(args)
+    if args.timeline:
+        return timeline(args)
     if args.busy_summary:
         return busy_summary(args)
     if args.only:
@@ -470,6 +479,13 @@ def main() -> int:
             # the same product as separate launches (plain product, z, correction)
             tcomp = gemm_call_time(pc, B.BILOCO_SCHED_COMPOSED, rc, calls)
             tcm = gemm_call_time(pc, B.BILOCO_SCHED_COMPOSED_MFMA, rc, calls)
+            # the matrix-core schedules side by side (z in a launch of its own,
+            # and every workgroup computing a tile of z at entry)
+            mfma_times = {}
+            for ms in (B.BILOCO_SCHED_FUSED_MFMA, B.BILOCO_SCHED_MFMA_ALLWG):
+                if ms in B.biloco_schedules_for(pc.M, pc.N, pc.K, pc.r):
+                    mfma_times[SCHED_NAMES[ms] + "_us_per_call"] = round(
+                        gemm_call_time(pc, ms, rc, calls) * 1e6, 3)
             bc = algorithmic_bytes(pc.M, pc.N, pc.K, pc.r)
             del rc, pc
             torch.cuda.empty_cache()
@@ -491,7 +507,8 @@ def main() -> int:
                                    "correction_overhead": round(tc / tz - 1.0, 4),
                                    "composed_us_per_call": round(tcomp * 1e6, 3),
                                    "composed_mfma_us_per_call": round(tcm * 1e6, 3),
-                                   "speedup_vs_composed": round(min(tcomp, tcm) / tc, 3)}
+                                   "speedup_vs_composed": round(min(tcomp, tcm) / tc, 3),
+                                   **mfma_times}
         out["per_config"] = table
         out["weight_quant"] = weight_quant_table()
         out["decompose"] = decompose_time()
@@ -523,6 +540,117 @@ def _pmc_rows(directory: str):
             for row in csv.DictReader(fh):
                 rows.append((row["Kernel_Name"], row["Counter_Name"], float(row["Counter_Value"])))
     return rows
+
+
+TL_SLOTS = {
+    "gemv": ["start", "first row's loads issued", "every row's loads issued", "rows done",
+             "z values checked", "correction started", "stored"],
+    "mfma": ["start", "loads issued", "z tile counted in", "activation decoded", "row block 0 done",
+             "finisher known", "finisher done", "last row-block slot", "row blocks done",
+             "first correction word ready", "correction done", "stored"],
+}
+
+
+def timeline(args) -> int:
+    """Per-wave stamps (100 MHz real-time counter, in us from the earliest
+    workgroup start) of the last call of a graph of 20 calls over rotated
+    weights, from the timeline build of the library: quantiles over waves per
+    named point, printed as JSON and written to profiles/timeline_<schedule>_
+    <workload>.md with the command that made it."""
+    import ctypes
+    import numpy as np
+    import torch
+    from bit_weight_gemm_amd import binding as B
+    from bit_weight_gemm_amd import build as hb
+    from bit_weight_gemm_amd import workloads as wl
+    from bit_weight_gemm_amd.problem import DeviceProblem
+    if not os.path.exists(hb.TL_LIB):
+        raise SystemExit(f"{hb.TL_LIB} is missing: build it with __graft_entry__.build()")
+    B.LIB_PATH = hb.TL_LIB
+    L = B.lib()
+    cfg = args.config
+    d = wl.make_config(cfg, r=0 if args.timeline_r0 else None)
+    sched = args.schedule or B.biloco_default_schedule(d["M"], d["N"], d["K"], d["r"])
+    step = args.timeline_step
+    p = DeviceProblem(d, quantize=not step)
+    rot = Rotation(p, 20)
+
+    def one(i, st):
+        if step:
+            p.gemm_quant(sched, stream=st, **rot.kw(i))
+        else:
+            p.gemm(sched, stream=st, **rot.kw(i))
+    t, g = time_graph(one, 20)
+    fam = "gemv" if sched in (1, 2) and d["M"] <= 2 else "mfma"
+    zero = getattr(L, f"biloco_tl_{fam}_zero")
+    read = getattr(L, f"biloco_tl_{fam}_read")
+    read.argtypes = [ctypes.c_void_p, ctypes.c_int]
+    torch.cuda.synchronize()
+    assert zero() == 0
+    g.replay()
+    torch.cuda.synchronize()
+    n = 4096 * 8 * 16
+    buf = np.zeros(n, np.uint64)
+    assert read(buf.ctypes.data, n) == 0
+    tl = buf.reshape(4096, 8, 16).astype(np.int64)
+    wgs = np.nonzero(tl[:, 0, 0])[0]
+    tl = tl[wgs]
+    t0 = tl[:, :, 0][tl[:, :, 0] > 0].min()
+    rel = np.where(tl > 0, (tl - t0) * 0.01, np.nan)
+    names = TL_SLOTS[fam]
+    groups = {}
+    if fam == "gemv":
+        stream_wg = tl[:, 0, 1] > 0
+        groups["stream workgroups"] = (stream_wg, range(len(names)))
+        if (~stream_wg).any():
+            groups["side workgroups"] = (~stream_wg, [0, 2])
+    else:
+        groups["all workgroups"] = (np.ones(len(wgs), bool), [k for k in range(len(names)) if k != 6])
+        fin = tl[:, 0, 12] == 1
+        if fin.any():
+            groups["finisher workgroups"] = (fin, [6])
+    out = {"config": cfg, "r": d["r"], "schedule": SCHED_NAMES.get(sched, sched),
+           "call": "quantise + product" if step else "product", "us_per_call_timeline_build":
+           round(t * 1e6, 3), "workgroups": int(len(wgs)), "groups": {}}
+    if fam == "mfma":
+        out["finishers"] = int((tl[:, 0, 12] == 1).sum())
+        out["waves_computing_z_locally"] = int((tl[:, :, 13] == 1).sum())
+    for gname, (mask, slots) in groups.items():
+        rows = {}
+        for k in slots:
+            v = rel[mask, :, k].ravel()
+            v = v[~np.isnan(v)]
+            label = "z published" if gname.startswith("side") and k == 2 else names[k]
+            if v.size:
+                rows[label] = {q: round(float(np.percentile(v, pc)), 2) for q, pc in
+                                  (("min", 0), ("p10", 10), ("median", 50), ("p90", 90), ("max", 100))}
+                rows[label]["waves"] = int(v.size)
+        out["groups"][gname] = rows
+    cmd = "python3 bench.py --timeline --config %d%s%s%s" % (
+        cfg, f" --schedule {args.schedule}" if args.schedule else "",
+        " --timeline-r0" if args.timeline_r0 else "", " --timeline-step" if step else "")
+    wname = f"M{d['M']}_K{d['K']}_N{d['N']}_r{d['r']}"
+    lines = [f"# Timeline: {out['schedule']}, {out['call']}, M={d['M']} K={d['K']} N={d['N']} r={d['r']}", "",
+             "Command (repository root, one MI355X, after `__graft_entry__.build()`):", "", "```", cmd, "```", "",
+             "Per-wave stamps of the 100 MHz real-time counter at named points of the kernel "
+             "(the library built with BILOCO_TIMELINE), for the last call of a graph of 20 calls over "
+             "rotated weights; microseconds from the earliest workgroup start.  The stamps' stores "
+             f"slow the call a little: {out['us_per_call_timeline_build']} us per call in this build.", ""]
+    if fam == "mfma":
+        lines += [f"Finisher workgroups: {out['finishers']}; waves that computed z locally: "
+                  f"{out['waves_computing_z_locally']}.", ""]
+    for gname, rows in out["groups"].items():
+        lines += [f"## {gname}", "", "| point | waves | min | p10 | median | p90 | max |",
+                  "|---|---:|---:|---:|---:|---:|---:|"]
+        for k, v in rows.items():
+            lines.append(f"| {k} | {v['waves']} | {v['min']} | {v['p10']} | {v['median']} | {v['p90']} | {v['max']} |")
+        lines.append("")
+    tag = "_step" if step else ""
+    path = os.path.join(ROOT, "profiles", f"timeline_{out['schedule']}_{wname}{tag}.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines))
+    print(json.dumps(out), flush=True)
+    return 0
 
 
 BUSY_COUNTERS = ["GRBM_GUI_ACTIVE", "GRBM_COUNT", "SQ_BUSY_CU_CYCLES", "SQ_ACTIVE_INST_VALU",

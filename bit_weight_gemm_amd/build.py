@@ -31,9 +31,9 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-function"]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC] + COMMON + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, build_dir: str = BUILD, extra=()) -> str:
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC] + COMMON + list(extra) + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     p = subprocess.run(cmd, capture_output=True, text=True)
     if p.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{p.stderr}")
@@ -72,6 +72,29 @@ def build(verbose: bool = True) -> str:
     if verbose:
         print(f"built {LIB}")
     return LIB
+
+
+TL_BUILD = os.path.join(PKG, "_build_tl")
+TL_LIB = os.path.join(PKG, "libbiloco_tl.so")
+
+
+def build_timeline(verbose: bool = True) -> str:
+    """The same library compiled with BILOCO_TIMELINE: the product kernels
+    also write per-wave stamps of the real-time counter, which bench.py's
+    --timeline leg reads (a measurement build; never the product path)."""
+    os.makedirs(TL_BUILD, exist_ok=True)
+    srcs = [s for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(lambda s: _compile(s, TL_BUILD, ["-DBILOCO_TIMELINE"]), srcs))
+    tmp = TL_LIB + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
+    p = subprocess.run(cmd, capture_output=True, text=True)
+    if p.returncode != 0:
+        raise RuntimeError(f"link failed:\n{p.stderr}")
+    os.replace(tmp, TL_LIB)
+    if verbose:
+        print(f"built {TL_LIB}")
+    return TL_LIB
 
 
 if __name__ == "__main__":

@@ -28,6 +28,7 @@ bool schedule_allowed(int s, int M, int N, int K, int r) {
         case BILOCO_SCHED_FUSED_MFMA: return mfma_supported(M, N, K, r);
         case BILOCO_SCHED_COMPOSED:
         case BILOCO_SCHED_COMPOSED_MFMA: return composed_supported(M, N, K, r);
+        case BILOCO_SCHED_MFMA_ALLWG: return mfma_one_supported(M, N, K, r);
         default: return false;
     }
 }
@@ -204,7 +205,7 @@ biloco_status biloco_gemm_check(const void *a_codes, const void *a_scales, const
         {alpha_bf16, (size_t)r * 2},   {workspace, need}};
     for (auto &in : ins)
         if (overlaps(y_bf16, ny, in.p, in.n)) return BILOCO_ERR_INVALID_VALUE;
-    if (schedule < BILOCO_SCHED_AUTO || schedule > BILOCO_SCHED_COMPOSED_MFMA)
+    if (schedule < BILOCO_SCHED_AUTO || schedule > BILOCO_SCHED_MFMA_ALLWG)
         return BILOCO_ERR_INVALID_VALUE;
     if (schedule != BILOCO_SCHED_AUTO && !schedule_allowed(schedule, M, N, K, r))
         return BILOCO_ERR_UNSUPPORTED;
@@ -220,7 +221,7 @@ int32_t biloco_schedules_for(int32_t M, int32_t N, int32_t K, int32_t r, int32_t
                              int32_t cap) {
     if (check_shape(M, N, K, r) != BILOCO_OK) return 0;
     int32_t n = 0;
-    for (int s = BILOCO_SCHED_UNFUSED; s <= BILOCO_SCHED_COMPOSED_MFMA; ++s)
+    for (int s = BILOCO_SCHED_UNFUSED; s <= BILOCO_SCHED_MFMA_ALLWG; ++s)
         if (schedule_allowed(s, M, N, K, r)) {
             if (out && n < cap) out[n] = s;
             ++n;
@@ -250,6 +251,7 @@ biloco_status biloco_gemm_lowrank_sched(const uint8_t *a_codes, const uint8_t *a
         case BILOCO_SCHED_FUSED_MFMA: e = launch_gemm_mfma(a, stream); break;
         case BILOCO_SCHED_COMPOSED: e = launch_gemm_composed(a, false, stream); break;
         case BILOCO_SCHED_COMPOSED_MFMA: e = launch_gemm_composed(a, true, stream); break;
+        case BILOCO_SCHED_MFMA_ALLWG: e = launch_gemm_mfma_one(a, stream); break;
         default: e = launch_gemm_unfused(a, stream); break;
     }
     return e == hipSuccess ? BILOCO_OK : BILOCO_ERR_HIP;
@@ -301,6 +303,7 @@ biloco_status biloco_gemm_lowrank_quant(const uint16_t *x_bf16, uint8_t *a_codes
         case BILOCO_SCHED_FUSED_MFMA: e = launch_gemm_mfma(a, stream); break;
         case BILOCO_SCHED_COMPOSED: e = launch_gemm_composed(a, false, stream); break;
         case BILOCO_SCHED_COMPOSED_MFMA: e = launch_gemm_composed(a, true, stream); break;
+        case BILOCO_SCHED_MFMA_ALLWG: e = launch_gemm_mfma_one(a, stream); break;
         default: e = launch_gemm_unfused(a, stream); break;
     }
     return e == hipSuccess ? BILOCO_OK : BILOCO_ERR_HIP;

@@ -201,6 +201,51 @@ __device__ __forceinline__ uint32_t load1_nt(__amdgpu_buffer_rsrc_t r, int off) 
     return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, kPolicyNt);
 }
 
+// ---------------------------------------------------------------- timelines
+// Per-wave stamps of the 100 MHz real-time counter at named points of a
+// kernel, for the measurement build only (compiled with BILOCO_TIMELINE: a
+// library of its own; in the product library the macros are empty).  Slot
+// pt of wave w of workgroup b: tl[(b * 8 + w) * kTlSlots + pt], workgroups
+// below kTlMaxWorkgroups; written by lane 0 with an ordinary vector store.
+constexpr int kTlSlots = 16, kTlMaxWorkgroups = 4096;
+#ifdef BILOCO_TIMELINE
+#define BILOCO_TL_AT(buf, pt, v)                                                              \
+    do {                                                                                       \
+        if ((threadIdx.x & 63) == 0 && blockIdx.x < (unsigned)kTlMaxWorkgroups)               \
+            (buf)[((int)blockIdx.x * 8 + (int)(threadIdx.x >> 6)) * kTlSlots + (pt)] = (v);   \
+    } while (0)
+#else
+#define BILOCO_TL_AT(buf, pt, v) do { } while (0)
+#endif
+
+// ---------------------------------------------------------------- hand-offs
+// Values one workgroup publishes for others of the same launch.  Relaxed
+// agent-scope atomics are coherent per access across the XCDs' L2 caches
+// (sc1), with no cache-wide fence.  A tagged word carries the fp32 (or
+// 32-bit) value with the call's tag in its high half, so data and tag travel
+// together and a reader can tell a value of this call from a stale one.
+__device__ __forceinline__ uint32_t ld_u32(const uint32_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_u32(uint32_t *p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_tagged_u32(uint64_t *p, uint32_t v, uint32_t tag) {
+    __hip_atomic_store(p, ((uint64_t)tag << 32) | v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_tagged(uint64_t *p, float v, uint32_t tag) {
+    st_tagged_u32(p, __float_as_uint(v), tag);
+}
+// agent-scope loads (sc1) through a buffer resource: ordinary vector loads
+// for the wait counters
+constexpr int kPolicySc1 = 16;
+__device__ __forceinline__ uint64_t ld_tagged(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kPolicySc1));
+}
+__device__ __forceinline__ u32x4_t load16_sc1(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kPolicySc1));
+}
+
 // ---------------------------------------------------------------- reductions
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

@@ -111,7 +111,12 @@ hipError_t launch_gemm_fused_gemv(const GemmArgs &a, hipStream_t stream);
 hipError_t launch_gemm_gemv_two_launch(const GemmArgs &a, hipStream_t stream);
 hipError_t launch_z_gemv(const GemmArgs &a, float *z, hipStream_t stream);   // M <= 2
 bool gemv_supported(int M, int N, int K, int r);   // shapes the one-launch vector-ALU schedule handles
+// bound of a one-launch consumer's wait for z, in ticks of the 100 MHz
+// real-time counter; 0 makes consumers compute z themselves
+uint32_t spin_limit_default();
 hipError_t launch_gemm_mfma(const GemmArgs &a, hipStream_t stream);
+bool mfma_one_supported(int M, int N, int K, int r);   // shapes the one-launch matrix-core schedule handles
+hipError_t launch_gemm_mfma_one(const GemmArgs &a, hipStream_t stream);
 hipError_t launch_z_mfma(const GemmArgs &a, float *zf, hipStream_t stream);   // M >= 1, r >= 1
 // z = alpha (.) (x . V) as plain fp32 [M][rpad32(r)] at z (r > 0)
 hipError_t launch_z_fp32(const GemmArgs &a, float *z, hipStream_t stream);

@@ -53,6 +53,16 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kGemvThreads = 512;   // 8 waves per workgroup
 
+// measurement build only: per-wave stamps (slots: 0 start, 1 first row's
+// loads issued, 2 every row's loads issued (side workgroups: z published),
+// 3 rows done, 4 z values checked, 5 correction started, 6 stored)
+#ifdef BILOCO_TIMELINE
+__device__ uint64_t g_tl_gemv[kTlMaxWorkgroups * 8 * kTlSlots];
+#define TLG(pt) BILOCO_TL_AT(g_tl_gemv, pt, __builtin_amdgcn_s_memrealtime())
+#else
+#define TLG(pt) do { } while (0)
+#endif
+
 struct GemvParams {
     const uint8_t *a_codes;
     const uint8_t *a_scales;
@@ -106,12 +116,6 @@ __device__ __forceinline__ float scale_mant(float s) {
     return __uint_as_float((__float_as_uint(s) & 0x007FFFFFu) | 0x3F800000u);
 }
 
-__device__ __forceinline__ uint32_t ld_u32(const uint32_t *p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_u32(uint32_t *p, uint32_t v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 // Sum of one value over the 8 waves of the workgroup (red: 8 floats).
 __device__ __forceinline__ float block_sum8(float v, float *red) {
@@ -211,16 +215,6 @@ constexpr int kZXR = 16;      // ranks per side item: half of one 32-bit V word
 constexpr int kSideWorkgroups = 32;   // side workgroups per launch (at most)
 constexpr int kZXU = 3;       // k-quads per thread per round of side inputs
 
-__device__ __forceinline__ void st_tagged(uint64_t *p, float v, uint32_t tag) {
-    const uint64_t w = ((uint64_t)tag << 32) | __float_as_uint(v);
-    __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// agent-scope load (sc1) through a buffer resource, an ordinary vector load
-// for the wait counters
-constexpr int kPolicySc1 = 16;
-__device__ __forceinline__ uint64_t ld_tagged(__amdgpu_buffer_rsrc_t r, int off) {
-    return __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kPolicySc1));
-}
 
 template <int MM>
 struct ZXInputs {
@@ -368,6 +362,7 @@ __device__ void side_workgroup(const GemvParams &p, float (*slots)[kZXR * MM]) {
         if (it != b) zx_load<MM>(p, it, 0, in);
         zx_item<MM>(p, it, in, ep + 1u, slots);
     }
+    TLG(2);
     if (b == 0) {
         for (int j = 1 + threadIdx.x; j < (int)gridDim.x; j += kGemvThreads)
             while (ld_u32(p.seen + j) != ep + 1u) __builtin_amdgcn_s_sleep(2);
@@ -507,6 +502,7 @@ __global__ void __launch_bounds__(kGemvThreads) fused_gemv_kernel(GemvParams p) 
 
     // the wave index as a scalar, so that the row count below is one too
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    TLG(0);
     const int KB = p.K >> 4, KH = p.K >> 1;
     uint32_t *s_act = s_dyn;
     float *s_z = reinterpret_cast<float *>(s_dyn + (size_t)MM * KB * 8);
@@ -784,6 +780,7 @@ __global__ void __launch_bounds__(kGemvThreads) fused_gemv_kernel(GemvParams p) 
         // others
         load_row(0);
         __builtin_amdgcn_sched_barrier(0);
+        TLG(1);
         if constexpr (ZMODE == 1) z_request(zv);
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (ZMODE == 1) z_produce();
@@ -791,6 +788,7 @@ __global__ void __launch_bounds__(kGemvThreads) fused_gemv_kernel(GemvParams p) 
 #pragma unroll
         for (int rr = 1; rr < NR; ++rr) load_row(rr);
         __builtin_amdgcn_sched_barrier(0);
+        TLG(2);
 
         // the lane's activation, decoded while the rows stream in (its words
         // pass an empty asm here, so that neither the decode nor its wait is
@@ -874,6 +872,7 @@ __global__ void __launch_bounds__(kGemvThreads) fused_gemv_kernel(GemvParams p) 
             break;
     }
 
+    TLG(3);
     // 9. one launch: z into LDS, then the correction.  Values whose tag is not
     // yet this call's are re-read within a bounded time, and computed here if
     // still missing.
@@ -900,7 +899,9 @@ __global__ void __launch_bounds__(kGemvThreads) fused_gemv_kernel(GemvParams p) 
                                           : z_local(p, m, i);
             }
         }
+        TLG(4);
         __syncthreads();
+        TLG(5);
         add_correction<MM, R, R, QMAX>(p, s_z, ul, part);
     }
 
@@ -915,6 +916,7 @@ __global__ void __launch_bounds__(kGemvThreads) fused_gemv_kernel(GemvParams p) 
                 else p.y[(int64_t)m * p.N + row0 + rr] = f32_to_bf16_rne(sum);
             }
         }
+    TLG(6);
 }
 
 // z[m][i] into its correction operand slot: index i = 32 w + 16 h + 4 j + g
@@ -1037,14 +1039,6 @@ hipError_t launch_m(const GemvParams &p, int kbl, int grid, size_t lds, int zmod
     }
 }
 
-uint32_t spin_limit_default() {
-    // the bound of a consumer's wait for a z value, in ticks of the 100 MHz
-    // real-time counter (100 us).  Debug override (BILOCO_DEBUG_SPIN_LIMIT):
-    // 0 makes every consumer compute z itself, so that tests can run the
-    // fallback from the host.
-    const char *s = getenv("BILOCO_DEBUG_SPIN_LIMIT");
-    return s ? (uint32_t)strtoul(s, nullptr, 10) : 10000u;
-}
 
 int kbl_of(int K) { return (K / 16 + 63) / 64; }
 // the instantiated KBL a K runs with (see launch_m)
@@ -1062,6 +1056,15 @@ void gemv_grid(int N, int kbl, int mm, int *wgs, int *rows_per_wg) {
     *wgs = (N + rpg - 1) / rpg;
 }
 }  // namespace
+
+uint32_t spin_limit_default() {
+    // the bound of a consumer's wait for a z value, in ticks of the 100 MHz
+    // real-time counter (100 us).  Debug override (BILOCO_DEBUG_SPIN_LIMIT):
+    // 0 makes every consumer compute z itself, so that tests can run the
+    // fallback from the host.
+    const char *s = getenv("BILOCO_DEBUG_SPIN_LIMIT");
+    return s ? (uint32_t)strtoul(s, nullptr, 10) : 10000u;
+}
 
 bool gemv_supported(int M, int N, int K, int r) {
     const int kbl = kbl_of(K);
@@ -1183,4 +1186,14 @@ hipError_t launch_gemm_gemv_two_launch(const GemmArgs &a, hipStream_t stream) {
     return launch_gemv(a, true, stream);
 }
 
+#ifdef BILOCO_TIMELINE
+extern "C" int biloco_tl_gemv_zero() {
+    static uint64_t z[kTlMaxWorkgroups * 8 * kTlSlots];
+    return (int)hipMemcpyToSymbol(HIP_SYMBOL(g_tl_gemv), z, sizeof(z), 0, hipMemcpyHostToDevice);
+}
+extern "C" int biloco_tl_gemv_read(uint64_t *host, int n) {
+    if (n < 0 || n > kTlMaxWorkgroups * 8 * kTlSlots) return -1;
+    return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(g_tl_gemv), (size_t)n * 8, 0, hipMemcpyDeviceToHost);
+}
+#endif
 }  // namespace biloco

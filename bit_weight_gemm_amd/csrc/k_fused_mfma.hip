@@ -61,6 +61,20 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
+// measurement build only: per-wave stamps of the product kernel (slots:
+// 0 start, 1 loads issued, 2 z tile counted in, 3 activation decoded, 4 row
+// block 0 done, 5 finisher known, 6 finisher done, 7 last row-block slot
+// reached, 8 row blocks done, 9 first correction word ready, 10 correction
+// done, 11 stored; values: 12 finisher flag, 13 z computed locally)
+#ifdef BILOCO_TIMELINE
+__device__ uint64_t g_tl_mfma[kTlMaxWorkgroups * 8 * kTlSlots];
+#define TLM(pt) BILOCO_TL_AT(g_tl_mfma, pt, __builtin_amdgcn_s_memrealtime())
+#define TLMV(pt, v) BILOCO_TL_AT(g_tl_mfma, pt, (uint64_t)(v))
+#else
+#define TLM(pt) do { } while (0)
+#define TLMV(pt, v) do { } while (0)
+#endif
+
 constexpr int kZThreads = 512;          // z kernel: 8 waves
 constexpr int kZWaves = kZThreads / 64;
 constexpr int kZStepsPerWave = 4;       // K-steps (32 k) per wave in the z kernel
@@ -122,6 +136,15 @@ struct MfmaParams {
     // product kernel
     int S, cps, chunks, RB, Gs;
     float *ypart;               // [S][RB][MB][64 lanes][4] (D layout)
+    // one launch (z computed by every workgroup at entry)
+    uint32_t *epoch;            // workspace header word 0
+    uint32_t *seen;             // workspace header flags, one per workgroup
+    float *zpt;                 // tile partials of z [ntiles][MB 2][64 lanes][4] (D layout)
+    uint64_t *zat;              // z operands as tagged words [W][MB][2 hi/lo][64 lanes][4]
+    int P, psteps;              // K-parts per word and K-steps per part
+    int ntiles;                 // W P tiles, tile t = part W + word
+    int g8;                     // workgroups per XCD that hold a tile (0: tile = workgroup index)
+    uint32_t spin_limit;        // bound of a wait on z, in 100 MHz ticks; 0 = compute z locally
 };
 
 // One output element: bf16 into y, or fp32 into yf when the caller asked for it.
@@ -343,6 +366,47 @@ __global__ void __launch_bounds__(kZrThreads) mfma_zreduce_kernel(MfmaParams p) 
 }
 
 // =====================================================================
+// one launch: z of one word computed by one wave alone (the fallback after
+// a bounded wait for the finisher's words ran out; slow, plain loads)
+// =====================================================================
+constexpr int kZsw = 4;          // z-tile K-steps per wave loaded at once
+constexpr int kMaxZParts = 16;   // K-parts per word (the finisher loads them all at once)
+
+// Lane (col = lane % 16, q = lane / 16) builds, per m-block, the correction
+// operand words of z[m][32 w + 4 q + j] and z[m][32 w + 4 q + j + 16]
+// (m = 16 mb + col), bf16 high and low parts, as the finisher does.
+template <int MB>
+__device__ __forceinline__ void z_word_local(const MfmaParams &p, int w, int lane, u32x4_t (&zz)[MB][2]) {
+    const int col = lane & 15, q = lane >> 4;
+    for (int mb = 0; mb < MB; ++mb) {
+        const int m = 16 * mb + col;
+        float acc[8];
+        for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
+        if (m < p.M) {
+            for (int k = 0; k < p.K; ++k) {
+                const float xv = bf16_to_f32(p.x[(int64_t)m * p.K + k]);
+                const uint32_t vw = p.v[(int64_t)w * p.K + k];
+                for (int j = 0; j < 8; ++j) {
+                    const int ii = 4 * q + (j & 3) + 16 * (j >> 2);
+                    acc[j] += ((vw >> ii) & 1u) ? -xv : xv;
+                }
+            }
+        }
+        for (int j = 0; j < 4; ++j) {
+            uint32_t hi[2], lo[2];
+            for (int t = 0; t < 2; ++t) {
+                const int i = 32 * w + 4 * q + j + 16 * t;
+                const float z = (i < p.r && m < p.M) ? acc[j + 4 * t] * bf16_to_f32(p.alpha[i]) : 0.0f;
+                hi[t] = f32_to_bf16_rne(z);
+                lo[t] = f32_to_bf16_rne(z - bf16_to_f32(hi[t]));
+            }
+            zz[mb][0][j] = hi[0] | (hi[1] << 16);
+            zz[mb][1][j] = lo[0] | (lo[1] << 16);
+        }
+    }
+}
+
+// =====================================================================
 // launch 2: the product
 // =====================================================================
 // Workgroup (slice s, row-block range).  Wave q owns the chunks
@@ -356,17 +420,69 @@ __global__ void __launch_bounds__(kZrThreads) mfma_zreduce_kernel(MfmaParams p) 
 // (row block past the range, chunk past the wave's share) loads zeros
 // through an out-of-range buffer offset, so every path issues the same loads
 // and the hardware wait counts stay exact.
-template <int MB, int RBW, int CPW>
+template <int MB, int RBW, int CPW, bool ONE>
 __global__ void __launch_bounds__(kPThreads) mfma_product_kernel(MfmaParams p) {
     constexpr int PPR = scale_pieces(CPW);              // 16-byte scale pieces per row
     constexpr int kPipe = MfmaShape<MB>::kPipe;
+    static_assert(!ONE || RBW >= 3, "the z tile's wave sums use the last two row-block slots");
     // LDS: the waves' partial sums [wave][row block][mb][64 lanes], then each
-    // wave's block scales of R [wave][row][PPR 16-byte pieces]
+    // wave's block scales of R [wave][row][PPR 16-byte pieces].  One launch:
+    // the finisher's sums [512] and its transpose of z [MB 16][32] use the
+    // waves' slots of the last row block (free until that row block ends) for
+    // two m-blocks, a region of their own after the scales for one.
     extern __shared__ float4_t s_part[];
     u32x4_t *s_sc = reinterpret_cast<u32x4_t *>(s_part + (size_t)kPWaves * RBW * MB * 64);
+    float4_t *s_tail = reinterpret_cast<float4_t *>(s_sc + (size_t)kPWaves * RBW * 16 * PPR);
+    auto fin_at = [&](int t) -> float4_t & {
+        if constexpr (MB == 2) return s_part[((size_t)(t >> 6) * RBW + RBW - 1) * MB * 64 + (t & 63)];
+        else return s_tail[t];
+    };
+    auto zt_at = [&](int m, int i) -> float & {
+        if constexpr (MB == 2)
+            return reinterpret_cast<float *>(s_part + ((size_t)(m >> 3) * RBW + RBW - 1) * MB * 64 + 64)[(m & 7) * 32 + i];
+        else return reinterpret_cast<float *>(s_tail + kPThreads)[m * 32 + i];
+    };
+    __shared__ uint32_t s_flag;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int col = lane & 15, grp = lane >> 4;
     const int KH = p.K >> 1, KB = p.K >> 4;
+    TLM(0);
+
+    // ---- one launch: the call's epoch, and this workgroup's z tile (word
+    // zw, K-part zkp), whose inputs are requested before anything else
+    uint32_t ep = 0;
+    if constexpr (ONE) ep = ld_u32(p.epoch);
+    int zt = p.ntiles;
+    if constexpr (ONE) {
+        const int xq = blockIdx.x & 7, jq = blockIdx.x >> 3;
+        zt = p.g8 > 0 ? (jq < p.g8 ? xq * p.g8 + jq : p.ntiles) : (int)blockIdx.x;
+    }
+    const bool has_tile = ONE && zt < p.ntiles;
+    const int zw = has_tile ? zt % p.W : 0, zkp = has_tile ? zt / p.W : 0;
+    const int zst0 = zkp * p.psteps;
+    const int znst = has_tile ? min(p.psteps, (p.K >> 5) - zst0) : 0;
+    constexpr int ZU = ONE ? kZsw : 1;
+    u32x4_t zx[ZU][MB], zv[ZU][2];
+    const __amdgpu_buffer_rsrc_t r_x = buffer_of(p.x, ONE ? (int64_t)p.M * p.K * 2 : 0);
+    const __amdgpu_buffer_rsrc_t r_v = buffer_of(p.v + (ONE ? (int64_t)zw * p.K : 0), ONE ? (int64_t)p.K * 4 : 0);
+    // K-steps round * 8 kZsw + wave + 8 u of the part (rows past M and steps
+    // past the part read zeros)
+    auto z_load = [&](int round) {
+#pragma unroll
+        for (int u = 0; u < ZU; ++u) {
+            const int st = round * kPWaves * ZU + wave + kPWaves * u;
+            const bool ok = st < znst;
+            const int k0 = (zst0 + st) * 32 + 8 * grp;
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                const int m = 16 * mb + col;
+                zx[u][mb] = load16(r_x, opaque(ok && m < p.M ? (m * p.K + k0) * 2 : kOob));
+            }
+            zv[u][0] = load16(r_v, opaque(ok ? k0 * 4 : kOob));
+            zv[u][1] = load16(r_v, opaque(ok ? k0 * 4 + 16 : kOob));
+        }
+    };
+    if (has_tile) z_load(0);
     const int s = blockIdx.x % p.S, wgi = blockIdx.x / p.S;
     const int rb_begin = (int)((int64_t)wgi * p.RB / p.Gs);      // Gs row groups of <= RBW blocks
     const int rb_end = (int)((int64_t)(wgi + 1) * p.RB / p.Gs);
@@ -430,7 +546,18 @@ __global__ void __launch_bounds__(kPThreads) mfma_product_kernel(MfmaParams p) {
         }
     };
     const bool has_corr = wave < nws;
-    if (has_corr) corr_load(wave);
+    auto u_load = [&](int wi) {
+        const int w = s + p.S * wi;
+#pragma unroll
+        for (int rbl = 0; rbl < RBW; ++rbl) {
+            const int n = min((pb + min(rbl, nrb - 1)) * 16 + col, p.N - 1);
+            uw[rbl] = p.u[(int64_t)w * p.N + n];
+        }
+    };
+    if (has_corr) {
+        if constexpr (ONE) u_load(wave);
+        else corr_load(wave);
+    }
 
     // ---- code loads of R: the first kPipe row blocks now, each further one
     // once the row block kPipe before it is done.  Issued all at once, the
@@ -462,6 +589,80 @@ __global__ void __launch_bounds__(kPThreads) mfma_product_kernel(MfmaParams p) {
     for (int rbl = 0; rbl < RBW; ++rbl)
         if (rbl < kPipe) load_rb(rbl);
     __builtin_amdgcn_sched_barrier(0);
+
+    TLM(1);
+    // ---- one launch: the epoch has been read (the bookkeeper may advance it
+    // once every workgroup says so); the z tile: x . V+- over the part, every
+    // m, the 32 ranks of word zw, by all 8 waves, summed in LDS by wave 0,
+    // which stores the tile's partial, waits for the store, and counts the
+    // tile in (the last of the P tiles of a word finishes it further down)
+    uint32_t zold = 0;
+    if constexpr (ONE) {
+        if (threadIdx.x == 0) st_u32(p.seen + blockIdx.x, ep + 1u);
+        if (has_tile) {
+            float4_t zacc[MB][2];
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) zacc[mb][0] = zacc[mb][1] = float4_t{0.f, 0.f, 0.f, 0.f};
+            auto z_mfma = [&](int round) {
+#pragma unroll
+                for (int u = 0; u < ZU; ++u) {
+                    if (round * kPWaves * ZU + wave + kPWaves * u < znst) {
+                        const uint32_t vw[8] = {zv[u][0].x, zv[u][0].y, zv[u][0].z, zv[u][0].w,
+                                                zv[u][1].x, zv[u][1].y, zv[u][1].z, zv[u][1].w};
+#pragma unroll
+                        for (int ib = 0; ib < 2; ++ib) {
+                            const int bit = 16 * ib + col;
+                            u32x4_t bv;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                bv[e] = (((vw[2 * e] >> bit) & 1u) << 15) |
+                                        (((vw[2 * e + 1] >> bit) & 1u) << 31) | 0x3F803F80u;
+#pragma unroll
+                            for (int mb = 0; mb < MB; ++mb) zacc[mb][ib] = mfma_bf16(zx[u][mb], bv, zacc[mb][ib]);
+                        }
+                    }
+                }
+            };
+            z_mfma(0);
+            for (int round = 1; round * kPWaves * ZU < znst; ++round) {
+                z_load(round);
+                z_mfma(round);
+            }
+            float4_t *zslot = s_part + ((size_t)wave * RBW + RBW - 2) * MB * 64 + lane;
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int ib = 0; ib < 2; ++ib) zslot[(mb * 2 + ib) * 64] = zacc[mb][ib];
+            __syncthreads();
+            if (wave == 0) {
+#pragma unroll
+                for (int q = 1; q < kPWaves; ++q)
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                        for (int ib = 0; ib < 2; ++ib)
+                            zacc[mb][ib] += s_part[((size_t)q * RBW + RBW - 2) * MB * 64 + (mb * 2 + ib) * 64 + lane];
+            }
+            __syncthreads();
+            if (wave == 0) {
+                uint64_t *dst = reinterpret_cast<uint64_t *>(p.zpt) + ((size_t)zt * MB * 2 * 64 + lane) * 2;
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                    for (int ib = 0; ib < 2; ++ib) {
+                        const float4_t v = zacc[mb][ib];
+                        uint64_t *d = dst + (size_t)(mb * 2 + ib) * 64 * 2;
+                        __hip_atomic_store(d, ((uint64_t)__float_as_uint(v[1]) << 32) | __float_as_uint(v[0]),
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        __hip_atomic_store(d + 1, ((uint64_t)__float_as_uint(v[3]) << 32) | __float_as_uint(v[2]),
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    }
+                stores_done();
+                if (lane == 0) zold = arrive(p.zcnt + zw);
+            }
+            TLM(2);
+        }
+    }
 
     // this wave's scale windows go to its own LDS region, row block by row
     // block (no barrier: only this wave reads them)
@@ -503,18 +704,104 @@ __global__ void __launch_bounds__(kPThreads) mfma_product_kernel(MfmaParams p) {
                                       : dequant8(act_c[c][mb][d], s_hi, m_hi);
         }
 
+    // ---- one launch: the finisher of a word (the workgroup whose tile came
+    // in last) sums the word's P tile partials, scales by alpha, splits into
+    // bf16 high and low parts in the correction operand's layout and
+    // publishes them as tagged words.  It learns that it is the last after
+    // its first row blocks (the count's reply has come back by then), loads
+    // the partials ahead of the next row block's codes and finishes two row
+    // blocks later, when they have arrived.
+    constexpr int NF4 = MB * 128;                      // float4 per tile partial
+    constexpr int FJ = kMaxZParts * NF4 / kPThreads;   // partial float4 per thread
+    const int f_idx = threadIdx.x % NF4, f_p0 = threadIdx.x / NF4, f_step = kPThreads / NF4;
+    float4_t fin[FJ];
+    const __amdgpu_buffer_rsrc_t r_zp =
+        buffer_of(p.zpt, ONE ? (int64_t)p.ntiles * NF4 * 16 : 0);
+    auto fin_load = [&]() {
+#pragma unroll
+        for (int j = 0; j < FJ; ++j) {
+            const int kp = f_p0 + f_step * j;
+            const bool ok = kp < p.P;
+            fin[j] = __builtin_bit_cast(float4_t,
+                load16_sc1(r_zp, opaque(ok ? ((kp * p.W + zw) * NF4 + f_idx) * 16 : kOob)));
+        }
+    };
+    auto finish = [&]() {
+        float4_t sum = fin[0];
+#pragma unroll
+        for (int j = 1; j < FJ; ++j) sum += fin[j];
+        fin_at(threadIdx.x) = sum;
+        __syncthreads();
+        if ((int)threadIdx.x < NF4) {
+            float4_t v = fin_at(threadIdx.x);
+            for (int gq = 1; gq < f_step; ++gq) v += fin_at(gq * NF4 + threadIdx.x);
+            const int l = threadIdx.x & 63, blk = threadIdx.x >> 6, mb = blk >> 1, ib = blk & 1;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) zt_at(16 * mb + 4 * (l >> 4) + e, 16 * ib + (l & 15)) = v[e];
+        }
+        __syncthreads();
+        const uint32_t tag = ep + 1u;
+#pragma unroll
+        for (int idx0 = 0; idx0 < MB * 512; idx0 += kPThreads) {
+            const int idx = idx0 + threadIdx.x;
+            const int j = idx & 7, l = (idx >> 3) & 63, mb = idx >> 9;
+            const int m = 16 * mb + (l & 15), q = l >> 4;
+            const int ii = 4 * q + (j & 3) + 16 * (j >> 2);
+            const int i = 32 * zw + ii;
+            const float al = bf16_to_f32(p.alpha[i < p.r ? i : p.r - 1]);
+            const float zz = (i < p.r && m < p.M) ? zt_at(m, ii) * al : 0.0f;
+            const uint32_t zh = f32_to_bf16_rne(zz);
+            const uint32_t zl = f32_to_bf16_rne(zz - bf16_to_f32(zh));
+            const uint32_t oh = __shfl_xor(zh, 4, 64), ol = __shfl_xor(zl, 4, 64);
+            if (j < 4) {
+                uint64_t *dst = p.zat + ((((size_t)zw * MB + mb) * 2) * 64 + l) * 4 + j;
+                st_tagged_u32(dst, zh | (oh << 16), tag);
+                st_tagged_u32(dst + 64 * 4, zl | (ol << 16), tag);
+            }
+        }
+        // every tile of the word has been counted: ready for the next call
+        if (threadIdx.x == 0) st_u32(p.zcnt + zw, 0u);
+        // the LDS it used holds row-block sums again from here on
+        __syncthreads();
+    };
+    // (kA <= 1 and kB <= RBW - 2 keep the partials' registers and the
+    // prefetched z words, taken at row block RBW - 1, from ever being live
+    // at once)
+    const int kA = min(1, nrb - 1), kB = min(min(kA + 2, nrb - 1), RBW - 2);
+    bool last = false;
+
+    // ---- one launch: this wave's first correction word, as tagged words,
+    // requested at the start of the last row-block slot (the last row block
+    // of a workgroup with a full range)
+    u32x4_t za[MB][2][2];
+    const __amdgpu_buffer_rsrc_t r_za = buffer_of(p.zat, ONE ? (int64_t)p.W * MB * 2 * 64 * 4 * 8 : 0);
+    auto za_load = [&](int wi) {
+        const int w = s + p.S * wi;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf)
+                    za[mb][h][hf] = load16_sc1(r_za, opaque(((((w * MB + mb) * 2 + h) * 64 + lane) * 4 + 2 * hf) * 8));
+    };
+
+    TLM(3);
     // ---- per row block: the correction of this wave's first word, then the
     // wave's chunks of the product, into the wave's own LDS slot
     float4_t *mine = s_part + (size_t)wave * RBW * MB * 64 + lane;
 #pragma unroll
     for (int rbl = 0; rbl < RBW; ++rbl) {
         if (lane < 16 * PPR) my_sc[rbl * 16 * PPR + lane] = scv[rbl];
+        if constexpr (ONE)
+            if (rbl == RBW - 1 && has_corr) za_load(wave);
+        if (rbl == RBW - 1) TLM(7);
         if (rbl < nrb) {
             float4_t acc[MB][2], cacc[MB];
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
                 acc[mb][0] = acc[mb][1] = cacc[mb] = float4_t{0.f, 0.f, 0.f, 0.f};
-            if (has_corr) {
+            if (!ONE && has_corr) {
                 const uint32_t t = uw[rbl];
                 const u32x4_t bv = {sign_pair_bf16(t, 4 * grp + 0), sign_pair_bf16(t, 4 * grp + 1),
                                     sign_pair_bf16(t, 4 * grp + 2), sign_pair_bf16(t, 4 * grp + 3)};
@@ -544,14 +831,93 @@ __global__ void __launch_bounds__(kPThreads) mfma_product_kernel(MfmaParams p) {
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
                 mine[(rbl * MB + mb) * 64] = p.g * (acc[mb][0] + acc[mb][1]) + cacc[mb];
+            if (rbl == 0) TLM(4);
+            if constexpr (ONE) {
+                if (rbl == kA) {
+                    if (threadIdx.x == 0) s_flag = (has_tile && zold == (uint32_t)(p.P - 1)) ? 1u : 0u;
+                    __syncthreads();
+                    last = s_flag != 0u;
+                    TLM(5);
+                    TLMV(12, last ? 1 : 0);
+                    if (last) fin_load();
+                }
+                if (rbl == kB && last) {
+                    finish();
+                    TLM(6);
+                }
+            }
         }
         // keep each row block's dequantisation next to its MFMAs
         __builtin_amdgcn_sched_barrier(0);
         if (rbl + kPipe < RBW) load_rb(rbl + kPipe);
         __builtin_amdgcn_sched_barrier(0);
     }
+    TLM(8);
+    // ---- one launch: every correction word of this wave, from the tagged
+    // operands (a word not yet published is read again within a bounded
+    // time, then computed by the wave itself)
+    if constexpr (ONE) {
+        const uint32_t tag = ep + 1u;
+        for (int wi = wave; wi < nws; wi += kPWaves) {
+            const int w = s + p.S * wi;
+            if (wi != wave) {
+                u_load(wi);
+                za_load(wi);
+            }
+            bool local = p.spin_limit == 0u;
+            if (!local) {
+                const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+                while (true) {
+                    bool ok = true;
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                        for (int h = 0; h < 2; ++h)
+#pragma unroll
+                            for (int hf = 0; hf < 2; ++hf)
+                                ok = ok && za[mb][h][hf].y == tag && za[mb][h][hf].w == tag;
+                    if (__builtin_amdgcn_ballot_w64(!ok) == 0) break;
+                    if (__builtin_amdgcn_s_memrealtime() - t0 >= (uint64_t)p.spin_limit) {
+                        local = true;
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(2);
+                    za_load(wi);
+                }
+            }
+            if (wi == wave) {
+                TLM(9);
+                TLMV(13, local ? 1 : 0);
+            }
+            u32x4_t zz1[MB][2];
+            if (!local) {
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                    for (int h = 0; h < 2; ++h)
+                        zz1[mb][h] = u32x4_t{za[mb][h][0].x, za[mb][h][0].z, za[mb][h][1].x, za[mb][h][1].z};
+            } else {
+                z_word_local<MB>(p, w, lane, zz1);
+            }
+#pragma unroll
+            for (int rbl = 0; rbl < RBW; ++rbl) {
+                if (rbl < nrb) {
+                    const uint32_t t = uw[rbl];
+                    const u32x4_t bv = {sign_pair_bf16(t, 4 * grp + 0), sign_pair_bf16(t, 4 * grp + 1),
+                                        sign_pair_bf16(t, 4 * grp + 2), sign_pair_bf16(t, 4 * grp + 3)};
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb) {
+                        float4_t cacc = mfma_bf16(zz1[mb][0], bv, float4_t{0.f, 0.f, 0.f, 0.f});
+                        cacc = mfma_bf16(zz1[mb][1], bv, cacc);
+                        mine[(rbl * MB + mb) * 64] += cacc;
+                    }
+                }
+            }
+        }
+    }
+    TLM(10);
     // further correction words of this wave (more than 8 per slice)
-    for (int wi = wave + kPWaves; wi < nws; wi += kPWaves) {
+    for (int wi = wave + kPWaves; !ONE && wi < nws; wi += kPWaves) {
         corr_load(wi);
 #pragma unroll
         for (int rbl = 0; rbl < RBW; ++rbl) {
@@ -599,6 +965,19 @@ __global__ void __launch_bounds__(kPThreads) mfma_product_kernel(MfmaParams p) {
                 ypart[(((int64_t)s * p.RB + pb + rbl) * MB + mb) * 64 + l] = wave_sum(idx);
         }
     }
+    TLM(11);
+    // one launch: workgroup 0 advances the epoch once every workgroup has read
+    // it (its flag shows epoch + 1), so no workgroup of this call can see the
+    // next value.  Every workgroup sets its flag near its start and none waits
+    // for this one, so the wait ends once all have started.
+    if constexpr (ONE) {
+        if (blockIdx.x == 0) {
+            for (int j = 1 + (int)threadIdx.x; j < (int)gridDim.x; j += kPThreads)
+                while (ld_u32(p.seen + j) != ep + 1u) __builtin_amdgcn_s_sleep(2);
+            __syncthreads();
+            if (threadIdx.x == 0) st_u32(p.epoch, ep + 1u);
+        }
+    }
 }
 
 // =====================================================================
@@ -636,8 +1015,13 @@ namespace {
 struct MfmaPlan {
     int mb, W, zs, zsteps, chunks, S, cps, RB, Gs, grid, rbw, cpw;
     size_t lds;
+    // one launch: z tiles (P K-parts of psteps K-steps per word), their
+    // placement, whether the shape takes that schedule, and its LDS
+    int P, psteps, ntiles, g8;
+    bool one_ok;
+    size_t lds_one;
     // workspace offsets inside the matrix-core area
-    size_t off_zpart, off_za, off_ypart, bytes;
+    size_t off_zpart, off_za, off_ypart, off_zpt, off_zat, bytes;
 };
 
 size_t align256(size_t b) { return (b + 255) / 256 * 256; }
@@ -678,6 +1062,25 @@ MfmaPlan mfma_plan(int M, int N, int K, int r) {
     const int rb_wg = (q.RB + q.Gs - 1) / q.Gs;
     q.rbw = rb_wg <= small ? small : large;
     q.lds = (size_t)kPWaves * q.rbw * q.mb * 64 * 16 + (size_t)kPWaves * q.rbw * 16 * 16 * scale_pieces(q.cpw);
+    // (two m-blocks: the finisher's LDS lives in the row-block slots)
+    q.lds_one = q.lds + (q.mb == 2 ? 0 : (size_t)kPThreads * 16 + (size_t)q.mb * 16 * 32 * 4);
+    // one launch: as many K-parts per word as the workgroups hold tiles (at
+    // most kMaxZParts); tiles of one part sit on one XCD (workgroup b runs on
+    // XCD b % 8), so x's part is fetched once per XCD
+    if (q.W > 0) {
+        q.g8 = q.grid >= 8 ? q.grid / 8 : 0;
+        const int tmax = q.g8 > 0 ? 8 * q.g8 : q.grid;
+        int P = tmax / q.W;
+        P = P < kMaxZParts ? P : kMaxZParts;
+        P = P < steps ? P : steps;
+        if (P >= 1) {
+            q.psteps = (steps + P - 1) / P;
+            q.P = (steps + q.psteps - 1) / q.psteps;
+            q.ntiles = q.W * q.P;
+        }
+        q.one_ok = P >= 1 && q.rbw >= 3 && (int64_t)M * K * 2 <= (int64_t)INT32_MAX - 16 &&
+                   q.lds_one <= kLdsLimit;
+    }
     // workspace
     size_t off = 0;
     q.off_zpart = off;
@@ -686,17 +1089,24 @@ MfmaPlan mfma_plan(int M, int N, int K, int r) {
     off += (size_t)q.W * q.mb * 2 * 64 * 16;
     q.off_ypart = off;
     if (q.S > 1) off += (size_t)q.S * q.RB * q.mb * 64 * 16;
+    if (q.one_ok) {
+        off = align256(off);
+        q.off_zpt = off;
+        off += (size_t)q.ntiles * q.mb * 128 * 16;
+        q.off_zat = off;
+        off += (size_t)q.W * q.mb * 2 * 64 * 4 * 8;
+    }
     q.bytes = off > 0 ? align256(off) : 0;
     return q;
 }
 
 // Dynamic LDS above 64 KiB must be allowed once per kernel.
-template <int MB, int RBW, int CPW>
+template <int MB, int RBW, int CPW, bool ONE>
 hipError_t allow_lds() {
     static std::once_flag once;
     static hipError_t err = hipSuccess;
     std::call_once(once, [] {
-        err = hipFuncSetAttribute(reinterpret_cast<const void *>(&mfma_product_kernel<MB, RBW, CPW>),
+        err = hipFuncSetAttribute(reinterpret_cast<const void *>(&mfma_product_kernel<MB, RBW, CPW, ONE>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsLimit);
     });
     return err;
@@ -706,6 +1116,11 @@ hipError_t allow_lds() {
 bool mfma_supported(int M, int N, int K, int r) {
     if (M < 1 || M > 32 || N < 1 || K < 32 || K % 32 != 0 || r < 0) return false;
     return mfma_plan(M, N, K, r).lds <= kLdsLimit;
+}
+
+bool mfma_one_supported(int M, int N, int K, int r) {
+    if (r < 1 || !mfma_supported(M, N, K, r)) return false;
+    return mfma_plan(M, N, K, r).one_ok;
 }
 
 size_t mfma_ws_bytes(int M, int N, int K, int r) {
@@ -753,7 +1168,57 @@ MfmaParams mfma_params(const GemmArgs &a, MfmaPlan &q_out) {
     // (r > 0 calls always get a whole workspace)
     if (a.r > 0) p.zcnt = reinterpret_cast<uint32_t *>(static_cast<char *>(a.ws) + kWsZcntOffset);
     p.rpad = rpad32(a.r);
+    if (q.one_ok && q.bytes > 0) {
+        char *ws = static_cast<char *>(a.ws) + (a.ws_is_mfma_area ? 0 : ws_mfma_offset(a.M, a.r));
+        p.zpt = reinterpret_cast<float *>(ws + q.off_zpt);
+        p.zat = reinterpret_cast<uint64_t *>(ws + q.off_zat);
+        p.epoch = reinterpret_cast<uint32_t *>(static_cast<char *>(a.ws) + ws_epoch_offset());
+        p.seen = reinterpret_cast<uint32_t *>(static_cast<char *>(a.ws) + ws_seen_offset());
+        p.P = q.P;
+        p.psteps = q.psteps;
+        p.ntiles = q.ntiles;
+        p.g8 = q.g8;
+    }
+    static const uint32_t spin = spin_limit_default();
+    p.spin_limit = spin;
     return p;
+}
+
+// The product launch (and, with K split, the epilogue launch).
+template <bool ONE>
+hipError_t launch_product(const MfmaPlan &q, const MfmaParams &p, hipStream_t stream) {
+    const dim3 grid(q.grid), block(kPThreads);
+    const size_t lds = ONE ? q.lds_one : q.lds;
+    constexpr int c1 = MfmaShape<1>::kCpw, c2 = MfmaShape<2>::kCpw;
+    constexpr int s1 = MfmaShape<1>::kRbwSmall, l1 = MfmaShape<1>::kRbwLarge;
+    constexpr int s2 = MfmaShape<2>::kRbwSmall, l2 = MfmaShape<2>::kRbwLarge;
+    constexpr int cw = MfmaShape<1>::kCpwWide, rw = MfmaShape<1>::kRbwWide;
+    hipError_t e;
+    if (q.mb == 1 && q.cpw == cw) {
+        e = allow_lds<1, rw, cw, ONE>();
+        if (e == hipSuccess) hipLaunchKernelGGL((mfma_product_kernel<1, rw, cw, ONE>), grid, block, lds, stream, p);
+    } else if (q.mb == 1 && q.rbw == s1) {
+        e = allow_lds<1, s1, c1, ONE>();
+        if (e == hipSuccess) hipLaunchKernelGGL((mfma_product_kernel<1, s1, c1, ONE>), grid, block, lds, stream, p);
+    } else if (q.mb == 1) {
+        e = allow_lds<1, l1, c1, ONE>();
+        if (e == hipSuccess) hipLaunchKernelGGL((mfma_product_kernel<1, l1, c1, ONE>), grid, block, lds, stream, p);
+    } else if (q.rbw == s2) {
+        e = allow_lds<2, s2, c2, ONE>();
+        if (e == hipSuccess) hipLaunchKernelGGL((mfma_product_kernel<2, s2, c2, ONE>), grid, block, lds, stream, p);
+    } else {
+        e = allow_lds<2, l2, c2, ONE>();
+        if (e == hipSuccess) hipLaunchKernelGGL((mfma_product_kernel<2, l2, c2, ONE>), grid, block, lds, stream, p);
+    }
+    if (e != hipSuccess) return e;
+    e = hipGetLastError();
+    if (e != hipSuccess || q.S == 1) return e;
+    const int items = q.RB * q.mb * 64;
+    if (q.mb == 1)
+        hipLaunchKernelGGL(mfma_epilogue_kernel<1>, dim3((items + 255) / 256), dim3(256), 0, stream, p);
+    else
+        hipLaunchKernelGGL(mfma_epilogue_kernel<2>, dim3((items + 255) / 256), dim3(256), 0, stream, p);
+    return hipGetLastError();
 }
 }  // namespace
 
@@ -792,36 +1257,28 @@ hipError_t launch_gemm_mfma(const GemmArgs &a, hipStream_t stream) {
         if (e != hipSuccess) return e;
         p.zsplit = 0;
     }
-    const dim3 grid(q.grid), block(kPThreads);
-    constexpr int c1 = MfmaShape<1>::kCpw, c2 = MfmaShape<2>::kCpw;
-    constexpr int s1 = MfmaShape<1>::kRbwSmall, l1 = MfmaShape<1>::kRbwLarge;
-    constexpr int s2 = MfmaShape<2>::kRbwSmall, l2 = MfmaShape<2>::kRbwLarge;
-    constexpr int cw = MfmaShape<1>::kCpwWide, rw = MfmaShape<1>::kRbwWide;
-    if (q.mb == 1 && q.cpw == cw) {
-        e = allow_lds<1, rw, cw>();
-        if (e == hipSuccess) hipLaunchKernelGGL((mfma_product_kernel<1, rw, cw>), grid, block, q.lds, stream, p);
-    } else if (q.mb == 1 && q.rbw == s1) {
-        e = allow_lds<1, s1, c1>();
-        if (e == hipSuccess) hipLaunchKernelGGL((mfma_product_kernel<1, s1, c1>), grid, block, q.lds, stream, p);
-    } else if (q.mb == 1) {
-        e = allow_lds<1, l1, c1>();
-        if (e == hipSuccess) hipLaunchKernelGGL((mfma_product_kernel<1, l1, c1>), grid, block, q.lds, stream, p);
-    } else if (q.rbw == s2) {
-        e = allow_lds<2, s2, c2>();
-        if (e == hipSuccess) hipLaunchKernelGGL((mfma_product_kernel<2, s2, c2>), grid, block, q.lds, stream, p);
-    } else {
-        e = allow_lds<2, l2, c2>();
-        if (e == hipSuccess) hipLaunchKernelGGL((mfma_product_kernel<2, l2, c2>), grid, block, q.lds, stream, p);
-    }
-    if (e != hipSuccess) return e;
-    e = hipGetLastError();
-    if (e != hipSuccess || q.S == 1) return e;
-    const int items = q.RB * q.mb * 64;
-    if (q.mb == 1)
-        hipLaunchKernelGGL(mfma_epilogue_kernel<1>, dim3((items + 255) / 256), dim3(256), 0, stream, p);
-    else
-        hipLaunchKernelGGL(mfma_epilogue_kernel<2>, dim3((items + 255) / 256), dim3(256), 0, stream, p);
-    return hipGetLastError();
+    return launch_product<false>(q, p, stream);
 }
 
+// One launch: every workgroup computes one tile of z at entry, the last
+// tile of each word finishes it, and the product's workgroups apply the
+// finished words after their row blocks (plus the split-K epilogue when K
+// is split).
+hipError_t launch_gemm_mfma_one(const GemmArgs &a, hipStream_t stream) {
+    if (!mfma_one_supported(a.M, a.N, a.K, a.r)) return hipErrorNotSupported;
+    MfmaPlan q;
+    MfmaParams p = mfma_params(a, q);
+    return launch_product<true>(q, p, stream);
+}
+
+#ifdef BILOCO_TIMELINE
+extern "C" int biloco_tl_mfma_zero() {
+    static uint64_t z[kTlMaxWorkgroups * 8 * kTlSlots];
+    return (int)hipMemcpyToSymbol(HIP_SYMBOL(g_tl_mfma), z, sizeof(z), 0, hipMemcpyHostToDevice);
+}
+extern "C" int biloco_tl_mfma_read(uint64_t *host, int n) {
+    if (n < 0 || n > kTlMaxWorkgroups * 8 * kTlSlots) return -1;
+    return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(g_tl_mfma), (size_t)n * 8, 0, hipMemcpyDeviceToHost);
+}
+#endif
 }  // namespace biloco

@@ -73,6 +73,18 @@ typedef int32_t biloco_status;
 #define BILOCO_SCHED_COMPOSED_MFMA 5 /* as BILOCO_SCHED_COMPOSED, the correction by bf16
                                        MFMAs of z (high + low) against U's +-1 signs
                                        instead of lookup tables; r <= 1024 */
+#define BILOCO_SCHED_MFMA_ALLWG  6  /* matrix-core products, r >= 1 (BiLoCo "Kernel": the
+                                       mode where every CTA takes part in the correction
+                                       at kernel entry): one product launch in which
+                                       every workgroup first computes one tile of z
+                                       (a 32-index word of V over a K-part), the last
+                                       tile of each word finishes it, and the product
+                                       applies the finished words after its row blocks;
+                                       plus the K-slice sum launch when K is split.
+                                       Needs every workgroup of the launch resident at
+                                       once for its speed, not for its results: a wait
+                                       for z is bounded, after which the waiting wave
+                                       computes the word itself */
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char *biloco_status_string(biloco_status s);

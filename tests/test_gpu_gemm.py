@@ -160,6 +160,14 @@ for (M, K, N, r) in [(1, 256, 256, 16), (2, 1024, 300, 40), (1, 5120, 512, 512)]
         p.gemm(B.BILOCO_SCHED_FUSED_GEMV)
     torch.cuda.synchronize()
     check_y(p.y_float(), y_ref, f'fallback {{(M, K, N, r)}}')
+for (M, K, N, r) in [(8, 1024, 300, 40), (32, 2048, 200, 100), (3, 512, 64, 33)]:
+    d = wl.make_inputs(M, K, N, r, seed=41 + M)
+    y_ref = oracle.gemm_lowrank(d['x'], d['wcode'], d['wscales'], d['g'], d['V'], d['U'], d['alpha'])
+    p = DeviceProblem(d)
+    for it in range(3):
+        p.gemm(B.BILOCO_SCHED_MFMA_ALLWG)
+    torch.cuda.synchronize()
+    check_y(p.y_float(), y_ref, f'all-workgroup fallback {{(M, K, N, r)}}')
 print('FALLBACK_OK')
 """
 
@@ -274,7 +282,9 @@ def test_rank_above_1024(M, r):
 
 @pytest.mark.parametrize("cfg,sched", [(1, B.BILOCO_SCHED_AUTO), (2, B.BILOCO_SCHED_AUTO),
                                       (3, B.BILOCO_SCHED_AUTO), (4, B.BILOCO_SCHED_AUTO),
-                                      (1, B.BILOCO_SCHED_FUSED_GEMV), (1, B.BILOCO_SCHED_FUSED_MFMA)])
+                                      (1, B.BILOCO_SCHED_FUSED_GEMV), (1, B.BILOCO_SCHED_FUSED_MFMA),
+                                      (2, B.BILOCO_SCHED_MFMA_ALLWG), (3, B.BILOCO_SCHED_MFMA_ALLWG),
+                                      (4, B.BILOCO_SCHED_MFMA_ALLWG)])
 def test_graph_replay_as_timed(cfg, sched):
     """The form the benchmark times: quantise-and-multiply calls captured once
     in a graph over rotated copies of the weights, replayed several times with
