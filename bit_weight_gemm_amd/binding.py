@@ -13,7 +13,9 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libbiloco_hip.so")
+# another build of the same library (the host-sanitized one the tests load)
+# can be named with BILOCO_HIP_LIB
+LIB_PATH = os.environ.get("BILOCO_HIP_LIB") or os.path.join(_PKG, "libbiloco_hip.so")
 
 BILOCO_OK = 0
 BILOCO_ERR_INVALID_VALUE = 1
