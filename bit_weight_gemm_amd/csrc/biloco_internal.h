@@ -31,36 +31,37 @@ struct GemmArgs {
     bool ws_is_mfma_area = false;
 };
 
-// Workspace layout (byte offsets).  The first 192 KiB are fixed for every
+// Workspace layout (byte offsets).  The first 80 KiB are fixed for every
 // shape, so that no call of one shape can write over the counters, flags or
 // tagged values another shape relies on (one workspace may serve calls of
 // different shapes, one after the other):
 //   [0, 4)                 epoch of the one-launch schedules (uint32)
 //   [256, 256 + 4 G)       one "seen" flag per workgroup of a one-launch call
 //                          (G <= kGemvMaxWorkgroups + 1)
-//   [kWsZcntOffset, 64 KiB) the matrix-core z launch's per-word arrival
-//                          counters (at most kWsZcntMax words), zero between calls
-//   [64 KiB, 192 KiB)      z as (fp32 value | 32-bit epoch tag << 32) words of
-//                          the one-launch vector schedule: one copy per XCD,
-//                          [8][MM <= 2][rpad <= 1024]
-//   [192 KiB, ...)         the areas of the shape, in this order:
+//   [kWsZcntOffset, 64 KiB) per-word arrival counters of the matrix-core z
+//                          launch and of the all-workgroup schedule's z tiles
+//                          (at most kWsZcntMax words), zero between calls
+//   [64 KiB, 80 KiB)       z as (fp32 value | 32-bit epoch tag << 32) words of
+//                          the one-launch vector schedule, [MM <= 2][rpad <= 1024]
+//   [80 KiB, ...)          the areas of the shape, in this order:
 //     r > 0: z as plain fp32 [M][Rpad] (two-launch schedule)
 //     r > 0, M <= 2: the vector product's correction operands: z split into
 //            bf16 high and low parts, laid out per lane
 //            [M][ceil(Rpad / 512)][64 lanes][4][high, low] (bf16 pairs)
-//     (256-aligned) the matrix-core schedule's area: z slice partials, z
-//            operands, K-slice partials of y (sized by mfma_ws_bytes)
+//     (256-aligned) the matrix-core schedules' area: z slice partials, z
+//            operands, K-slice partials of y, and (r > 0) the all-workgroup
+//            schedule's z tile partials and tagged z operand words (sized by
+//            mfma_ws_bytes)
 //     (256-aligned, r > 0) the separate-launch schedule's fp32 product [M][N]
 //            and its r = 0 product's split-K partials
 constexpr int kGemvMaxWorkgroups = 8192;
 constexpr size_t kWsHeaderBytes = 64 * 1024;
 constexpr size_t kWsZcntOffset = 34 * 1024;
 constexpr int kWsZcntMax = (int)((kWsHeaderBytes - kWsZcntOffset) / 4);
-constexpr int kZtCopies = 8;                       // one tagged copy of z per XCD
 constexpr int kZtMaxRows = 2, kZtMaxRank = 1024;
 constexpr size_t kWsZtOffset = kWsHeaderBytes;
-constexpr size_t kWsZtBytes = (size_t)8 * kZtCopies * kZtMaxRows * kZtMaxRank;
-constexpr size_t kWsAreaOffset = kWsZtOffset + kWsZtBytes;    // 192 KiB
+constexpr size_t kWsZtBytes = (size_t)8 * kZtMaxRows * kZtMaxRank;
+constexpr size_t kWsAreaOffset = kWsZtOffset + kWsZtBytes;    // 80 KiB
 static_assert(256 + 4 * (kGemvMaxWorkgroups + 1) <= kWsZcntOffset, "seen flags fit the header");
 __host__ __device__ inline int rpad32(int r) { return (r + 31) / 32 * 32; }
 inline size_t ws_epoch_offset() { return 0; }

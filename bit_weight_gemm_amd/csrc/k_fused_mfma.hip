@@ -153,6 +153,15 @@ __device__ __forceinline__ void store_y(const MfmaParams &p, int64_t idx, float 
     else p.y[idx] = f32_to_bf16_rne(v);
 }
 
+// Workgroup b runs on XCD b mod 8.  This numbering gives XCD x the
+// consecutive work indices [x G8, (x + 1) G8) (G8 = grid / 8, rounded down;
+// the last grid mod 8 workgroups keep their index), so work that shares an
+// input (a K-slice's x or activation) shares one XCD's L2.
+__device__ __forceinline__ int xcd_major_index(int b, int grid) {
+    const int g8 = grid >> 3;
+    return b < 8 * g8 ? (b & 7) * g8 + (b >> 3) : b;
+}
+
 __device__ __forceinline__ float4_t mfma_f16(const u32x4_t &a, const u32x4_t &b, float4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a),
                                                   __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
@@ -259,7 +268,8 @@ __global__ void __launch_bounds__(kZThreads) mfma_z_kernel(MfmaParams p) {
     __shared__ float s_t[MB * 16][33];
     __shared__ uint32_t s_last;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int w = blockIdx.x % p.W, s = blockIdx.x / p.W;
+    const int t = xcd_major_index((int)blockIdx.x, (int)gridDim.x);
+    const int w = t % p.W, s = t / p.W;
     // the activation's FP4 quantisation rides along (read by the product)
     if (p.qa_codes) {
         const int64_t nb = (int64_t)p.M * (p.K >> 4);
@@ -483,7 +493,9 @@ __global__ void __launch_bounds__(kPThreads) mfma_product_kernel(MfmaParams p) {
         }
     };
     if (has_tile) z_load(0);
-    const int s = blockIdx.x % p.S, wgi = blockIdx.x / p.S;
+    // slice-major work index: the workgroups of one K-slice share an XCD
+    const int wt = xcd_major_index((int)blockIdx.x, (int)gridDim.x);
+    const int s = wt / p.Gs, wgi = wt % p.Gs;
     const int rb_begin = (int)((int64_t)wgi * p.RB / p.Gs);      // Gs row groups of <= RBW blocks
     const int rb_end = (int)((int64_t)(wgi + 1) * p.RB / p.Gs);
     const int c0 = s * p.cps;
@@ -569,7 +581,9 @@ __global__ void __launch_bounds__(kPThreads) mfma_product_kernel(MfmaParams p) {
     u32x4_t cw[RBW][CPW];
     // block scales of R, requested with the row block's codes: per row the
     // 16-byte-aligned window of PPR pieces that holds the wave's (at most
-    // CPW x 8) scale bytes, lane PPR row + piece
+    // CPW x 8) scale bytes, lane PPR row + piece.  (Exact 8-byte loads of each
+    // chunk's scales, where K allows them, changed neither the HBM traffic
+    // measurably nor the time.)
     u32x4_t scv[RBW];
     auto load_rb = [&](int rbl) {
         {
