@@ -201,3 +201,28 @@ def test_gemm_quant_rejects_before_hip():
     assert call(as_=A * 4 + 16) == B.BILOCO_ERR_INVALID_VALUE      # scales inside w_codes
     assert call(ac=A * 2) == B.BILOCO_ERR_INVALID_VALUE            # codes over scales
     assert call(sched=9) == B.BILOCO_ERR_INVALID_VALUE
+
+
+def test_timeline_stamps_only_in_the_measurement_build():
+    """The per-wave timeline stamps are compiled only into libbiloco_tl.so
+    (BILOCO_TIMELINE); the product library holds neither the stamp arrays'
+    readers nor any other timeline symbol."""
+    import subprocess
+    from bit_weight_gemm_amd import build as hb
+
+    def dynamic_symbols(path):
+        out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True,
+                             text=True, check=True).stdout
+        return {line.split()[-1] for line in out.splitlines() if line.strip()}
+
+    product = dynamic_symbols(B.LIB_PATH)
+    assert not any(s.startswith("biloco_tl_") for s in product)
+    if not os.path.exists(hb.TL_LIB):
+        pytest.skip("timeline build not present (built by __graft_entry__.build())")
+    tl = dynamic_symbols(hb.TL_LIB)
+    for name in ("biloco_tl_gemv_zero", "biloco_tl_gemv_read", "biloco_tl_mfma_zero",
+                 "biloco_tl_mfma_read"):
+        assert name in tl, name
+    # the measurement build exports the same C ABI as the product
+    for name in B.EXPORTED:
+        assert name in tl, name
