@@ -27,7 +27,7 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, 10^9 B/s
 ROT_BYTES = 1.2e9              # distinct weight bytes a timed graph walks through
 SCHED_NAMES = {1: "unfused", 2: "fused_gemv", 3: "fused_mfma", 4: "composed",
-               5: "composed_mfma", 6: "mfma_allwg"}
+               5: "composed_mfma", 6: "mfma_allwg", 7: "mfma_side"}
 METRIC = "fused GEMM µs/call + effective HBM GB/s (% peak) at M=1..32, r=512"
 
 
@@ -79,6 +79,7 @@ CALL_KERNELS = {"unfused": "z_kernel + fused_gemv_kernel",
 # counter records); other schedules' files may change without voiding them
 SCHED_FILES = {"fused_gemv": ["k_fused_gemv.hip", "biloco_device.h", "biloco_internal.h"],
                "mfma_allwg": ["k_fused_mfma.hip", "biloco_device.h", "biloco_internal.h"],
+               "mfma_side": ["k_fused_mfma.hip", "biloco_device.h", "biloco_internal.h"],
                "unfused": ["k_fused_gemv.hip", "biloco_device.h", "biloco_internal.h"],
                "fused_mfma": ["k_fused_mfma.hip", "biloco_device.h", "biloco_internal.h"]}
 
@@ -482,7 +483,7 @@ def main() -> int:
             # the matrix-core schedules side by side (z in a launch of its own,
             # and every workgroup computing a tile of z at entry)
             mfma_times = {}
-            for ms in (B.BILOCO_SCHED_FUSED_MFMA, B.BILOCO_SCHED_MFMA_ALLWG):
+            for ms in (B.BILOCO_SCHED_FUSED_MFMA, B.BILOCO_SCHED_MFMA_ALLWG, B.BILOCO_SCHED_MFMA_SIDE):
                 if ms in B.biloco_schedules_for(pc.M, pc.N, pc.K, pc.r):
                     mfma_times[SCHED_NAMES[ms] + "_us_per_call"] = round(
                         gemm_call_time(pc, ms, rc, calls) * 1e6, 3)
@@ -605,7 +606,10 @@ def timeline(args) -> int:
         if (~stream_wg).any():
             groups["side workgroups"] = (~stream_wg, [0, 2])
     else:
-        groups["all workgroups"] = (np.ones(len(wgs), bool), [k for k in range(len(names)) if k != 6])
+        prod = tl[:, 0, 1] > 0          # side workgroups stream no rows
+        groups["product workgroups"] = (prod, [k for k in range(len(names)) if k != 6])
+        if (~prod).any():
+            groups["side workgroups"] = (~prod, [0, 3, 4, 5, 6, 2])
         fin = tl[:, 0, 12] == 1
         if fin.any():
             groups["finisher workgroups"] = (fin, [6])
@@ -620,7 +624,11 @@ def timeline(args) -> int:
         for k in slots:
             v = rel[mask, :, k].ravel()
             v = v[~np.isnan(v)]
-            label = "z published" if gname.startswith("side") and k == 2 else names[k]
+            label = names[k]
+            if gname.startswith("side"):
+                label = {2: "z published" if fam == "gemv" else "z words published",
+                         3: "first word: first loads issued", 4: "first word: first loads used",
+                         5: "first word: second loads used", 6: "first word: waves' sums in LDS"}.get(k, label)
             if v.size:
                 rows[label] = {q: round(float(np.percentile(v, pc)), 2) for q, pc in
                                   (("min", 0), ("p10", 10), ("median", 50), ("p90", 90), ("max", 100))}

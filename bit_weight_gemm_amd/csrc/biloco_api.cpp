@@ -29,6 +29,7 @@ bool schedule_allowed(int s, int M, int N, int K, int r) {
         case BILOCO_SCHED_COMPOSED:
         case BILOCO_SCHED_COMPOSED_MFMA: return composed_supported(M, N, K, r);
         case BILOCO_SCHED_MFMA_ALLWG: return mfma_one_supported(M, N, K, r);
+        case BILOCO_SCHED_MFMA_SIDE: return mfma_side_supported(M, N, K, r);
         default: return false;
     }
 }
@@ -50,8 +51,12 @@ biloco_status check_shape(int32_t M, int32_t N, int32_t K, int32_t r) {
 // one-launch vector-ALU schedule (side workgroups compute z while the
 // others stream R) takes 7.3 us per call and 9.1 us per quantising call,
 // against 8.8 and 9.5 us for two launches (z, then the product).  r = 0
-// has one launch either way.  From M = 3 on, the matrix-core schedule.
+// has one launch either way.  From M = 3 on, the matrix-core schedules: with
+// side workgroups where x is small enough for one workgroup to read it per
+// word (M = 8, K = 5120, N = 13824, r = 512: 17.0 us per call against 21.1
+// us with z in launches of its own), else with z in launches of its own.
 int resolve_schedule(int M, int N, int K, int r) {
+    if (M >= 3 && mfma_side_supported(M, N, K, r)) return BILOCO_SCHED_MFMA_SIDE;
     if (M >= 3 && mfma_supported(M, N, K, r)) return BILOCO_SCHED_FUSED_MFMA;
     if (r > 0 && gemv_supported(M, N, K, r)) return BILOCO_SCHED_FUSED_GEMV;
     return BILOCO_SCHED_UNFUSED;
@@ -205,7 +210,7 @@ biloco_status biloco_gemm_check(const void *a_codes, const void *a_scales, const
         {alpha_bf16, (size_t)r * 2},   {workspace, need}};
     for (auto &in : ins)
         if (overlaps(y_bf16, ny, in.p, in.n)) return BILOCO_ERR_INVALID_VALUE;
-    if (schedule < BILOCO_SCHED_AUTO || schedule > BILOCO_SCHED_MFMA_ALLWG)
+    if (schedule < BILOCO_SCHED_AUTO || schedule > BILOCO_SCHED_MFMA_SIDE)
         return BILOCO_ERR_INVALID_VALUE;
     if (schedule != BILOCO_SCHED_AUTO && !schedule_allowed(schedule, M, N, K, r))
         return BILOCO_ERR_UNSUPPORTED;
@@ -221,7 +226,7 @@ int32_t biloco_schedules_for(int32_t M, int32_t N, int32_t K, int32_t r, int32_t
                              int32_t cap) {
     if (check_shape(M, N, K, r) != BILOCO_OK) return 0;
     int32_t n = 0;
-    for (int s = BILOCO_SCHED_UNFUSED; s <= BILOCO_SCHED_MFMA_ALLWG; ++s)
+    for (int s = BILOCO_SCHED_UNFUSED; s <= BILOCO_SCHED_MFMA_SIDE; ++s)
         if (schedule_allowed(s, M, N, K, r)) {
             if (out && n < cap) out[n] = s;
             ++n;
@@ -252,6 +257,7 @@ biloco_status biloco_gemm_lowrank_sched(const uint8_t *a_codes, const uint8_t *a
         case BILOCO_SCHED_COMPOSED: e = launch_gemm_composed(a, false, stream); break;
         case BILOCO_SCHED_COMPOSED_MFMA: e = launch_gemm_composed(a, true, stream); break;
         case BILOCO_SCHED_MFMA_ALLWG: e = launch_gemm_mfma_one(a, stream); break;
+        case BILOCO_SCHED_MFMA_SIDE: e = launch_gemm_mfma_side(a, stream); break;
         default: e = launch_gemm_unfused(a, stream); break;
     }
     return e == hipSuccess ? BILOCO_OK : BILOCO_ERR_HIP;
@@ -304,6 +310,7 @@ biloco_status biloco_gemm_lowrank_quant(const uint16_t *x_bf16, uint8_t *a_codes
         case BILOCO_SCHED_COMPOSED: e = launch_gemm_composed(a, false, stream); break;
         case BILOCO_SCHED_COMPOSED_MFMA: e = launch_gemm_composed(a, true, stream); break;
         case BILOCO_SCHED_MFMA_ALLWG: e = launch_gemm_mfma_one(a, stream); break;
+        case BILOCO_SCHED_MFMA_SIDE: e = launch_gemm_mfma_side(a, stream); break;
         default: e = launch_gemm_unfused(a, stream); break;
     }
     return e == hipSuccess ? BILOCO_OK : BILOCO_ERR_HIP;

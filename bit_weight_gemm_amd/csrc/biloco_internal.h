@@ -118,6 +118,8 @@ uint32_t spin_limit_default();
 hipError_t launch_gemm_mfma(const GemmArgs &a, hipStream_t stream);
 bool mfma_one_supported(int M, int N, int K, int r);   // shapes the one-launch matrix-core schedule handles
 hipError_t launch_gemm_mfma_one(const GemmArgs &a, hipStream_t stream);
+bool mfma_side_supported(int M, int N, int K, int r);  // shapes the side-workgroup matrix-core schedule handles
+hipError_t launch_gemm_mfma_side(const GemmArgs &a, hipStream_t stream);
 hipError_t launch_z_mfma(const GemmArgs &a, float *zf, hipStream_t stream);   // M >= 1, r >= 1
 // z = alpha (.) (x . V) as plain fp32 [M][rpad32(r)] at z (r > 0)
 hipError_t launch_z_fp32(const GemmArgs &a, float *z, hipStream_t stream);

@@ -145,6 +145,9 @@ struct MfmaParams {
     int ntiles;                 // W P tiles, tile t = part W + word
     int g8;                     // workgroups per XCD that hold a tile (0: tile = workgroup index)
     uint32_t spin_limit;        // bound of a wait on z, in 100 MHz ticks; 0 = compute z locally
+    // side-workgroup schedule: the first n_side workgroups compute whole words
+    // of z over all of K and stream no rows
+    int n_side;
 };
 
 // One output element: bf16 into y, or fp32 into yf when the caller asked for it.
@@ -417,6 +420,117 @@ __device__ __forceinline__ void z_word_local(const MfmaParams &p, int w, int lan
 }
 
 // =====================================================================
+// side-workgroup schedule: z by workgroups that stream no rows
+// =====================================================================
+// Side workgroup b computes the words b, b + n_side, ... of z over all of K
+// (x . V+- with bf16 MFMAs, every m), scales them by alpha, splits them
+// into bf16 high and low parts in the correction operand's order and
+// publishes them as tagged words (value | the call's epoch + 1 << 32).  Its
+// waves take the K-steps wave, wave + 8, ..., kSideSteps at a time, and
+// meet in LDS.  Side workgroup 0 is also the bookkeeper: it advances the
+// epoch once every workgroup of the launch has set its flag.  No side
+// workgroup waits for anything but that.
+constexpr int kSideSteps = 8;     // K-steps per wave per round of loads
+template <int MB>
+__device__ __forceinline__ void side_z_workgroup(const MfmaParams &p, float4_t *lds) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int col = lane & 15, grp = lane >> 4;
+    const uint32_t ep = ld_u32(p.epoch);
+    if (threadIdx.x == 0) st_u32(p.seen + blockIdx.x, ep + 1u);
+    const uint32_t tag = ep + 1u;
+    const int steps = p.K >> 5;
+    const __amdgpu_buffer_rsrc_t r_x = buffer_of(p.x, (int64_t)p.M * p.K * 2);
+    float *s_zt = reinterpret_cast<float *>(lds + (size_t)kPWaves * MB * 2 * 64);   // [MB 16][32]
+    for (int w = blockIdx.x; w < p.W; w += p.n_side) {
+        const __amdgpu_buffer_rsrc_t r_v = buffer_of(p.v + (int64_t)w * p.K, (int64_t)p.K * 4);
+        float4_t acc[MB][2];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) acc[mb][0] = acc[mb][1] = float4_t{0.f, 0.f, 0.f, 0.f};
+        for (int st0 = 0; st0 < steps; st0 += kPWaves * kSideSteps) {
+            u32x4_t xs[kSideSteps][MB], vs[kSideSteps][2];
+#pragma unroll
+            for (int u = 0; u < kSideSteps; ++u) {
+                const int st = st0 + wave + kPWaves * u;
+                const bool ok = st < steps;
+                const int k0 = st * 32 + 8 * grp;
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) {
+                    const int m = 16 * mb + col;
+                    xs[u][mb] = load16(r_x, opaque(ok && m < p.M ? (m * p.K + k0) * 2 : kOob));
+                }
+                vs[u][0] = load16(r_v, opaque(ok ? k0 * 4 : kOob));
+                vs[u][1] = load16(r_v, opaque(ok ? k0 * 4 + 16 : kOob));
+            }
+            if (st0 == 0 && w == (int)blockIdx.x) TLM(3);
+#pragma unroll
+            for (int u = 0; u < kSideSteps; ++u) {
+                if (st0 + wave + kPWaves * u < steps) {
+                    const uint32_t vw[8] = {vs[u][0].x, vs[u][0].y, vs[u][0].z, vs[u][0].w,
+                                            vs[u][1].x, vs[u][1].y, vs[u][1].z, vs[u][1].w};
+#pragma unroll
+                    for (int ib = 0; ib < 2; ++ib) {
+                        const int bit = 16 * ib + col;
+                        u32x4_t bv;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            bv[e] = (((vw[2 * e] >> bit) & 1u) << 15) |
+                                    (((vw[2 * e + 1] >> bit) & 1u) << 31) | 0x3F803F80u;
+#pragma unroll
+                        for (int mb = 0; mb < MB; ++mb) acc[mb][ib] = mfma_bf16(xs[u][mb], bv, acc[mb][ib]);
+                    }
+                }
+            }
+            if (w == (int)blockIdx.x) {
+                if (st0 == 0) TLM(4);
+                else if (st0 == kPWaves * kSideSteps) TLM(5);
+            }
+        }
+        // the waves' sums (D layout: m = 16 mb + 4 (l / 16) + e, rank 16 ib + l % 16)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int ib = 0; ib < 2; ++ib) lds[((size_t)wave * MB * 2 + mb * 2 + ib) * 64 + lane] = acc[mb][ib];
+        __syncthreads();
+        if (w == (int)blockIdx.x) TLM(6);
+        if ((int)threadIdx.x < MB * 128) {
+            const int l = threadIdx.x & 63, blk = threadIdx.x >> 6, mb = blk >> 1, ib = blk & 1;
+            float4_t v = lds[(size_t)blk * 64 + l];
+#pragma unroll
+            for (int q = 1; q < kPWaves; ++q) v += lds[((size_t)q * MB * 2 + blk) * 64 + l];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s_zt[(16 * mb + 4 * (l >> 4) + e) * 32 + 16 * ib + (l & 15)] = v[e];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int idx0 = 0; idx0 < MB * 512; idx0 += kPThreads) {
+            const int idx = idx0 + threadIdx.x;
+            const int j = idx & 7, l = (idx >> 3) & 63, mb = idx >> 9;
+            const int m = 16 * mb + (l & 15), q = l >> 4;
+            const int ii = 4 * q + (j & 3) + 16 * (j >> 2);
+            const int i = 32 * w + ii;
+            const float al = bf16_to_f32(p.alpha[i < p.r ? i : p.r - 1]);
+            const float zz = (i < p.r && m < p.M) ? s_zt[m * 32 + ii] * al : 0.0f;
+            const uint32_t zh = f32_to_bf16_rne(zz);
+            const uint32_t zl = f32_to_bf16_rne(zz - bf16_to_f32(zh));
+            const uint32_t oh = __shfl_xor(zh, 4, 64), ol = __shfl_xor(zl, 4, 64);
+            if (j < 4) {
+                uint64_t *dst = p.zat + ((((size_t)w * MB + mb) * 2) * 64 + l) * 4 + j;
+                st_tagged_u32(dst, zh | (oh << 16), tag);
+                st_tagged_u32(dst + 64 * 4, zl | (ol << 16), tag);
+            }
+        }
+        __syncthreads();     // the LDS serves the next word
+        TLM(2);
+    }
+    if (blockIdx.x == 0) {
+        for (int j = 1 + (int)threadIdx.x; j < (int)gridDim.x; j += kPThreads)
+            while (ld_u32(p.seen + j) != ep + 1u) __builtin_amdgcn_s_sleep(2);
+        __syncthreads();
+        if (threadIdx.x == 0) st_u32(p.epoch, ep + 1u);
+    }
+}
+
+// =====================================================================
 // launch 2: the product
 // =====================================================================
 // Workgroup (slice s, row-block range).  Wave q owns the chunks
@@ -430,11 +544,16 @@ __device__ __forceinline__ void z_word_local(const MfmaParams &p, int w, int lan
 // (row block past the range, chunk past the wave's share) loads zeros
 // through an out-of-range buffer offset, so every path issues the same loads
 // and the hardware wait counts stay exact.
-template <int MB, int RBW, int CPW, bool ONE>
+// ZM: 0 = z from the z launch (operands complete at the start); 1 = every
+// workgroup computes a tile of z at entry (all-workgroup schedule); 2 = the
+// first n_side workgroups compute z (side-workgroup schedule).  With 1 and 2
+// the product applies tagged z words after its row blocks.
+template <int MB, int RBW, int CPW, int ZM>
 __global__ void __launch_bounds__(kPThreads) mfma_product_kernel(MfmaParams p) {
+    constexpr bool ONE = ZM != 0, TILE = ZM == 1, SIDE = ZM == 2;
     constexpr int PPR = scale_pieces(CPW);              // 16-byte scale pieces per row
     constexpr int kPipe = MfmaShape<MB>::kPipe;
-    static_assert(!ONE || RBW >= 3, "the z tile's wave sums use the last two row-block slots");
+    static_assert(!TILE || RBW >= 3, "the z tile's wave sums use the last two row-block slots");
     // LDS: the waves' partial sums [wave][row block][mb][64 lanes], then each
     // wave's block scales of R [wave][row][PPR 16-byte pieces].  One launch:
     // the finisher's sums [512] and its transpose of z [MB 16][32] use the
@@ -460,21 +579,27 @@ __global__ void __launch_bounds__(kPThreads) mfma_product_kernel(MfmaParams p) {
 
     // ---- one launch: the call's epoch, and this workgroup's z tile (word
     // zw, K-part zkp), whose inputs are requested before anything else
+    if constexpr (SIDE) {
+        if ((int)blockIdx.x < p.n_side) {
+            side_z_workgroup<MB>(p, s_part);
+            return;
+        }
+    }
     uint32_t ep = 0;
     if constexpr (ONE) ep = ld_u32(p.epoch);
     int zt = p.ntiles;
-    if constexpr (ONE) {
+    if constexpr (TILE) {
         const int xq = blockIdx.x & 7, jq = blockIdx.x >> 3;
         zt = p.g8 > 0 ? (jq < p.g8 ? xq * p.g8 + jq : p.ntiles) : (int)blockIdx.x;
     }
-    const bool has_tile = ONE && zt < p.ntiles;
+    const bool has_tile = TILE && zt < p.ntiles;
     const int zw = has_tile ? zt % p.W : 0, zkp = has_tile ? zt / p.W : 0;
     const int zst0 = zkp * p.psteps;
     const int znst = has_tile ? min(p.psteps, (p.K >> 5) - zst0) : 0;
-    constexpr int ZU = ONE ? kZsw : 1;
+    constexpr int ZU = TILE ? kZsw : 1;
     u32x4_t zx[ZU][MB], zv[ZU][2];
-    const __amdgpu_buffer_rsrc_t r_x = buffer_of(p.x, ONE ? (int64_t)p.M * p.K * 2 : 0);
-    const __amdgpu_buffer_rsrc_t r_v = buffer_of(p.v + (ONE ? (int64_t)zw * p.K : 0), ONE ? (int64_t)p.K * 4 : 0);
+    const __amdgpu_buffer_rsrc_t r_x = buffer_of(p.x, TILE ? (int64_t)p.M * p.K * 2 : 0);
+    const __amdgpu_buffer_rsrc_t r_v = buffer_of(p.v + (TILE ? (int64_t)zw * p.K : 0), TILE ? (int64_t)p.K * 4 : 0);
     // K-steps round * 8 kZsw + wave + 8 u of the part (rows past M and steps
     // past the part read zeros)
     auto z_load = [&](int round) {
@@ -494,7 +619,8 @@ __global__ void __launch_bounds__(kPThreads) mfma_product_kernel(MfmaParams p) {
     };
     if (has_tile) z_load(0);
     // slice-major work index: the workgroups of one K-slice share an XCD
-    const int wt = xcd_major_index((int)blockIdx.x, (int)gridDim.x);
+    const int wt = SIDE ? xcd_major_index((int)blockIdx.x - p.n_side, (int)gridDim.x - p.n_side)
+                        : xcd_major_index((int)blockIdx.x, (int)gridDim.x);
     const int s = wt / p.Gs, wgi = wt % p.Gs;
     const int rb_begin = (int)((int64_t)wgi * p.RB / p.Gs);      // Gs row groups of <= RBW blocks
     const int rb_end = (int)((int64_t)(wgi + 1) * p.RB / p.Gs);
@@ -730,7 +856,7 @@ __global__ void __launch_bounds__(kPThreads) mfma_product_kernel(MfmaParams p) {
     const int f_idx = threadIdx.x % NF4, f_p0 = threadIdx.x / NF4, f_step = kPThreads / NF4;
     float4_t fin[FJ];
     const __amdgpu_buffer_rsrc_t r_zp =
-        buffer_of(p.zpt, ONE ? (int64_t)p.ntiles * NF4 * 16 : 0);
+        buffer_of(p.zpt, TILE ? (int64_t)p.ntiles * NF4 * 16 : 0);
     auto fin_load = [&]() {
 #pragma unroll
         for (int j = 0; j < FJ; ++j) {
@@ -786,7 +912,9 @@ __global__ void __launch_bounds__(kPThreads) mfma_product_kernel(MfmaParams p) {
 
     // ---- one launch: this wave's first correction word, as tagged words,
     // requested at the start of the last row-block slot (the last row block
-    // of a workgroup with a full range)
+    // of a workgroup with a full range; with side workgroups, requesting them
+    // one slot earlier found them not yet published and measured slower)
+    constexpr int kZaSlot = RBW - 1;
     u32x4_t za[MB][2][2];
     const __amdgpu_buffer_rsrc_t r_za = buffer_of(p.zat, ONE ? (int64_t)p.W * MB * 2 * 64 * 4 * 8 : 0);
     auto za_load = [&](int wi) {
@@ -808,7 +936,7 @@ __global__ void __launch_bounds__(kPThreads) mfma_product_kernel(MfmaParams p) {
     for (int rbl = 0; rbl < RBW; ++rbl) {
         if (lane < 16 * PPR) my_sc[rbl * 16 * PPR + lane] = scv[rbl];
         if constexpr (ONE)
-            if (rbl == RBW - 1 && has_corr) za_load(wave);
+            if (rbl == kZaSlot && has_corr) za_load(wave);
         if (rbl == RBW - 1) TLM(7);
         if (rbl < nrb) {
             float4_t acc[MB][2], cacc[MB];
@@ -846,7 +974,7 @@ __global__ void __launch_bounds__(kPThreads) mfma_product_kernel(MfmaParams p) {
             for (int mb = 0; mb < MB; ++mb)
                 mine[(rbl * MB + mb) * 64] = p.g * (acc[mb][0] + acc[mb][1]) + cacc[mb];
             if (rbl == 0) TLM(4);
-            if constexpr (ONE) {
+            if constexpr (TILE) {
                 if (rbl == kA) {
                     if (threadIdx.x == 0) s_flag = (has_tile && zold == (uint32_t)(p.P - 1)) ? 1u : 0u;
                     __syncthreads();
@@ -984,7 +1112,7 @@ __global__ void __launch_bounds__(kPThreads) mfma_product_kernel(MfmaParams p) {
     // it (its flag shows epoch + 1), so no workgroup of this call can see the
     // next value.  Every workgroup sets its flag near its start and none waits
     // for this one, so the wait ends once all have started.
-    if constexpr (ONE) {
+    if constexpr (TILE) {
         if (blockIdx.x == 0) {
             for (int j = 1 + (int)threadIdx.x; j < (int)gridDim.x; j += kPThreads)
                 while (ld_u32(p.seen + j) != ep + 1u) __builtin_amdgcn_s_sleep(2);
@@ -1034,13 +1162,22 @@ struct MfmaPlan {
     int P, psteps, ntiles, g8;
     bool one_ok;
     size_t lds_one;
+    // side-workgroup schedule: side workgroups ahead of the product's
+    int n_side;
     // workspace offsets inside the matrix-core area
     size_t off_zpart, off_za, off_ypart, off_zpt, off_zat, bytes;
 };
 
 size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 
-MfmaPlan mfma_plan(int M, int N, int K, int r) {
+// Side workgroups of the side-workgroup schedule: one word of z each (8 or
+// 16, a multiple of 8 so that the product's XCD-major numbering keeps its
+// XCDs); the shape qualifies when x is small enough for one workgroup to
+// read it once per word and the product still fits the remaining CUs.
+constexpr int kSideMaxXBytes = 96 * 1024;
+int side_count(int W) { return W <= 8 ? 8 : 16; }
+
+MfmaPlan mfma_plan(int M, int N, int K, int r, int grid_target = kGridTarget) {
     MfmaPlan q{};
     q.mb = M <= 16 ? 1 : 2;
     q.W = (r + 31) / 32;
@@ -1068,7 +1205,7 @@ MfmaPlan mfma_plan(int M, int N, int K, int r) {
     // the large variant, more workgroups (several rounds) otherwise
     const int small = wide ? MfmaShape<1>::kRbwWide : q.mb == 1 ? MfmaShape<1>::kRbwSmall : MfmaShape<2>::kRbwSmall;
     const int large = wide ? MfmaShape<1>::kRbwWide : q.mb == 1 ? MfmaShape<1>::kRbwLarge : MfmaShape<2>::kRbwLarge;
-    q.Gs = kGridTarget / q.S;
+    q.Gs = grid_target / q.S;
     if (q.Gs < 1) q.Gs = 1;
     if (q.Gs < (q.RB + large - 1) / large) q.Gs = (q.RB + large - 1) / large;
     if (q.Gs > q.RB) q.Gs = q.RB;
@@ -1103,24 +1240,28 @@ MfmaPlan mfma_plan(int M, int N, int K, int r) {
     off += (size_t)q.W * q.mb * 2 * 64 * 16;
     q.off_ypart = off;
     if (q.S > 1) off += (size_t)q.S * q.RB * q.mb * 64 * 16;
+    if (q.W > 0) {
+        // tagged z operand words (all-workgroup and side-workgroup schedules)
+        off = align256(off);
+        q.off_zat = off;
+        off += (size_t)q.W * q.mb * 2 * 64 * 4 * 8;
+    }
     if (q.one_ok) {
         off = align256(off);
         q.off_zpt = off;
         off += (size_t)q.ntiles * q.mb * 128 * 16;
-        q.off_zat = off;
-        off += (size_t)q.W * q.mb * 2 * 64 * 4 * 8;
     }
     q.bytes = off > 0 ? align256(off) : 0;
     return q;
 }
 
 // Dynamic LDS above 64 KiB must be allowed once per kernel.
-template <int MB, int RBW, int CPW, bool ONE>
+template <int MB, int RBW, int CPW, int ZM>
 hipError_t allow_lds() {
     static std::once_flag once;
     static hipError_t err = hipSuccess;
     std::call_once(once, [] {
-        err = hipFuncSetAttribute(reinterpret_cast<const void *>(&mfma_product_kernel<MB, RBW, CPW, ONE>),
+        err = hipFuncSetAttribute(reinterpret_cast<const void *>(&mfma_product_kernel<MB, RBW, CPW, ZM>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsLimit);
     });
     return err;
@@ -1137,15 +1278,34 @@ bool mfma_one_supported(int M, int N, int K, int r) {
     return mfma_plan(M, N, K, r).one_ok;
 }
 
+namespace {
+// the product's plan with room for the side workgroups (grid = q.grid + n_side)
+MfmaPlan side_plan(int M, int N, int K, int r) {
+    const int W = (r + 31) / 32;
+    const int n_side = side_count(W);
+    MfmaPlan q = mfma_plan(M, N, K, r, kGridTarget - n_side);
+    q.n_side = n_side;
+    return q;
+}
+}  // namespace
+
+bool mfma_side_supported(int M, int N, int K, int r) {
+    if (r < 1 || !mfma_supported(M, N, K, r)) return false;
+    if ((int64_t)M * K * 2 > kSideMaxXBytes) return false;
+    const MfmaPlan q = side_plan(M, N, K, r);
+    // every workgroup resident at once: the product's fit the CUs the side
+    // workgroups leave, and the side path's LDS fits the product's
+    return q.grid + q.n_side <= kGridTarget && q.lds <= kLdsLimit &&
+           (size_t)kPWaves * q.mb * 2 * 64 * 16 + (size_t)q.mb * 16 * 32 * 4 <= q.lds;
+}
+
 size_t mfma_ws_bytes(int M, int N, int K, int r) {
     return mfma_supported(M, N, K, r) ? mfma_plan(M, N, K, r).bytes : 0;
 }
 
 namespace {
 // Parameters and workspace areas of one call (shared by the launchers below).
-MfmaParams mfma_params(const GemmArgs &a, MfmaPlan &q_out) {
-    const MfmaPlan q = mfma_plan(a.M, a.N, a.K, a.r);
-    q_out = q;
+MfmaParams mfma_params(const GemmArgs &a, const MfmaPlan &q) {
     MfmaParams p{};
     p.a_codes = a.a_codes;
     p.a_scales = a.a_scales;
@@ -1182,16 +1342,18 @@ MfmaParams mfma_params(const GemmArgs &a, MfmaPlan &q_out) {
     // (r > 0 calls always get a whole workspace)
     if (a.r > 0) p.zcnt = reinterpret_cast<uint32_t *>(static_cast<char *>(a.ws) + kWsZcntOffset);
     p.rpad = rpad32(a.r);
-    if (q.one_ok && q.bytes > 0) {
+    if (q.W > 0 && q.bytes > 0) {
         char *ws = static_cast<char *>(a.ws) + (a.ws_is_mfma_area ? 0 : ws_mfma_offset(a.M, a.r));
-        p.zpt = reinterpret_cast<float *>(ws + q.off_zpt);
         p.zat = reinterpret_cast<uint64_t *>(ws + q.off_zat);
         p.epoch = reinterpret_cast<uint32_t *>(static_cast<char *>(a.ws) + ws_epoch_offset());
         p.seen = reinterpret_cast<uint32_t *>(static_cast<char *>(a.ws) + ws_seen_offset());
-        p.P = q.P;
-        p.psteps = q.psteps;
-        p.ntiles = q.ntiles;
-        p.g8 = q.g8;
+        if (q.one_ok) {
+            p.zpt = reinterpret_cast<float *>(ws + q.off_zpt);
+            p.P = q.P;
+            p.psteps = q.psteps;
+            p.ntiles = q.ntiles;
+            p.g8 = q.g8;
+        }
     }
     static const uint32_t spin = spin_limit_default();
     p.spin_limit = spin;
@@ -1199,30 +1361,30 @@ MfmaParams mfma_params(const GemmArgs &a, MfmaPlan &q_out) {
 }
 
 // The product launch (and, with K split, the epilogue launch).
-template <bool ONE>
+template <int ZM>
 hipError_t launch_product(const MfmaPlan &q, const MfmaParams &p, hipStream_t stream) {
-    const dim3 grid(q.grid), block(kPThreads);
-    const size_t lds = ONE ? q.lds_one : q.lds;
+    const dim3 grid(q.grid + (ZM == 2 ? q.n_side : 0)), block(kPThreads);
+    const size_t lds = ZM == 1 ? q.lds_one : q.lds;
     constexpr int c1 = MfmaShape<1>::kCpw, c2 = MfmaShape<2>::kCpw;
     constexpr int s1 = MfmaShape<1>::kRbwSmall, l1 = MfmaShape<1>::kRbwLarge;
     constexpr int s2 = MfmaShape<2>::kRbwSmall, l2 = MfmaShape<2>::kRbwLarge;
     constexpr int cw = MfmaShape<1>::kCpwWide, rw = MfmaShape<1>::kRbwWide;
     hipError_t e;
     if (q.mb == 1 && q.cpw == cw) {
-        e = allow_lds<1, rw, cw, ONE>();
-        if (e == hipSuccess) hipLaunchKernelGGL((mfma_product_kernel<1, rw, cw, ONE>), grid, block, lds, stream, p);
+        e = allow_lds<1, rw, cw, ZM>();
+        if (e == hipSuccess) hipLaunchKernelGGL((mfma_product_kernel<1, rw, cw, ZM>), grid, block, lds, stream, p);
     } else if (q.mb == 1 && q.rbw == s1) {
-        e = allow_lds<1, s1, c1, ONE>();
-        if (e == hipSuccess) hipLaunchKernelGGL((mfma_product_kernel<1, s1, c1, ONE>), grid, block, lds, stream, p);
+        e = allow_lds<1, s1, c1, ZM>();
+        if (e == hipSuccess) hipLaunchKernelGGL((mfma_product_kernel<1, s1, c1, ZM>), grid, block, lds, stream, p);
     } else if (q.mb == 1) {
-        e = allow_lds<1, l1, c1, ONE>();
-        if (e == hipSuccess) hipLaunchKernelGGL((mfma_product_kernel<1, l1, c1, ONE>), grid, block, lds, stream, p);
+        e = allow_lds<1, l1, c1, ZM>();
+        if (e == hipSuccess) hipLaunchKernelGGL((mfma_product_kernel<1, l1, c1, ZM>), grid, block, lds, stream, p);
     } else if (q.rbw == s2) {
-        e = allow_lds<2, s2, c2, ONE>();
-        if (e == hipSuccess) hipLaunchKernelGGL((mfma_product_kernel<2, s2, c2, ONE>), grid, block, lds, stream, p);
+        e = allow_lds<2, s2, c2, ZM>();
+        if (e == hipSuccess) hipLaunchKernelGGL((mfma_product_kernel<2, s2, c2, ZM>), grid, block, lds, stream, p);
     } else {
-        e = allow_lds<2, l2, c2, ONE>();
-        if (e == hipSuccess) hipLaunchKernelGGL((mfma_product_kernel<2, l2, c2, ONE>), grid, block, lds, stream, p);
+        e = allow_lds<2, l2, c2, ZM>();
+        if (e == hipSuccess) hipLaunchKernelGGL((mfma_product_kernel<2, l2, c2, ZM>), grid, block, lds, stream, p);
     }
     if (e != hipSuccess) return e;
     e = hipGetLastError();
@@ -1239,7 +1401,7 @@ hipError_t launch_product(const MfmaPlan &q, const MfmaParams &p, hipStream_t st
 // The z kernel alone, also storing plain fp32 z at zf (separate-launch use).
 hipError_t launch_z_mfma(const GemmArgs &a, float *zf, hipStream_t stream) {
     if (a.r < 1 || !mfma_supported(a.M, a.N, a.K, a.r)) return hipErrorNotSupported;
-    MfmaPlan q;
+    const MfmaPlan q = mfma_plan(a.M, a.N, a.K, a.r);
     MfmaParams p = mfma_params(a, q);
     p.zf = zf;
     if (q.mb == 1)
@@ -1251,7 +1413,7 @@ hipError_t launch_z_mfma(const GemmArgs &a, float *zf, hipStream_t stream) {
 
 hipError_t launch_gemm_mfma(const GemmArgs &a, hipStream_t stream) {
     if (!mfma_supported(a.M, a.N, a.K, a.r)) return hipErrorNotSupported;
-    MfmaPlan q;
+    const MfmaPlan q = mfma_plan(a.M, a.N, a.K, a.r);
     MfmaParams p = mfma_params(a, q);
     hipError_t e = hipSuccess;
     if (a.r > 0) {
@@ -1271,7 +1433,7 @@ hipError_t launch_gemm_mfma(const GemmArgs &a, hipStream_t stream) {
         if (e != hipSuccess) return e;
         p.zsplit = 0;
     }
-    return launch_product<false>(q, p, stream);
+    return launch_product<0>(q, p, stream);
 }
 
 // One launch: every workgroup computes one tile of z at entry, the last
@@ -1280,9 +1442,20 @@ hipError_t launch_gemm_mfma(const GemmArgs &a, hipStream_t stream) {
 // is split).
 hipError_t launch_gemm_mfma_one(const GemmArgs &a, hipStream_t stream) {
     if (!mfma_one_supported(a.M, a.N, a.K, a.r)) return hipErrorNotSupported;
-    MfmaPlan q;
+    const MfmaPlan q = mfma_plan(a.M, a.N, a.K, a.r);
     MfmaParams p = mfma_params(a, q);
-    return launch_product<true>(q, p, stream);
+    return launch_product<1>(q, p, stream);
+}
+
+// Side workgroups: the first side_count(W) workgroups compute z word by word
+// while the others stream R; the product applies the tagged words after its
+// row blocks (plus the K-slice sum launch when K is split).
+hipError_t launch_gemm_mfma_side(const GemmArgs &a, hipStream_t stream) {
+    if (!mfma_side_supported(a.M, a.N, a.K, a.r)) return hipErrorNotSupported;
+    const MfmaPlan q = side_plan(a.M, a.N, a.K, a.r);
+    MfmaParams p = mfma_params(a, q);
+    p.n_side = q.n_side;
+    return launch_product<2>(q, p, stream);
 }
 
 #ifdef BILOCO_TIMELINE

@@ -85,6 +85,15 @@ typedef int32_t biloco_status;
                                        once for its speed, not for its results: a wait
                                        for z is bounded, after which the waiting wave
                                        computes the word itself */
+#define BILOCO_SCHED_MFMA_SIDE   7  /* matrix-core products, r >= 1, x of at most 96 KiB
+                                       (BiLoCo "Kernel": side CTAs compute z while the
+                                       others stream R): one product launch whose first
+                                       8 or 16 workgroups stream no rows and compute
+                                       whole words of z over all of K; the others apply
+                                       the published words after their row blocks; plus
+                                       the K-slice sum launch when K is split.  Needs
+                                       every workgroup resident at once for its speed, not
+                                       for its results (bounded waits, as above) */
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char *biloco_status_string(biloco_status s);
