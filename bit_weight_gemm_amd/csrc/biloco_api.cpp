@@ -53,8 +53,9 @@ biloco_status check_shape(int32_t M, int32_t N, int32_t K, int32_t r) {
 // against 8.8 and 9.5 us for two launches (z, then the product).  r = 0
 // has one launch either way.  From M = 3 on, the matrix-core schedules: with
 // side workgroups where x is small enough for one workgroup to read it per
-// word (M = 8, K = 5120, N = 13824, r = 512: 17.0 us per call against 21.1
-// us with z in launches of its own), else with z in launches of its own.
+// word (M = 8, K = 5120, N = 13824, r = 512: 16.7-17.4 us per call against
+// 20.8-21.6 us with z in launches of its own), else with z in launches of
+// its own.
 int resolve_schedule(int M, int N, int K, int r) {
     if (M >= 3 && mfma_side_supported(M, N, K, r)) return BILOCO_SCHED_MFMA_SIDE;
     if (M >= 3 && mfma_supported(M, N, K, r)) return BILOCO_SCHED_FUSED_MFMA;

@@ -148,6 +148,8 @@ struct MfmaParams {
     // side-workgroup schedule: the first n_side workgroups compute whole words
     // of z over all of K and stream no rows
     int n_side;
+    int side_split;             // 1: a side workgroup per word; 2: per half of K of a word
+    uint64_t *zhp;              // first halves' partial z, tagged, [W][MB 16][32] (split 2)
 };
 
 // One output element: bf16 into y, or fp32 into yf when the caller asked for it.
@@ -441,17 +443,21 @@ __device__ __forceinline__ void side_z_workgroup(const MfmaParams &p, float4_t *
     const int steps = p.K >> 5;
     const __amdgpu_buffer_rsrc_t r_x = buffer_of(p.x, (int64_t)p.M * p.K * 2);
     float *s_zt = reinterpret_cast<float *>(lds + (size_t)kPWaves * MB * 2 * 64);   // [MB 16][32]
-    for (int w = blockIdx.x; w < p.W; w += p.n_side) {
+    const int split = p.side_split;
+    for (int item = blockIdx.x; item < p.W * split; item += p.n_side) {
+        // word w over the K-steps [hs0, hs1): all of K, or half h of it
+        const int w = item % p.W, h = item / p.W;
+        const int hs0 = h * steps / split, hs1 = (h + 1) * steps / split;
         const __amdgpu_buffer_rsrc_t r_v = buffer_of(p.v + (int64_t)w * p.K, (int64_t)p.K * 4);
         float4_t acc[MB][2];
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) acc[mb][0] = acc[mb][1] = float4_t{0.f, 0.f, 0.f, 0.f};
-        for (int st0 = 0; st0 < steps; st0 += kPWaves * kSideSteps) {
+        for (int st0 = hs0; st0 < hs1; st0 += kPWaves * kSideSteps) {
             u32x4_t xs[kSideSteps][MB], vs[kSideSteps][2];
 #pragma unroll
             for (int u = 0; u < kSideSteps; ++u) {
                 const int st = st0 + wave + kPWaves * u;
-                const bool ok = st < steps;
+                const bool ok = st < hs1;
                 const int k0 = st * 32 + 8 * grp;
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb) {
@@ -461,10 +467,10 @@ __device__ __forceinline__ void side_z_workgroup(const MfmaParams &p, float4_t *
                 vs[u][0] = load16(r_v, opaque(ok ? k0 * 4 : kOob));
                 vs[u][1] = load16(r_v, opaque(ok ? k0 * 4 + 16 : kOob));
             }
-            if (st0 == 0 && w == (int)blockIdx.x) TLM(3);
+            if (st0 == hs0 && item == (int)blockIdx.x) TLM(3);
 #pragma unroll
             for (int u = 0; u < kSideSteps; ++u) {
-                if (st0 + wave + kPWaves * u < steps) {
+                if (st0 + wave + kPWaves * u < hs1) {
                     const uint32_t vw[8] = {vs[u][0].x, vs[u][0].y, vs[u][0].z, vs[u][0].w,
                                             vs[u][1].x, vs[u][1].y, vs[u][1].z, vs[u][1].w};
 #pragma unroll
@@ -480,9 +486,9 @@ __device__ __forceinline__ void side_z_workgroup(const MfmaParams &p, float4_t *
                     }
                 }
             }
-            if (w == (int)blockIdx.x) {
-                if (st0 == 0) TLM(4);
-                else if (st0 == kPWaves * kSideSteps) TLM(5);
+            if (item == (int)blockIdx.x) {
+                if (st0 == hs0) TLM(4);
+                else if (st0 == hs0 + kPWaves * kSideSteps) TLM(5);
             }
         }
         // the waves' sums (D layout: m = 16 mb + 4 (l / 16) + e, rank 16 ib + l % 16)
@@ -491,7 +497,7 @@ __device__ __forceinline__ void side_z_workgroup(const MfmaParams &p, float4_t *
 #pragma unroll
             for (int ib = 0; ib < 2; ++ib) lds[((size_t)wave * MB * 2 + mb * 2 + ib) * 64 + lane] = acc[mb][ib];
         __syncthreads();
-        if (w == (int)blockIdx.x) TLM(6);
+        if (item == (int)blockIdx.x) TLM(6);
         if ((int)threadIdx.x < MB * 128) {
             const int l = threadIdx.x & 63, blk = threadIdx.x >> 6, mb = blk >> 1, ib = blk & 1;
             float4_t v = lds[(size_t)blk * 64 + l];
@@ -501,6 +507,43 @@ __device__ __forceinline__ void side_z_workgroup(const MfmaParams &p, float4_t *
             for (int e = 0; e < 4; ++e) s_zt[(16 * mb + 4 * (l >> 4) + e) * 32 + 16 * ib + (l & 15)] = v[e];
         }
         __syncthreads();
+        if (split == 2) {
+            uint64_t *hp = p.zhp + (size_t)w * MB * 512;
+            if (h == 0) {
+                // the first half's sums, tagged, for the word's second-half workgroup
+                for (int idx = threadIdx.x; idx < MB * 512; idx += kPThreads) st_tagged(hp + idx, s_zt[idx], tag);
+                __syncthreads();     // the LDS serves the next item
+                continue;
+            }
+            // second half: add the first half's sums (a bounded wait; past it,
+            // each value is summed here over the first half's K-steps)
+            const __amdgpu_buffer_rsrc_t r_hp = buffer_of(hp, (int64_t)MB * 512 * 8);
+            for (int idx = threadIdx.x; idx < MB * 512; idx += kPThreads) {
+                uint64_t a = ld_tagged(r_hp, opaque(idx * 8));
+                if ((uint32_t)(a >> 32) != tag && p.spin_limit) {
+                    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+                    do {
+                        __builtin_amdgcn_s_sleep(1);
+                        a = ld_tagged(r_hp, opaque(idx * 8));
+                    } while ((uint32_t)(a >> 32) != tag &&
+                             __builtin_amdgcn_s_memrealtime() - t0 < (uint64_t)p.spin_limit);
+                }
+                float first;
+                if ((uint32_t)(a >> 32) == tag && p.spin_limit) {
+                    first = __uint_as_float((uint32_t)a);
+                } else {
+                    const int m = idx >> 5, ii = idx & 31;
+                    first = 0.0f;
+                    if (m < p.M)
+                        for (int k = 0; k < hs0 * 32; ++k) {
+                            const float xv = bf16_to_f32(p.x[(int64_t)m * p.K + k]);
+                            first += ((p.v[(int64_t)w * p.K + k] >> ii) & 1u) ? -xv : xv;
+                        }
+                }
+                s_zt[idx] += first;
+            }
+            __syncthreads();
+        }
 #pragma unroll
         for (int idx0 = 0; idx0 < MB * 512; idx0 += kPThreads) {
             const int idx = idx0 + threadIdx.x;
@@ -1162,20 +1205,23 @@ struct MfmaPlan {
     int P, psteps, ntiles, g8;
     bool one_ok;
     size_t lds_one;
-    // side-workgroup schedule: side workgroups ahead of the product's
-    int n_side;
+    // side-workgroup schedule: side workgroups ahead of the product's, and
+    // whether each word's K is split over two of them
+    int n_side, side_split;
     // workspace offsets inside the matrix-core area
-    size_t off_zpart, off_za, off_ypart, off_zpt, off_zat, bytes;
+    size_t off_zpart, off_za, off_ypart, off_zpt, off_zat, off_zhp, bytes;
 };
 
 size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 
-// Side workgroups of the side-workgroup schedule: one word of z each (8 or
-// 16, a multiple of 8 so that the product's XCD-major numbering keeps its
-// XCDs); the shape qualifies when x is small enough for one workgroup to
-// read it once per word and the product still fits the remaining CUs.
+// Side workgroups of the side-workgroup schedule (a multiple of 8, so that
+// the product's XCD-major numbering keeps its XCDs): two per word, each over
+// half of K, while 2 W <= 32; else 16, a word each.  The shape qualifies when
+// x is small enough for a workgroup to read it once per word and the product
+// still fits the remaining CUs.
 constexpr int kSideMaxXBytes = 96 * 1024;
-int side_count(int W) { return W <= 8 ? 8 : 16; }
+int side_split_of(int W) { return 2 * W <= 32 ? 2 : 1; }
+int side_count(int W) { return side_split_of(W) == 2 ? (2 * W + 7) / 8 * 8 : 16; }
 
 MfmaPlan mfma_plan(int M, int N, int K, int r, int grid_target = kGridTarget) {
     MfmaPlan q{};
@@ -1241,10 +1287,13 @@ MfmaPlan mfma_plan(int M, int N, int K, int r, int grid_target = kGridTarget) {
     q.off_ypart = off;
     if (q.S > 1) off += (size_t)q.S * q.RB * q.mb * 64 * 16;
     if (q.W > 0) {
-        // tagged z operand words (all-workgroup and side-workgroup schedules)
+        // tagged z operand words (all-workgroup and side-workgroup schedules),
+        // then the side workgroups' tagged first-half sums
         off = align256(off);
         q.off_zat = off;
         off += (size_t)q.W * q.mb * 2 * 64 * 4 * 8;
+        q.off_zhp = off;
+        off += (size_t)q.W * q.mb * 512 * 8;
     }
     if (q.one_ok) {
         off = align256(off);
@@ -1285,6 +1334,7 @@ MfmaPlan side_plan(int M, int N, int K, int r) {
     const int n_side = side_count(W);
     MfmaPlan q = mfma_plan(M, N, K, r, kGridTarget - n_side);
     q.n_side = n_side;
+    q.side_split = side_split_of(W);
     return q;
 }
 }  // namespace
@@ -1345,6 +1395,7 @@ MfmaParams mfma_params(const GemmArgs &a, const MfmaPlan &q) {
     if (q.W > 0 && q.bytes > 0) {
         char *ws = static_cast<char *>(a.ws) + (a.ws_is_mfma_area ? 0 : ws_mfma_offset(a.M, a.r));
         p.zat = reinterpret_cast<uint64_t *>(ws + q.off_zat);
+        p.zhp = reinterpret_cast<uint64_t *>(ws + q.off_zhp);
         p.epoch = reinterpret_cast<uint32_t *>(static_cast<char *>(a.ws) + ws_epoch_offset());
         p.seen = reinterpret_cast<uint32_t *>(static_cast<char *>(a.ws) + ws_seen_offset());
         if (q.one_ok) {
@@ -1455,6 +1506,7 @@ hipError_t launch_gemm_mfma_side(const GemmArgs &a, hipStream_t stream) {
     const MfmaPlan q = side_plan(a.M, a.N, a.K, a.r);
     MfmaParams p = mfma_params(a, q);
     p.n_side = q.n_side;
+    p.side_split = q.side_split;
     return launch_product<2>(q, p, stream);
 }
 

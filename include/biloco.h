@@ -88,8 +88,8 @@ typedef int32_t biloco_status;
 #define BILOCO_SCHED_MFMA_SIDE   7  /* matrix-core products, r >= 1, x of at most 96 KiB
                                        (BiLoCo "Kernel": side CTAs compute z while the
                                        others stream R): one product launch whose first
-                                       8 or 16 workgroups stream no rows and compute
-                                       whole words of z over all of K; the others apply
+                                       8 to 32 workgroups stream no rows and compute z,
+                                       a word or half a word of K each; the others apply
                                        the published words after their row blocks; plus
                                        the K-slice sum launch when K is split.  Needs
                                        every workgroup resident at once for its speed, not

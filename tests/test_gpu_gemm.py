@@ -160,14 +160,18 @@ for (M, K, N, r) in [(1, 256, 256, 16), (2, 1024, 300, 40), (1, 5120, 512, 512)]
         p.gemm(B.BILOCO_SCHED_FUSED_GEMV)
     torch.cuda.synchronize()
     check_y(p.y_float(), y_ref, f'fallback {{(M, K, N, r)}}')
-for (M, K, N, r) in [(8, 1024, 300, 40), (32, 2048, 200, 100), (3, 512, 64, 33)]:
+for (M, K, N, r) in [(8, 1024, 300, 40), (32, 2048, 200, 100), (3, 512, 64, 33), (8, 1024, 200, 500)]:
     d = wl.make_inputs(M, K, N, r, seed=41 + M)
     y_ref = oracle.gemm_lowrank(d['x'], d['wcode'], d['wscales'], d['g'], d['V'], d['U'], d['alpha'])
     p = DeviceProblem(d)
-    for it in range(3):
-        p.gemm(B.BILOCO_SCHED_MFMA_ALLWG)
-    torch.cuda.synchronize()
-    check_y(p.y_float(), y_ref, f'all-workgroup fallback {{(M, K, N, r)}}')
+    for sched in (B.BILOCO_SCHED_MFMA_ALLWG, B.BILOCO_SCHED_MFMA_SIDE):
+        if sched not in B.biloco_schedules_for(M, N, K, r):
+            continue
+        for it in range(3):
+            p.y.zero_()
+            p.gemm(sched)
+        torch.cuda.synchronize()
+        check_y(p.y_float(), y_ref, f'matrix-core one-launch fallback {{sched}} {{(M, K, N, r)}}')
 print('FALLBACK_OK')
 """
 
