@@ -27,7 +27,7 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, 10^9 B/s
 ROT_BYTES = 1.2e9              # distinct weight bytes a timed graph walks through
 SCHED_NAMES = {1: "unfused", 2: "fused_gemv", 3: "fused_mfma", 4: "composed",
-               5: "composed_mfma", 6: "mfma_allwg", 7: "mfma_side"}
+               5: "composed_mfma", 6: "mfma_allwg", 7: "mfma_side", 8: "mfma_zepi"}
 METRIC = "fused GEMM µs/call + effective HBM GB/s (% peak) at M=1..32, r=512"
 
 
@@ -483,7 +483,8 @@ def main() -> int:
             # the matrix-core schedules side by side (z in a launch of its own,
             # and every workgroup computing a tile of z at entry)
             mfma_times = {}
-            for ms in (B.BILOCO_SCHED_FUSED_MFMA, B.BILOCO_SCHED_MFMA_ALLWG, B.BILOCO_SCHED_MFMA_SIDE):
+            for ms in (B.BILOCO_SCHED_FUSED_MFMA, B.BILOCO_SCHED_MFMA_ALLWG, B.BILOCO_SCHED_MFMA_SIDE,
+                       B.BILOCO_SCHED_MFMA_ZEPI):
                 if ms in B.biloco_schedules_for(pc.M, pc.N, pc.K, pc.r):
                     mfma_times[SCHED_NAMES[ms] + "_us_per_call"] = round(
                         gemm_call_time(pc, ms, rc, calls) * 1e6, 3)

@@ -31,6 +31,7 @@ BILOCO_SCHED_COMPOSED = 4
 BILOCO_SCHED_COMPOSED_MFMA = 5
 BILOCO_SCHED_MFMA_ALLWG = 6
 BILOCO_SCHED_MFMA_SIDE = 7
+BILOCO_SCHED_MFMA_ZEPI = 8
 
 EXPORTED = ["biloco_status_string", "biloco_pack_signs", "biloco_quant_act_fp4",
             "biloco_gemm_workspace_bytes", "biloco_gemm_lowrank", "biloco_gemm_lowrank_sched",

@@ -30,6 +30,7 @@ bool schedule_allowed(int s, int M, int N, int K, int r) {
         case BILOCO_SCHED_COMPOSED_MFMA: return composed_supported(M, N, K, r);
         case BILOCO_SCHED_MFMA_ALLWG: return mfma_one_supported(M, N, K, r);
         case BILOCO_SCHED_MFMA_SIDE: return mfma_side_supported(M, N, K, r);
+        case BILOCO_SCHED_MFMA_ZEPI: return mfma_ze_supported(M, N, K, r);
         default: return false;
     }
 }
@@ -55,9 +56,13 @@ biloco_status check_shape(int32_t M, int32_t N, int32_t K, int32_t r) {
 // side workgroups where x is small enough for one workgroup to read it per
 // word (M = 8, K = 5120, N = 13824, r = 512: 16.7-17.4 us per call against
 // 20.8-21.6 us with z in launches of its own), else with z in launches of
-// its own.
+// its own.  Where K is split over workgroups and x is larger (M = 32,
+// K = 13824, N = 5120, r = 512 and M = 32, K = 8192, N = 8192, r = 1024),
+// z computed by K-part in side workgroups and applied in the K-slice sum
+// launch: 23.4-23.9 us against 27.4-28.0 us with z in launches of its own.
 int resolve_schedule(int M, int N, int K, int r) {
     if (M >= 3 && mfma_side_supported(M, N, K, r)) return BILOCO_SCHED_MFMA_SIDE;
+    if (M >= 3 && mfma_ze_supported(M, N, K, r)) return BILOCO_SCHED_MFMA_ZEPI;
     if (M >= 3 && mfma_supported(M, N, K, r)) return BILOCO_SCHED_FUSED_MFMA;
     if (r > 0 && gemv_supported(M, N, K, r)) return BILOCO_SCHED_FUSED_GEMV;
     return BILOCO_SCHED_UNFUSED;
@@ -211,7 +216,7 @@ biloco_status biloco_gemm_check(const void *a_codes, const void *a_scales, const
         {alpha_bf16, (size_t)r * 2},   {workspace, need}};
     for (auto &in : ins)
         if (overlaps(y_bf16, ny, in.p, in.n)) return BILOCO_ERR_INVALID_VALUE;
-    if (schedule < BILOCO_SCHED_AUTO || schedule > BILOCO_SCHED_MFMA_SIDE)
+    if (schedule < BILOCO_SCHED_AUTO || schedule > BILOCO_SCHED_MFMA_ZEPI)
         return BILOCO_ERR_INVALID_VALUE;
     if (schedule != BILOCO_SCHED_AUTO && !schedule_allowed(schedule, M, N, K, r))
         return BILOCO_ERR_UNSUPPORTED;
@@ -227,7 +232,7 @@ int32_t biloco_schedules_for(int32_t M, int32_t N, int32_t K, int32_t r, int32_t
                              int32_t cap) {
     if (check_shape(M, N, K, r) != BILOCO_OK) return 0;
     int32_t n = 0;
-    for (int s = BILOCO_SCHED_UNFUSED; s <= BILOCO_SCHED_MFMA_SIDE; ++s)
+    for (int s = BILOCO_SCHED_UNFUSED; s <= BILOCO_SCHED_MFMA_ZEPI; ++s)
         if (schedule_allowed(s, M, N, K, r)) {
             if (out && n < cap) out[n] = s;
             ++n;
@@ -259,6 +264,7 @@ biloco_status biloco_gemm_lowrank_sched(const uint8_t *a_codes, const uint8_t *a
         case BILOCO_SCHED_COMPOSED_MFMA: e = launch_gemm_composed(a, true, stream); break;
         case BILOCO_SCHED_MFMA_ALLWG: e = launch_gemm_mfma_one(a, stream); break;
         case BILOCO_SCHED_MFMA_SIDE: e = launch_gemm_mfma_side(a, stream); break;
+        case BILOCO_SCHED_MFMA_ZEPI: e = launch_gemm_mfma_ze(a, stream); break;
         default: e = launch_gemm_unfused(a, stream); break;
     }
     return e == hipSuccess ? BILOCO_OK : BILOCO_ERR_HIP;
@@ -312,6 +318,7 @@ biloco_status biloco_gemm_lowrank_quant(const uint16_t *x_bf16, uint8_t *a_codes
         case BILOCO_SCHED_COMPOSED_MFMA: e = launch_gemm_composed(a, true, stream); break;
         case BILOCO_SCHED_MFMA_ALLWG: e = launch_gemm_mfma_one(a, stream); break;
         case BILOCO_SCHED_MFMA_SIDE: e = launch_gemm_mfma_side(a, stream); break;
+        case BILOCO_SCHED_MFMA_ZEPI: e = launch_gemm_mfma_ze(a, stream); break;
         default: e = launch_gemm_unfused(a, stream); break;
     }
     return e == hipSuccess ? BILOCO_OK : BILOCO_ERR_HIP;

@@ -38,9 +38,13 @@ struct GemmArgs {
 //   [0, 4)                 epoch of the one-launch schedules (uint32)
 //   [256, 256 + 4 G)       one "seen" flag per workgroup of a one-launch call
 //                          (G <= kGemvMaxWorkgroups + 1)
-//   [kWsZcntOffset, 64 KiB) per-word arrival counters of the matrix-core z
-//                          launch and of the all-workgroup schedule's z tiles
-//                          (at most kWsZcntMax words), zero between calls
+//   [kWsZcntOffset, kWsZeCntOffset) per-word arrival counters of the
+//                          matrix-core z launch and of the all-workgroup
+//                          schedule's z tiles (at most kWsZcntMax words), zero
+//                          between calls
+//   [kWsZeCntOffset, 64 KiB) the arrival counter of the z-in-epilogue
+//                          schedule's side workgroups (it only grows, by
+//                          kZeParts per call)
 //   [64 KiB, 80 KiB)       z as (fp32 value | 32-bit epoch tag << 32) words of
 //                          the one-launch vector schedule, [MM <= 2][rpad <= 1024]
 //   [80 KiB, ...)          the areas of the shape, in this order:
@@ -57,7 +61,8 @@ struct GemmArgs {
 constexpr int kGemvMaxWorkgroups = 8192;
 constexpr size_t kWsHeaderBytes = 64 * 1024;
 constexpr size_t kWsZcntOffset = 34 * 1024;
-constexpr int kWsZcntMax = (int)((kWsHeaderBytes - kWsZcntOffset) / 4);
+constexpr size_t kWsZeCntOffset = kWsHeaderBytes - 256;
+constexpr int kWsZcntMax = (int)((kWsZeCntOffset - kWsZcntOffset) / 4);
 constexpr int kZtMaxRows = 2, kZtMaxRank = 1024;
 constexpr size_t kWsZtOffset = kWsHeaderBytes;
 constexpr size_t kWsZtBytes = (size_t)8 * kZtMaxRows * kZtMaxRank;
@@ -120,6 +125,8 @@ bool mfma_one_supported(int M, int N, int K, int r);   // shapes the one-launch 
 hipError_t launch_gemm_mfma_one(const GemmArgs &a, hipStream_t stream);
 bool mfma_side_supported(int M, int N, int K, int r);  // shapes the side-workgroup matrix-core schedule handles
 hipError_t launch_gemm_mfma_side(const GemmArgs &a, hipStream_t stream);
+bool mfma_ze_supported(int M, int N, int K, int r);    // shapes the z-in-epilogue matrix-core schedule handles
+hipError_t launch_gemm_mfma_ze(const GemmArgs &a, hipStream_t stream);
 hipError_t launch_z_mfma(const GemmArgs &a, float *zf, hipStream_t stream);   // M >= 1, r >= 1
 // z = alpha (.) (x . V) as plain fp32 [M][rpad32(r)] at z (r > 0)
 hipError_t launch_z_fp32(const GemmArgs &a, float *z, hipStream_t stream);

@@ -49,6 +49,7 @@
 // K order inside a 128-k chunk: lane group q = lane / 16 holds the 32 k from
 // 32 q to 32 q + 31.  These are one 16-byte code load and one 2-byte scale
 // load per row.  K-step d of the chunk takes k = 32 q + 8 d + e, e < 8.
+#include <algorithm>
 #include <mutex>
 
 #include "biloco_device.h"
@@ -150,6 +151,12 @@ struct MfmaParams {
     int n_side;
     int side_split;             // 1: a side workgroup per word; 2: per half of K of a word
     uint64_t *zhp;              // first halves' partial z, tagged, [W][MB 16][32] (split 2)
+    // z-in-epilogue schedule: the first kZeParts workgroups compute z's
+    // K-part partials (zs K-steps each, ze_sub of them staged in LDS at a
+    // time), then finish its words; the K-slice epilogue applies them
+    int ze_sub;
+    float4_t *zep;              // partials [kZeParts][W][2 rank halves][MB][64 lanes] (D layout)
+    uint32_t *zecnt;            // the side workgroups' arrival counter [0] and generation [1]
 };
 
 // One output element: bf16 into y, or fp32 into yf when the caller asked for it.
@@ -574,6 +581,299 @@ __device__ __forceinline__ void side_z_workgroup(const MfmaParams &p, float4_t *
 }
 
 // =====================================================================
+// z-in-epilogue schedule: z by K-part in side workgroups, its correction
+// in the K-slice epilogue
+// =====================================================================
+// Side workgroup p of P (n_side) takes K-steps [p zs, (p + 1) zs) of every
+// word: it stages that part of x (A-operand order) and of V's words in LDS,
+// ze_sub K-steps at a time, and wave q computes words q, q + 8, ... with
+// bf16 MFMAs of x against V's +-1 signs (bits k and k + 1 of a rank paired
+// into one dword by a byte permute).  It stores its partials (D layout) with
+// 16-byte stores through to the coherence point (sc1), counts itself in, and
+// waits (bounded) until all P have; then it sums the parts of words p,
+// p + P, ..., scales them by alpha and stores z's bf16 high and low parts in
+// the correction operand's order (zA), read by the epilogue launch after
+// this one.  A word whose parts did not all arrive in time is computed from
+// x and V by the workgroup's wave 0 alone (z_word_local: slow, never
+// expected).  The wait is a sense-reversing barrier over a counter and a
+// generation word: each reads the generation, counts itself in, and the
+// last to arrive clears the counter and advances the generation, which the
+// others wait for.
+constexpr int kZeParts = 32;      // side workgroups (K-parts) at most; a multiple of 8 per shape
+constexpr int kZeWordsPerWave = 4;    // r <= 1024: 32 words over 8 waves
+constexpr int kZeLoads = 8;           // 16-byte pieces of x, and of V, per thread per staged round
+template <int MB>
+__device__ void ze_side_workgroup(const MfmaParams &p, float4_t *lds) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int col = lane & 15, grp = lane >> 4;
+    const int part = blockIdx.x, P = p.n_side;
+    TLM(0);
+    TLMV(14, 1);
+    const int steps = p.K >> 5;
+    const int st0 = part * p.zsteps;
+    const int nst = max(0, min(p.zsteps, steps - st0));
+    u32x4_t *s_x = reinterpret_cast<u32x4_t *>(lds);                     // [sub][MB][64]
+    uint32_t *s_v = reinterpret_cast<uint32_t *>(s_x + (size_t)p.ze_sub * MB * 64);   // [W][sub 32]
+    float4_t acc[kZeWordsPerWave][2][MB];
+#pragma unroll
+    for (int jw = 0; jw < kZeWordsPerWave; ++jw)
+#pragma unroll
+        for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) acc[jw][ib][mb] = float4_t{0.f, 0.f, 0.f, 0.f};
+    const __amdgpu_buffer_rsrc_t r_x = buffer_of(p.x, (int64_t)p.M * p.K * 2);
+    const __amdgpu_buffer_rsrc_t r_v = buffer_of(p.v, (int64_t)p.W * p.K * 4);
+    for (int sub0 = 0; sub0 < nst; sub0 += p.ze_sub) {
+        const int ns = min(p.ze_sub, nst - sub0);
+        const int k00 = (st0 + sub0) * 32;
+        if (sub0 > 0) __syncthreads();              // the previous round is consumed
+        // every load of the round first (at most kZeLoads 16-byte pieces of x
+        // and of V per thread: ze_sub is sized for that), then the LDS stores
+        u32x4_t lx[kZeLoads], lv[kZeLoads];
+#pragma unroll
+        for (int j = 0; j < kZeLoads; ++j) {
+            const int idx = (int)threadIdx.x + kPThreads * j;
+            const int l = idx & 63, mb = (idx >> 6) % MB, t = idx / (64 * MB);
+            const int m = 16 * mb + (l & 15), k0 = k00 + t * 32 + 8 * (l >> 4);
+            lx[j] = load16(r_x, opaque(t < ns && m < p.M ? (m * p.K + k0) * 2 : kOob));
+            const int w = idx / (ns * 8), j4 = idx - w * (ns * 8);
+            lv[j] = load16(r_v, opaque(w < p.W ? (w * p.K + k00 + 4 * j4) * 4 : kOob));
+        }
+#pragma unroll
+        for (int j = 0; j < kZeLoads; ++j) {
+            const int idx = (int)threadIdx.x + kPThreads * j;
+            if (idx < ns * MB * 64) s_x[idx] = lx[j];
+            const int w = idx / (ns * 8), j4 = idx - w * (ns * 8);
+            if (w < p.W) reinterpret_cast<u32x4_t *>(s_v + (size_t)w * p.ze_sub * 32)[j4] = lv[j];
+        }
+        __syncthreads();
+        TLM(1);
+        // K-step t's operands from LDS (x's A operand, this wave's words of
+        // V), read one step ahead of their MFMAs (two register sets)
+        struct ZeOps { u32x4_t a[MB]; u32x4_t v[kZeWordsPerWave][2]; };
+        auto ld_ops = [&](int t, ZeOps &o) {
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) o.a[mb] = s_x[(t * MB + mb) * 64 + lane];
+#pragma unroll
+            for (int jw = 0; jw < kZeWordsPerWave; ++jw) {
+                const int w = min(wave + kPWaves * jw, p.W - 1);
+                const uint32_t *vp = s_v + (size_t)w * p.ze_sub * 32 + t * 32 + 8 * grp;
+                o.v[jw][0] = *reinterpret_cast<const u32x4_t *>(vp);
+                o.v[jw][1] = *reinterpret_cast<const u32x4_t *>(vp + 4);
+            }
+        };
+        auto step = [&](const ZeOps &o) {
+#pragma unroll
+            for (int jw = 0; jw < kZeWordsPerWave; ++jw) {
+                if (wave + kPWaves * jw < p.W) {
+                    const uint32_t vw[8] = {o.v[jw][0].x, o.v[jw][0].y, o.v[jw][0].z, o.v[jw][0].w,
+                                            o.v[jw][1].x, o.v[jw][1].y, o.v[jw][1].z, o.v[jw][1].w};
+#pragma unroll
+                    for (int ib = 0; ib < 2; ++ib) {
+                        // bits of rank 16 ib + col at k = 2e and 2e + 1 into one dword
+                        const uint32_t sel = ib ? 0x07060302u : 0x05040100u;
+                        u32x4_t bv;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            bv[e] = sign_pair_bf16(__builtin_amdgcn_perm(vw[2 * e + 1], vw[2 * e], sel), col);
+#pragma unroll
+                        for (int mb = 0; mb < MB; ++mb) acc[jw][ib][mb] = mfma_bf16(o.a[mb], bv, acc[jw][ib][mb]);
+                    }
+                }
+            }
+        };
+        ZeOps oa, ob;
+        ld_ops(0, oa);
+        for (int t = 0; t < ns; t += 2) {
+            if (t + 1 < ns) ld_ops(t + 1, ob);
+            step(oa);
+            if (t + 2 < ns) ld_ops(t + 2, oa);
+            if (t + 1 < ns) step(ob);
+        }
+    }
+    TLM(2);
+    // this part's partials (16-byte stores through to the coherence point,
+    // sc1), then the count
+    const __amdgpu_buffer_rsrc_t r_zep = buffer_of(p.zep, (int64_t)kZeParts * p.W * 2 * MB * 64 * 16);
+#pragma unroll
+    for (int jw = 0; jw < kZeWordsPerWave; ++jw) {
+        const int w = wave + kPWaves * jw;
+        if (w < p.W) {
+#pragma unroll
+            for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+                    __builtin_amdgcn_raw_buffer_store_b128(
+                        __builtin_bit_cast(u32x4_t, acc[jw][ib][mb]), r_zep,
+                        (((((part * p.W + w) * 2 + ib) * MB + mb) * 64) + lane) * 16, 0, kPolicySc1);
+        }
+    }
+    stores_done();
+    TLM(3);
+    __syncthreads();
+    __shared__ uint32_t s_ok;
+    if (threadIdx.x == 0) {
+        const uint32_t gen = ld_u32(p.zecnt + 1);
+        __builtin_amdgcn_s_waitcnt(0);          // the generation is read before counting in
+        bool ok = true;
+        if (arrive(p.zecnt) == (uint32_t)(P - 1)) {
+            // (the cleared counter is needed only by the next call, after
+            // the launch boundary)
+            st_u32(p.zecnt, 0u);
+            st_u32(p.zecnt + 1, gen + 1u);
+        } else {
+            const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+            while (ld_u32(p.zecnt + 1) == gen) {
+                if (!p.spin_limit || __builtin_amdgcn_s_memrealtime() - t0 >= (uint64_t)p.spin_limit) {
+                    ok = false;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(2);
+            }
+        }
+        s_ok = ok ? 1u : 0u;
+    }
+    __syncthreads();
+    TLM(4);
+    const bool all_in = s_ok != 0u;
+    for (int w = part; w < p.W; w += P) {
+        if (!all_in) {
+            // fallback: wave 0 computes the word from x and V alone
+            if (wave == 0) {
+                u32x4_t zz[MB][2];
+                z_word_local<MB>(p, w, lane, zz);
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                    for (int h = 0; h < 2; ++h)
+                        reinterpret_cast<u32x4_t *>(p.zA)[(((size_t)w * MB + mb) * 2 + h) * 64 + lane] = zz[mb][h];
+            }
+            continue;
+        }
+        // the parts' sum in D layout: thread t loads float4 t % F (F = 2 MB 64
+        // per word) of the parts t / F, t / F + 2, ... (16-byte coherent
+        // loads, all requested first), the two halves meet in LDS
+        constexpr int F = 2 * MB * 64, NH = kPThreads / F, PPH = kZeParts / NH;
+        const int f = threadIdx.x % F, h = threadIdx.x / F;
+        float4_t pv[PPH];
+#pragma unroll
+        for (int j = 0; j < PPH; ++j) {
+            const int pp = h + NH * j;
+            pv[j] = __builtin_bit_cast(float4_t,
+                load16_sc1(r_zep, opaque(pp < P ? ((pp * p.W + w) * F + f) * 16 : kOob)));
+        }
+        float4_t sum4 = pv[0];
+#pragma unroll
+        for (int j = 1; j < PPH; ++j) sum4 += pv[j];
+        float4_t *s_red = reinterpret_cast<float4_t *>(lds);      // [NH][F], then the sums [F]
+        __syncthreads();                        // (the staging area is free)
+        s_red[h * F + f] = sum4;
+        __syncthreads();
+        if ((int)threadIdx.x < F) {
+            float4_t v = s_red[threadIdx.x];
+#pragma unroll
+            for (int hh = 1; hh < NH; ++hh) v += s_red[hh * F + threadIdx.x];
+            s_red[NH * F + threadIdx.x] = v;
+        }
+        __syncthreads();
+        const float *s_dz = reinterpret_cast<const float *>(s_red + NH * F);
+        // value (mb, l, j): z[m][ii], m = 16 mb + l % 16, ii = 4 (l / 16) +
+        // (j & 3) + 16 (j >> 2); its sum sits at D position (rank half
+        // ii / 16, lane ii % 16 + 16 ((m % 16) / 4), element m % 4)
+#pragma unroll
+        for (int v = 0; v < MB; ++v) {
+            const int idx = (int)threadIdx.x + kPThreads * v;
+            const int j = idx & 7, l = (idx >> 3) & 63, mb = idx >> 9;
+            const int mm = l & 15, m = 16 * mb + mm, q = l >> 4;
+            const int ii = 4 * q + (j & 3) + 16 * (j >> 2);
+            const int ib = ii >> 4, dl = (ii & 15) + 16 * (mm >> 2), de = mm & 3;
+            const float sum = s_dz[((ib * MB + mb) * 64 + dl) * 4 + de];
+            const int i = 32 * w + ii;
+            const float al = bf16_to_f32(p.alpha[i < p.r ? i : p.r - 1]);
+            const float zz = (i < p.r && m < p.M) ? sum * al : 0.0f;
+            const uint32_t zh = f32_to_bf16_rne(zz);
+            const uint32_t zl = f32_to_bf16_rne(zz - bf16_to_f32(zh));
+            // pair with the partner thread (j ^ 4) of the same 8-thread group
+            const uint32_t oh = __shfl_xor(zh, 4, 64), ol = __shfl_xor(zl, 4, 64);
+            if (j < 4) {
+                uint16_t *dst = reinterpret_cast<uint16_t *>(p.zA + ((((int64_t)w * MB + mb) * 2) * 64 + l) * 4 + j);
+                reinterpret_cast<uint32_t *>(dst)[0] = zh | (oh << 16);
+                reinterpret_cast<uint32_t *>(dst)[64 * 4] = zl | (ol << 16);
+            }
+        }
+    }
+    TLM(5);
+}
+
+// The K-slice sum with z's correction (z-in-epilogue schedule).  Workgroup
+// b takes m-block b % MB of the 8 row blocks from 8 (b / MB), one per wave:
+// z's operands of that m-block (every word's bf16 high and low parts) go to
+// LDS once, then each wave sums the slices' partials of its tile (g times
+// the product, D layout), adds z . U+- by bf16 MFMAs of z against U's signs
+// over every word, and stores.
+constexpr int kEpWaves = 8;
+template <int MB>
+__global__ void __launch_bounds__(64 * kEpWaves) mfma_epilogue_zc_kernel(MfmaParams p) {
+    extern __shared__ u32x4_t s_za[];             // [W][2 hi/lo][64 lanes]
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int col = lane & 15, grp = lane >> 4;
+    const int mb = blockIdx.x % MB, rb = (blockIdx.x / MB) * kEpWaves + wave;
+    const int n = rb * 16 + col, m0 = 16 * mb + 4 * grp;
+    const int nc = min(n, p.N - 1);
+    // z's operands (at most 32 words: 8 16-byte pieces per thread), U's
+    // words of this lane's row, the slices' partials: all requested first
+    constexpr int kZaPieces = 32 * 2 * 64 / (64 * kEpWaves);
+    u32x4_t za[kZaPieces];
+    const __amdgpu_buffer_rsrc_t r_za = buffer_of(p.zA, (int64_t)p.W * MB * 2 * 64 * 16);
+#pragma unroll
+    for (int j = 0; j < kZaPieces; ++j) {
+        const int idx = (int)threadIdx.x + 64 * kEpWaves * j;
+        const int l = idx & 63, h = (idx >> 6) & 1, w = idx >> 7;
+        za[j] = load16(r_za, opaque(w < p.W ? ((((w * MB + mb) * 2 + h) * 64) + l) * 16 : kOob));
+    }
+    const bool live = rb < p.RB;
+    const int rbc = live ? rb : p.RB - 1;
+    const float4_t *ypart = reinterpret_cast<const float4_t *>(p.ypart);
+    float4_t v = float4_t{0.f, 0.f, 0.f, 0.f};
+    for (int t0 = 0; t0 < p.S; t0 += kSumBatch) {
+        float4_t part[kSumBatch];
+#pragma unroll
+        for (int tt = 0; tt < kSumBatch; ++tt)
+            part[tt] = ypart[((int64_t)min(t0 + tt, p.S - 1) * p.RB + rbc) * MB * 64 + (int64_t)mb * 64 + lane];
+#pragma unroll
+        for (int tt = 0; tt < kSumBatch; ++tt)
+            if (t0 + tt < p.S) v += part[tt];
+    }
+    const __amdgpu_buffer_rsrc_t r_u = buffer_of(p.u, (int64_t)p.W * p.N * 4);
+    uint32_t uw[32];
+#pragma unroll
+    for (int j = 0; j < 32; ++j)
+        uw[j] = __builtin_amdgcn_raw_buffer_load_b32(r_u, opaque(j < p.W ? (j * p.N + nc) * 4 : kOob), 0, 0);
+#pragma unroll
+    for (int j = 0; j < kZaPieces; ++j) {
+        const int idx = (int)threadIdx.x + 64 * kEpWaves * j;
+        if (idx < p.W * 2 * 64) s_za[idx] = za[j];
+    }
+    __syncthreads();
+    // every word: the MFMAs of z (from LDS) against U's signs
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+        if (j < p.W) {
+            const uint32_t t = uw[j];
+            const u32x4_t bv = {sign_pair_bf16(t, 4 * grp + 0), sign_pair_bf16(t, 4 * grp + 1),
+                                sign_pair_bf16(t, 4 * grp + 2), sign_pair_bf16(t, 4 * grp + 3)};
+            v = mfma_bf16(s_za[(j * 2 + 0) * 64 + lane], bv, v);
+            v = mfma_bf16(s_za[(j * 2 + 1) * 64 + lane], bv, v);
+        }
+    }
+    if (live && n < p.N) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (m0 + e < p.M) store_y(p, (int64_t)(m0 + e) * p.N + n, v[e]);
+    }
+}
+
+// =====================================================================
 // launch 2: the product
 // =====================================================================
 // Workgroup (slice s, row-block range).  Wave q owns the chunks
@@ -589,11 +889,13 @@ __device__ __forceinline__ void side_z_workgroup(const MfmaParams &p, float4_t *
 // and the hardware wait counts stay exact.
 // ZM: 0 = z from the z launch (operands complete at the start); 1 = every
 // workgroup computes a tile of z at entry (all-workgroup schedule); 2 = the
-// first n_side workgroups compute z (side-workgroup schedule).  With 1 and 2
-// the product applies tagged z words after its row blocks.
+// first n_side workgroups compute z (side-workgroup schedule); 3 = the first
+// kZeParts workgroups compute z for the epilogue, and the product applies
+// no correction (z-in-epilogue schedule).  With 1 and 2 the product applies
+// tagged z words after its row blocks.
 template <int MB, int RBW, int CPW, int ZM>
 __global__ void __launch_bounds__(kPThreads) mfma_product_kernel(MfmaParams p) {
-    constexpr bool ONE = ZM != 0, TILE = ZM == 1, SIDE = ZM == 2;
+    constexpr bool ONE = ZM == 1 || ZM == 2, TILE = ZM == 1, SIDE = ZM == 2, EPI = ZM == 3;
     constexpr int PPR = scale_pieces(CPW);              // 16-byte scale pieces per row
     constexpr int kPipe = MfmaShape<MB>::kPipe;
     static_assert(!TILE || RBW >= 3, "the z tile's wave sums use the last two row-block slots");
@@ -625,6 +927,12 @@ __global__ void __launch_bounds__(kPThreads) mfma_product_kernel(MfmaParams p) {
     if constexpr (SIDE) {
         if ((int)blockIdx.x < p.n_side) {
             side_z_workgroup<MB>(p, s_part);
+            return;
+        }
+    }
+    if constexpr (EPI) {
+        if ((int)blockIdx.x < p.n_side) {
+            ze_side_workgroup<MB>(p, s_part);
             return;
         }
     }
@@ -662,7 +970,7 @@ __global__ void __launch_bounds__(kPThreads) mfma_product_kernel(MfmaParams p) {
     };
     if (has_tile) z_load(0);
     // slice-major work index: the workgroups of one K-slice share an XCD
-    const int wt = SIDE ? xcd_major_index((int)blockIdx.x - p.n_side, (int)gridDim.x - p.n_side)
+    const int wt = SIDE || EPI ? xcd_major_index((int)blockIdx.x - p.n_side, (int)gridDim.x - p.n_side)
                         : xcd_major_index((int)blockIdx.x, (int)gridDim.x);
     const int s = wt / p.Gs, wgi = wt % p.Gs;
     const int rb_begin = (int)((int64_t)wgi * p.RB / p.Gs);      // Gs row groups of <= RBW blocks
@@ -708,7 +1016,7 @@ __global__ void __launch_bounds__(kPThreads) mfma_product_kernel(MfmaParams p) {
     const int pb = rb_begin, nrb = rb_end - rb_begin;     // 1 .. RBW row blocks
 
     // correction words of this wave: w = s + S (wave + 8 j)
-    const int nws = p.W > s ? (p.W - s + p.S - 1) / p.S : 0;
+    const int nws = !EPI && p.W > s ? (p.W - s + p.S - 1) / p.S : 0;
 
     // ---- correction operands for the first word of this wave
     u32x4_t zz[MB][2];
@@ -1208,8 +1516,11 @@ struct MfmaPlan {
     // side-workgroup schedule: side workgroups ahead of the product's, and
     // whether each word's K is split over two of them
     int n_side, side_split;
+    // z-in-epilogue schedule: K-steps per side workgroup's part, and per
+    // round staged in LDS
+    int ze_steps, ze_sub;
     // workspace offsets inside the matrix-core area
-    size_t off_zpart, off_za, off_ypart, off_zpt, off_zat, off_zhp, bytes;
+    size_t off_zpart, off_za, off_ypart, off_zpt, off_zat, off_zhp, off_zep, bytes;
 };
 
 size_t align256(size_t b) { return (b + 255) / 256 * 256; }
@@ -1300,6 +1611,20 @@ MfmaPlan mfma_plan(int M, int N, int K, int r, int grid_target = kGridTarget) {
         q.off_zpt = off;
         off += (size_t)q.ntiles * q.mb * 128 * 16;
     }
+    // z-in-epilogue schedule (K split): the side workgroups' z partials
+    if (q.W > 0 && q.S > 1) {
+        q.ze_steps = (steps + kZeParts - 1) / kZeParts;
+        // a staged round: its LDS fits the product's, and its loads kZeLoads
+        // 16-byte pieces of x and of V per thread
+        const size_t per_step = (size_t)q.mb * 64 * 16 + (size_t)q.W * 32 * 4;
+        q.ze_sub = (int)(q.lds / per_step);
+        q.ze_sub = std::min(q.ze_sub, q.ze_steps);
+        q.ze_sub = std::min(q.ze_sub, kZeLoads * kPThreads / (64 * q.mb));
+        q.ze_sub = std::min(q.ze_sub, kZeLoads * kPThreads / (8 * q.W));
+        off = align256(off);
+        q.off_zep = off;
+        off += (size_t)kZeParts * q.W * 2 * q.mb * 64 * 16;
+    }
     q.bytes = off > 0 ? align256(off) : 0;
     return q;
 }
@@ -1347,6 +1672,35 @@ bool mfma_side_supported(int M, int N, int K, int r) {
     // workgroups leave, and the side path's LDS fits the product's
     return q.grid + q.n_side <= kGridTarget && q.lds <= kLdsLimit &&
            (size_t)kPWaves * q.mb * 2 * 64 * 16 + (size_t)q.mb * 16 * 32 * 4 <= q.lds;
+}
+
+namespace {
+// the product's plan with room for the z-in-epilogue side workgroups
+// (kZeParts side workgroups; fewer, in multiples of 8, where the product's
+// workgroups would not fit the CUs left)
+MfmaPlan ze_plan(int M, int N, int K, int r) {
+    MfmaPlan q = mfma_plan(M, N, K, r, kGridTarget - kZeParts);
+    q.n_side = kZeParts;
+    if (q.grid + q.n_side > kGridTarget && kGridTarget - q.grid >= 8) q.n_side = (kGridTarget - q.grid) / 8 * 8;
+    // K-steps per part for this many parts, and per staged round
+    q.ze_steps = (K / 32 + q.n_side - 1) / q.n_side;
+    const size_t per_step = (size_t)q.mb * 64 * 16 + (size_t)q.W * 32 * 4;
+    q.ze_sub = (int)std::min<size_t>(q.lds / per_step, (size_t)q.ze_steps);
+    q.ze_sub = std::min(q.ze_sub, kZeLoads * kPThreads / (64 * q.mb));
+    q.ze_sub = std::min(q.ze_sub, kZeLoads * kPThreads / (8 * q.W));
+    return q;
+}
+}  // namespace
+
+bool mfma_ze_supported(int M, int N, int K, int r) {
+    if (r < 1 || r > 32 * kZeWordsPerWave * kPWaves || !mfma_supported(M, N, K, r)) return false;
+    const MfmaPlan q = ze_plan(M, N, K, r);
+    // K split (the epilogue launch applies z) and a round of the side
+    // workgroups' staging fits the product's LDS.  (No product workgroup
+    // waits for anything, so a grid past one workgroup per CU only costs a
+    // second round of them; the side workgroups, dispatched first, wait only
+    // for one another, within a bound.)
+    return q.S > 1 && q.ze_sub >= 1;
 }
 
 size_t mfma_ws_bytes(int M, int N, int K, int r) {
@@ -1406,6 +1760,11 @@ MfmaParams mfma_params(const GemmArgs &a, const MfmaPlan &q) {
             p.g8 = q.g8;
         }
     }
+    if (q.W > 0 && q.S > 1 && q.bytes > 0) {
+        char *ws = static_cast<char *>(a.ws) + (a.ws_is_mfma_area ? 0 : ws_mfma_offset(a.M, a.r));
+        p.zep = reinterpret_cast<float4_t *>(ws + q.off_zep);
+        p.zecnt = reinterpret_cast<uint32_t *>(static_cast<char *>(a.ws) + kWsZeCntOffset);
+    }
     static const uint32_t spin = spin_limit_default();
     p.spin_limit = spin;
     return p;
@@ -1414,7 +1773,7 @@ MfmaParams mfma_params(const GemmArgs &a, const MfmaPlan &q) {
 // The product launch (and, with K split, the epilogue launch).
 template <int ZM>
 hipError_t launch_product(const MfmaPlan &q, const MfmaParams &p, hipStream_t stream) {
-    const dim3 grid(q.grid + (ZM == 2 ? q.n_side : 0)), block(kPThreads);
+    const dim3 grid(q.grid + (ZM == 2 || ZM == 3 ? q.n_side : 0)), block(kPThreads);
     const size_t lds = ZM == 1 ? q.lds_one : q.lds;
     constexpr int c1 = MfmaShape<1>::kCpw, c2 = MfmaShape<2>::kCpw;
     constexpr int s1 = MfmaShape<1>::kRbwSmall, l1 = MfmaShape<1>::kRbwLarge;
@@ -1441,7 +1800,16 @@ hipError_t launch_product(const MfmaPlan &q, const MfmaParams &p, hipStream_t st
     e = hipGetLastError();
     if (e != hipSuccess || q.S == 1) return e;
     const int items = q.RB * q.mb * 64;
-    if (q.mb == 1)
+    if (ZM == 3) {
+        // the K-slice sum with z's correction: kEpWaves row blocks of one
+        // m-block per workgroup, z's operands of that m-block in LDS
+        const dim3 eg(q.mb * ((q.RB + kEpWaves - 1) / kEpWaves)), eb(64 * kEpWaves);
+        const size_t elds = (size_t)q.W * 2 * 64 * 16;
+        if (q.mb == 1)
+            hipLaunchKernelGGL(mfma_epilogue_zc_kernel<1>, eg, eb, elds, stream, p);
+        else
+            hipLaunchKernelGGL(mfma_epilogue_zc_kernel<2>, eg, eb, elds, stream, p);
+    } else if (q.mb == 1)
         hipLaunchKernelGGL(mfma_epilogue_kernel<1>, dim3((items + 255) / 256), dim3(256), 0, stream, p);
     else
         hipLaunchKernelGGL(mfma_epilogue_kernel<2>, dim3((items + 255) / 256), dim3(256), 0, stream, p);
@@ -1508,6 +1876,18 @@ hipError_t launch_gemm_mfma_side(const GemmArgs &a, hipStream_t stream) {
     p.n_side = q.n_side;
     p.side_split = q.side_split;
     return launch_product<2>(q, p, stream);
+}
+
+// z in side workgroups of the product launch, by K-part; its correction in
+// the K-slice epilogue launch (K split only).
+hipError_t launch_gemm_mfma_ze(const GemmArgs &a, hipStream_t stream) {
+    if (!mfma_ze_supported(a.M, a.N, a.K, a.r)) return hipErrorNotSupported;
+    const MfmaPlan q = ze_plan(a.M, a.N, a.K, a.r);
+    MfmaParams p = mfma_params(a, q);
+    p.n_side = q.n_side;
+    p.zsteps = q.ze_steps;
+    p.ze_sub = q.ze_sub;
+    return launch_product<3>(q, p, stream);
 }
 
 #ifdef BILOCO_TIMELINE

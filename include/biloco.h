@@ -65,7 +65,9 @@ typedef int32_t biloco_status;
                                        sums its K-slices), then one product kernel whose
                                        accumulators take the correction before the store,
                                        then (only when K is split over workgroups) a launch
-                                       that sums the K-slices; the default at M >= 3 */
+                                       that sums the K-slices; the default at M >= 3 where
+                                       neither BILOCO_SCHED_MFMA_SIDE nor
+                                       BILOCO_SCHED_MFMA_ZEPI applies */
 #define BILOCO_SCHED_COMPOSED    4  /* separate launches: the plain FP4 product (fp32, in the
                                        workspace), z, then y = bf16(product + z . U^T) by
                                        4-bit sign lookup tables: the unfused form the fused
@@ -94,6 +96,18 @@ typedef int32_t biloco_status;
                                        the K-slice sum launch when K is split.  Needs
                                        every workgroup resident at once for its speed, not
                                        for its results (bounded waits, as above) */
+#define BILOCO_SCHED_MFMA_ZEPI   8  /* matrix-core products, 1 <= r <= 1024, K split over
+                                       workgroups (the default at M >= 3 there, unless
+                                       BILOCO_SCHED_MFMA_SIDE applies): one product launch
+                                       whose first 8 to 32 workgroups stream no rows and
+                                       compute z, a K-part of every word each, then
+                                       finish its words; the
+                                       product takes no correction; the launch that sums
+                                       the K-slices adds z . U^T (bf16 MFMAs of z's high
+                                       and low parts against U's signs) before the store.
+                                       The side workgroups' wait for one another is
+                                       bounded, after which the words still missing are
+                                       computed from x and V (slow) */
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char *biloco_status_string(biloco_status s);

@@ -107,7 +107,7 @@ def test_schedule_queries():
         for sch in avail:
             assert B.biloco_gemm_check(*_args(M, N, K, r), schedule=sch) == B.BILOCO_OK
     assert B.biloco_default_schedule(0, 1, 32, 0) == 0
-    assert B.biloco_gemm_check(*_args(), schedule=B.BILOCO_SCHED_MFMA_SIDE + 1) == B.BILOCO_ERR_INVALID_VALUE
+    assert B.biloco_gemm_check(*_args(), schedule=B.BILOCO_SCHED_MFMA_ZEPI + 1) == B.BILOCO_ERR_INVALID_VALUE
 
 
 def test_prep_entry_points_reject_before_hip():

@@ -160,11 +160,12 @@ for (M, K, N, r) in [(1, 256, 256, 16), (2, 1024, 300, 40), (1, 5120, 512, 512)]
         p.gemm(B.BILOCO_SCHED_FUSED_GEMV)
     torch.cuda.synchronize()
     check_y(p.y_float(), y_ref, f'fallback {{(M, K, N, r)}}')
-for (M, K, N, r) in [(8, 1024, 300, 40), (32, 2048, 200, 100), (3, 512, 64, 33), (8, 1024, 200, 500)]:
+for (M, K, N, r) in [(8, 1024, 300, 40), (32, 2048, 200, 100), (3, 512, 64, 33), (8, 1024, 200, 500),
+                     (32, 4096, 300, 100), (5, 8192, 300, 70)]:
     d = wl.make_inputs(M, K, N, r, seed=41 + M)
     y_ref = oracle.gemm_lowrank(d['x'], d['wcode'], d['wscales'], d['g'], d['V'], d['U'], d['alpha'])
     p = DeviceProblem(d)
-    for sched in (B.BILOCO_SCHED_MFMA_ALLWG, B.BILOCO_SCHED_MFMA_SIDE):
+    for sched in (B.BILOCO_SCHED_MFMA_ALLWG, B.BILOCO_SCHED_MFMA_SIDE, B.BILOCO_SCHED_MFMA_ZEPI):
         if sched not in B.biloco_schedules_for(M, N, K, r):
             continue
         for it in range(3):
