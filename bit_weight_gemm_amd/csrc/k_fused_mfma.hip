@@ -609,6 +609,10 @@ __device__ void ze_side_workgroup(const MfmaParams &p, float4_t *lds) {
     const int part = blockIdx.x, P = p.n_side;
     TLM(0);
     TLMV(14, 1);
+    // the barrier's generation, read first (it cannot change before this
+    // workgroup counts itself in, and the memory system is quiet now)
+    __shared__ uint32_t s_gen;
+    if (threadIdx.x == 0) s_gen = ld_u32(p.zecnt + 1);
     const int steps = p.K >> 5;
     const int st0 = part * p.zsteps;
     const int nst = max(0, min(p.zsteps, steps - st0));
@@ -713,8 +717,7 @@ __device__ void ze_side_workgroup(const MfmaParams &p, float4_t *lds) {
     __syncthreads();
     __shared__ uint32_t s_ok;
     if (threadIdx.x == 0) {
-        const uint32_t gen = ld_u32(p.zecnt + 1);
-        __builtin_amdgcn_s_waitcnt(0);          // the generation is read before counting in
+        const uint32_t gen = s_gen;
         bool ok = true;
         if (arrive(p.zecnt) == (uint32_t)(P - 1)) {
             // (the cleared counter is needed only by the next call, after
@@ -806,22 +809,22 @@ __device__ void ze_side_workgroup(const MfmaParams &p, float4_t *lds) {
 }
 
 // The K-slice sum with z's correction (z-in-epilogue schedule).  Workgroup
-// b takes m-block b % MB of the 8 row blocks from 8 (b / MB), one per wave:
-// z's operands of that m-block (every word's bf16 high and low parts) go to
-// LDS once, then each wave sums the slices' partials of its tile (g times
-// the product, D layout), adds z . U+- by bf16 MFMAs of z against U's signs
-// over every word, and stores.
-constexpr int kEpWaves = 8;
+// b takes m-block b % MB of the kEpWaves kEpRbw row blocks from
+// kEpWaves kEpRbw (b / MB), kEpRbw per wave: z's operands of that m-block
+// (every word's bf16 high and low parts) go to LDS once, then each wave
+// sums the slices' partials of its tiles (g times the product, D layout),
+// adds z . U+- by bf16 MFMAs of z against U's signs over every word, and
+// stores.
+constexpr int kEpWaves = 4, kEpRbw = 1;
 template <int MB>
 __global__ void __launch_bounds__(64 * kEpWaves) mfma_epilogue_zc_kernel(MfmaParams p) {
     extern __shared__ u32x4_t s_za[];             // [W][2 hi/lo][64 lanes]
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int col = lane & 15, grp = lane >> 4;
-    const int mb = blockIdx.x % MB, rb = (blockIdx.x / MB) * kEpWaves + wave;
-    const int n = rb * 16 + col, m0 = 16 * mb + 4 * grp;
-    const int nc = min(n, p.N - 1);
+    const int mb = blockIdx.x % MB, rb0 = ((blockIdx.x / MB) * kEpWaves + wave) * kEpRbw;
+    const int m0 = 16 * mb + 4 * grp;
     // z's operands (at most 32 words: 8 16-byte pieces per thread), U's
-    // words of this lane's row, the slices' partials: all requested first
+    // words of this lane's rows, the slices' partials: all requested first
     constexpr int kZaPieces = 32 * 2 * 64 / (64 * kEpWaves);
     u32x4_t za[kZaPieces];
     const __amdgpu_buffer_rsrc_t r_za = buffer_of(p.zA, (int64_t)p.W * MB * 2 * 64 * 16);
@@ -831,24 +834,31 @@ __global__ void __launch_bounds__(64 * kEpWaves) mfma_epilogue_zc_kernel(MfmaPar
         const int l = idx & 63, h = (idx >> 6) & 1, w = idx >> 7;
         za[j] = load16(r_za, opaque(w < p.W ? ((((w * MB + mb) * 2 + h) * 64) + l) * 16 : kOob));
     }
-    const bool live = rb < p.RB;
-    const int rbc = live ? rb : p.RB - 1;
     const float4_t *ypart = reinterpret_cast<const float4_t *>(p.ypart);
-    float4_t v = float4_t{0.f, 0.f, 0.f, 0.f};
-    for (int t0 = 0; t0 < p.S; t0 += kSumBatch) {
-        float4_t part[kSumBatch];
+    float4_t v[kEpRbw];
 #pragma unroll
-        for (int tt = 0; tt < kSumBatch; ++tt)
-            part[tt] = ypart[((int64_t)min(t0 + tt, p.S - 1) * p.RB + rbc) * MB * 64 + (int64_t)mb * 64 + lane];
+    for (int rr = 0; rr < kEpRbw; ++rr) {
+        const int rbc = min(rb0 + rr, p.RB - 1);
+        v[rr] = float4_t{0.f, 0.f, 0.f, 0.f};
+        for (int t0 = 0; t0 < p.S; t0 += kSumBatch) {
+            float4_t part[kSumBatch];
 #pragma unroll
-        for (int tt = 0; tt < kSumBatch; ++tt)
-            if (t0 + tt < p.S) v += part[tt];
+            for (int tt = 0; tt < kSumBatch; ++tt)
+                part[tt] = ypart[((int64_t)min(t0 + tt, p.S - 1) * p.RB + rbc) * MB * 64 + (int64_t)mb * 64 + lane];
+#pragma unroll
+            for (int tt = 0; tt < kSumBatch; ++tt)
+                if (t0 + tt < p.S) v[rr] += part[tt];
+        }
     }
     const __amdgpu_buffer_rsrc_t r_u = buffer_of(p.u, (int64_t)p.W * p.N * 4);
-    uint32_t uw[32];
+    uint32_t uw[kEpRbw][32];
 #pragma unroll
-    for (int j = 0; j < 32; ++j)
-        uw[j] = __builtin_amdgcn_raw_buffer_load_b32(r_u, opaque(j < p.W ? (j * p.N + nc) * 4 : kOob), 0, 0);
+    for (int rr = 0; rr < kEpRbw; ++rr) {
+        const int nc = min((rb0 + rr) * 16 + col, p.N - 1);
+#pragma unroll
+        for (int j = 0; j < 32; ++j)
+            uw[rr][j] = __builtin_amdgcn_raw_buffer_load_b32(r_u, opaque(j < p.W ? (j * p.N + nc) * 4 : kOob), 0, 0);
+    }
 #pragma unroll
     for (int j = 0; j < kZaPieces; ++j) {
         const int idx = (int)threadIdx.x + 64 * kEpWaves * j;
@@ -859,17 +869,25 @@ __global__ void __launch_bounds__(64 * kEpWaves) mfma_epilogue_zc_kernel(MfmaPar
 #pragma unroll
     for (int j = 0; j < 32; ++j) {
         if (j < p.W) {
-            const uint32_t t = uw[j];
-            const u32x4_t bv = {sign_pair_bf16(t, 4 * grp + 0), sign_pair_bf16(t, 4 * grp + 1),
-                                sign_pair_bf16(t, 4 * grp + 2), sign_pair_bf16(t, 4 * grp + 3)};
-            v = mfma_bf16(s_za[(j * 2 + 0) * 64 + lane], bv, v);
-            v = mfma_bf16(s_za[(j * 2 + 1) * 64 + lane], bv, v);
+            const u32x4_t zh = s_za[(j * 2 + 0) * 64 + lane], zl = s_za[(j * 2 + 1) * 64 + lane];
+#pragma unroll
+            for (int rr = 0; rr < kEpRbw; ++rr) {
+                const uint32_t t = uw[rr][j];
+                const u32x4_t bv = {sign_pair_bf16(t, 4 * grp + 0), sign_pair_bf16(t, 4 * grp + 1),
+                                    sign_pair_bf16(t, 4 * grp + 2), sign_pair_bf16(t, 4 * grp + 3)};
+                v[rr] = mfma_bf16(zh, bv, v[rr]);
+                v[rr] = mfma_bf16(zl, bv, v[rr]);
+            }
         }
     }
-    if (live && n < p.N) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            if (m0 + e < p.M) store_y(p, (int64_t)(m0 + e) * p.N + n, v[e]);
+    for (int rr = 0; rr < kEpRbw; ++rr) {
+        const int n = (rb0 + rr) * 16 + col;
+        if (rb0 + rr < p.RB && n < p.N) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (m0 + e < p.M) store_y(p, (int64_t)(m0 + e) * p.N + n, v[rr][e]);
+        }
     }
 }
 
@@ -1803,7 +1821,7 @@ hipError_t launch_product(const MfmaPlan &q, const MfmaParams &p, hipStream_t st
     if (ZM == 3) {
         // the K-slice sum with z's correction: kEpWaves row blocks of one
         // m-block per workgroup, z's operands of that m-block in LDS
-        const dim3 eg(q.mb * ((q.RB + kEpWaves - 1) / kEpWaves)), eb(64 * kEpWaves);
+        const dim3 eg(q.mb * ((q.RB + kEpWaves * kEpRbw - 1) / (kEpWaves * kEpRbw))), eb(64 * kEpWaves);
         const size_t elds = (size_t)q.W * 2 * 64 * 16;
         if (q.mb == 1)
             hipLaunchKernelGGL(mfma_epilogue_zc_kernel<1>, eg, eb, elds, stream, p);
