@@ -72,7 +72,8 @@ def code_text(src: str) -> str:
 # gives as the sum of these kernels' averages
 CALL_KERNELS = {"unfused": "z_kernel + fused_gemv_kernel",
                 "fused_mfma": "mfma_z_kernel + mfma_zreduce_kernel (K > 7168) + "
-                              "mfma_product_kernel + mfma_epilogue_kernel (split K)"}
+                              "mfma_product_kernel + mfma_epilogue_kernel (split K)",
+                "mfma_zepi": "mfma_product_kernel (z in its side workgroups) + mfma_epilogue_zc_kernel"}
 
 
 # the sources a schedule's launches are built from (the hash that keys its
@@ -81,7 +82,8 @@ SCHED_FILES = {"fused_gemv": ["k_fused_gemv.hip", "biloco_device.h", "biloco_int
                "mfma_allwg": ["k_fused_mfma.hip", "biloco_device.h", "biloco_internal.h"],
                "mfma_side": ["k_fused_mfma.hip", "biloco_device.h", "biloco_internal.h"],
                "unfused": ["k_fused_gemv.hip", "biloco_device.h", "biloco_internal.h"],
-               "fused_mfma": ["k_fused_mfma.hip", "biloco_device.h", "biloco_internal.h"]}
+               "fused_mfma": ["k_fused_mfma.hip", "biloco_device.h", "biloco_internal.h"],
+               "mfma_zepi": ["k_fused_mfma.hip", "biloco_device.h", "biloco_internal.h"]}
 
 
 def source_hash(sched_name: str | None = None) -> str:
@@ -607,10 +609,13 @@ def timeline(args) -> int:
         if (~stream_wg).any():
             groups["side workgroups"] = (~stream_wg, [0, 2])
     else:
-        prod = tl[:, 0, 1] > 0          # side workgroups stream no rows
+        ze = tl[:, 0, 14] == 1          # the z-in-epilogue schedule's side workgroups
+        prod = (tl[:, 0, 1] > 0) & ~ze  # side workgroups stream no rows
         groups["product workgroups"] = (prod, [k for k in range(len(names)) if k != 6])
-        if (~prod).any():
-            groups["side workgroups"] = (~prod, [0, 3, 4, 5, 6, 2])
+        if (~prod & ~ze).any():
+            groups["side workgroups"] = (~prod & ~ze, [0, 3, 4, 5, 6, 2])
+        if ze.any():
+            groups["z-in-epilogue side workgroups"] = (ze, [0, 1, 2, 3, 4, 5])
         fin = tl[:, 0, 12] == 1
         if fin.any():
             groups["finisher workgroups"] = (fin, [6])
@@ -626,7 +631,10 @@ def timeline(args) -> int:
             v = rel[mask, :, k].ravel()
             v = v[~np.isnan(v)]
             label = names[k]
-            if gname.startswith("side"):
+            if gname.startswith("z-in-epilogue"):
+                label = {0: "start", 1: "x and V part staged in LDS", 2: "part's MFMAs done",
+                         3: "partials stored", 4: "every part counted in", 5: "words finished"}[k]
+            elif gname.startswith("side"):
                 label = {2: "z published" if fam == "gemv" else "z words published",
                          3: "first word: first loads issued", 4: "first word: first loads used",
                          5: "first word: second loads used", 6: "first word: waves' sums in LDS"}.get(k, label)
