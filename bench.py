@@ -643,6 +643,20 @@ def timeline(args) -> int:
                                   (("min", 0), ("p10", 10), ("median", 50), ("p90", 90), ("max", 100))}
                 rows[label]["waves"] = int(v.size)
         out["groups"][gname] = rows
+    if fam == "mfma" and prod.any():
+        # where the product's time goes: by wave index inside the workgroup,
+        # the spread between a workgroup's first and last wave, and by XCD
+        # (workgroup b runs on XCD b % 8)
+        kd, ks = names.index("row blocks done"), names.index("stored")
+        done = rel[prod, :, kd]
+        spread = np.nanmax(done, axis=1) - np.nanmin(done, axis=1)
+        xcd = wgs[prod] % 8
+        out["product_breakdown"] = {
+            "row_blocks_done_median_by_wave": [round(float(np.nanmedian(done[:, w])), 2) for w in range(8)],
+            "within_workgroup_spread_us": {q: round(float(np.nanpercentile(spread, pc)), 2) for q, pc in
+                                           (("p10", 10), ("median", 50), ("p90", 90))},
+            "stored_median_by_xcd": [round(float(np.nanmedian(rel[prod, 0, ks][xcd == x])), 2)
+                                     if (xcd == x).any() else None for x in range(8)]}
     cmd = "python3 bench.py --timeline --config %d%s%s%s" % (
         cfg, f" --schedule {args.schedule}" if args.schedule else "",
         " --timeline-r0" if args.timeline_r0 else "", " --timeline-step" if step else "")
@@ -662,6 +676,14 @@ def timeline(args) -> int:
         for k, v in rows.items():
             lines.append(f"| {k} | {v['waves']} | {v['min']} | {v['p10']} | {v['median']} | {v['p90']} | {v['max']} |")
         lines.append("")
+    if "product_breakdown" in out:
+        pb = out["product_breakdown"]
+        lines += ["## product workgroups: where the time goes", "",
+                  "- row blocks done, median by wave index 0..7: " +
+                  ", ".join(str(v) for v in pb["row_blocks_done_median_by_wave"]),
+                  "- spread between a workgroup's first and last wave to finish its row blocks (p10 / median / p90): "
+                  + " / ".join(str(v) for v in pb["within_workgroup_spread_us"].values()),
+                  "- stored, median by XCD 0..7: " + ", ".join(str(v) for v in pb["stored_median_by_xcd"]), ""]
     tag = "_step" if step else ""
     path = os.path.join(ROOT, "profiles", f"timeline_{out['schedule']}_{wname}{tag}.md")
     with open(path, "w") as f:

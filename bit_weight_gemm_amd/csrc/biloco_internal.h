@@ -43,8 +43,8 @@ struct GemmArgs {
 //                          schedule's z tiles (at most kWsZcntMax words), zero
 //                          between calls
 //   [kWsZeCntOffset, 64 KiB) the arrival counter of the z-in-epilogue
-//                          schedule's side workgroups (it only grows, by
-//                          kZeParts per call)
+//                          schedule's side workgroups, zero between calls
+//                          (that schedule's K-slice sum launch clears it)
 //   [64 KiB, 80 KiB)       z as (fp32 value | 32-bit epoch tag << 32) words of
 //                          the one-launch vector schedule, [MM <= 2][rpad <= 1024]
 //   [80 KiB, ...)          the areas of the shape, in this order:

@@ -156,7 +156,7 @@ struct MfmaParams {
     // time), then finish its words; the K-slice epilogue applies them
     int ze_sub;
     float4_t *zep;              // partials [kZeParts][W][2 rank halves][MB][64 lanes] (D layout)
-    uint32_t *zecnt;            // the side workgroups' arrival counter [0] and generation [1]
+    uint32_t *zecnt;            // the side workgroups' arrival counter (zero between calls)
 };
 
 // One output element: bf16 into y, or fp32 into yf when the caller asked for it.
@@ -587,18 +587,32 @@ __device__ __forceinline__ void side_z_workgroup(const MfmaParams &p, float4_t *
 // Side workgroup p of P (n_side) takes K-steps [p zs, (p + 1) zs) of every
 // word: it stages that part of x (A-operand order) and of V's words in LDS,
 // ze_sub K-steps at a time, and wave q computes words q, q + 8, ... with
-// bf16 MFMAs of x against V's +-1 signs (bits k and k + 1 of a rank paired
-// into one dword by a byte permute).  It stores its partials (D layout) with
-// 16-byte stores through to the coherence point (sc1), counts itself in, and
-// waits (bounded) until all P have; then it sums the parts of words p,
-// p + P, ..., scales them by alpha and stores z's bf16 high and low parts in
-// the correction operand's order (zA), read by the epilogue launch after
-// this one.  A word whose parts did not all arrive in time is computed from
-// x and V by the workgroup's wave 0 alone (z_word_local: slow, never
-// expected).  The wait is a sense-reversing barrier over a counter and a
-// generation word: each reads the generation, counts itself in, and the
-// last to arrive clears the counter and advances the generation, which the
-// others wait for.
+// bf16 MFMAs of x against V's +-1 signs.  The staging pairs the sign bits of
+// k and k + 1 of 16 ranks into one dword by a byte permute, once per dword;
+// the MFMA loop reads one such dword per lane and word for two K-steps and
+// hands it to the lane's 16-lane row by DPP broadcast.  It stores its
+// partials (D layout) with 16-byte stores through to the coherence point
+// (sc1), counts itself in, and waits (bounded) until all P have; then it
+// sums the parts of words p, p + P, ..., scales them by alpha and stores z's
+// bf16 high and low parts in the correction operand's order (zA), read by
+// the epilogue launch after this one.  A word whose parts did not all arrive
+// in time is computed from x and V by the workgroup's wave 0 alone
+// (z_word_local: slow, never expected).  The wait polls the arrival counter
+// itself, which starts every call at zero: the epilogue launch clears it,
+// after the launch boundary, when no side workgroup reads it any more.
+// B operand of +-1 signs from four pair dwords held by lanes L0 .. L0 + 3 of
+// this lane's 16-lane row (DPP row broadcast): this lane's rank is bit col
+// of each half
+template <int L0>
+__device__ __forceinline__ u32x4_t signs_from_row(uint32_t pv, uint32_t mcol, int col) {
+    const uint32_t p0 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)pv, 0x150 + L0, 0xF, 0xF, false);
+    const uint32_t p1 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)pv, 0x151 + L0, 0xF, 0xF, false);
+    const uint32_t p2 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)pv, 0x152 + L0, 0xF, 0xF, false);
+    const uint32_t p3 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)pv, 0x153 + L0, 0xF, 0xF, false);
+    const int sh = 15 - col;
+    return u32x4_t{((p0 & mcol) << sh) | 0x3F803F80u, ((p1 & mcol) << sh) | 0x3F803F80u,
+                   ((p2 & mcol) << sh) | 0x3F803F80u, ((p3 & mcol) << sh) | 0x3F803F80u};
+}
 constexpr int kZeParts = 32;      // side workgroups (K-parts) at most; a multiple of 8 per shape
 constexpr int kZeWordsPerWave = 4;    // r <= 1024: 32 words over 8 waves
 constexpr int kZeLoads = 8;           // 16-byte pieces of x, and of V, per thread per staged round
@@ -609,15 +623,14 @@ __device__ void ze_side_workgroup(const MfmaParams &p, float4_t *lds) {
     const int part = blockIdx.x, P = p.n_side;
     TLM(0);
     TLMV(14, 1);
-    // the barrier's generation, read first (it cannot change before this
-    // workgroup counts itself in, and the memory system is quiet now)
-    __shared__ uint32_t s_gen;
-    if (threadIdx.x == 0) s_gen = ld_u32(p.zecnt + 1);
     const int steps = p.K >> 5;
     const int st0 = part * p.zsteps;
     const int nst = max(0, min(p.zsteps, steps - st0));
     u32x4_t *s_x = reinterpret_cast<u32x4_t *>(lds);                     // [sub][MB][64]
-    uint32_t *s_v = reinterpret_cast<uint32_t *>(s_x + (size_t)p.ze_sub * MB * 64);   // [W][sub 32]
+    // V's bits of a word and K-step, as the B operand's lanes want them:
+    // [grp][ib][e] holds ranks 16 ib .. 16 ib + 15 at k = 8 grp + 2 e (low
+    // half) and + 1 (high half)
+    uint32_t *s_p = reinterpret_cast<uint32_t *>(s_x + (size_t)p.ze_sub * MB * 64);   // [W][sub][32]
     float4_t acc[kZeWordsPerWave][2][MB];
 #pragma unroll
     for (int jw = 0; jw < kZeWordsPerWave; ++jw)
@@ -627,6 +640,9 @@ __device__ void ze_side_workgroup(const MfmaParams &p, float4_t *lds) {
             for (int mb = 0; mb < MB; ++mb) acc[jw][ib][mb] = float4_t{0.f, 0.f, 0.f, 0.f};
     const __amdgpu_buffer_rsrc_t r_x = buffer_of(p.x, (int64_t)p.M * p.K * 2);
     const __amdgpu_buffer_rsrc_t r_v = buffer_of(p.v, (int64_t)p.W * p.K * 4);
+    // this lane's two sign bits of every pair dword (rank col, rank 16 + col)
+    const uint32_t mcol = 0x00010001u << col;
+    const int nwords = (p.W - wave + kPWaves - 1) / kPWaves;    // words of this wave
     for (int sub0 = 0; sub0 < nst; sub0 += p.ze_sub) {
         const int ns = min(p.ze_sub, nst - sub0);
         const int k00 = (st0 + sub0) * 32;
@@ -648,51 +664,67 @@ __device__ void ze_side_workgroup(const MfmaParams &p, float4_t *lds) {
             const int idx = (int)threadIdx.x + kPThreads * j;
             if (idx < ns * MB * 64) s_x[idx] = lx[j];
             const int w = idx / (ns * 8), j4 = idx - w * (ns * 8);
-            if (w < p.W) reinterpret_cast<u32x4_t *>(s_v + (size_t)w * p.ze_sub * 32)[j4] = lv[j];
+            if (w < p.W) {
+                // k = 4 q .. 4 q + 3 of step t: pairs e = 2 h and 2 h + 1 of
+                // group q / 2
+                const int t = j4 >> 3, q = j4 & 7, gq = q >> 1, h = q & 1;
+                uint32_t *dst = s_p + ((size_t)w * p.ze_sub + t) * 32 + gq * 8 + 2 * h;
+                *reinterpret_cast<uint2 *>(dst) =
+                    uint2{__builtin_amdgcn_perm(lv[j].y, lv[j].x, 0x05040100u),
+                          __builtin_amdgcn_perm(lv[j].w, lv[j].z, 0x05040100u)};
+                *reinterpret_cast<uint2 *>(dst + 4) =
+                    uint2{__builtin_amdgcn_perm(lv[j].y, lv[j].x, 0x07060302u),
+                          __builtin_amdgcn_perm(lv[j].w, lv[j].z, 0x07060302u)};
+            }
         }
         __syncthreads();
         TLM(1);
-        // K-step t's operands from LDS (x's A operand, this wave's words of
-        // V), read one step ahead of their MFMAs (two register sets)
-        struct ZeOps { u32x4_t a[MB]; u32x4_t v[kZeWordsPerWave][2]; };
+        // two K-steps per round of LDS reads: x's A operands of both, and one
+        // pair dword per lane and word (lanes col < 8 hold step t's eight,
+        // the others step t + 1's), which the row's lanes share by DPP
+        // broadcast; read one round ahead of their MFMAs (two register sets)
+        struct ZeOps { u32x4_t a[2][MB]; uint32_t pv[kZeWordsPerWave]; };
         auto ld_ops = [&](int t, ZeOps &o) {
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb) o.a[mb] = s_x[(t * MB + mb) * 64 + lane];
+            for (int s2 = 0; s2 < 2; ++s2) {
+                const int ts = min(t + s2, ns - 1);
 #pragma unroll
-            for (int jw = 0; jw < kZeWordsPerWave; ++jw) {
-                const int w = min(wave + kPWaves * jw, p.W - 1);
-                const uint32_t *vp = s_v + (size_t)w * p.ze_sub * 32 + t * 32 + 8 * grp;
-                o.v[jw][0] = *reinterpret_cast<const u32x4_t *>(vp);
-                o.v[jw][1] = *reinterpret_cast<const u32x4_t *>(vp + 4);
+                for (int mb = 0; mb < MB; ++mb) o.a[s2][mb] = s_x[(ts * MB + mb) * 64 + lane];
             }
+            const int tp = min(t + (col >> 3), ns - 1);
+#pragma unroll
+            for (int jw = 0; jw < kZeWordsPerWave; ++jw)
+                if (jw < nwords)
+                    o.pv[jw] = s_p[((size_t)(wave + kPWaves * jw) * p.ze_sub + tp) * 32 + grp * 8 + (col & 7)];
         };
-        auto step = [&](const ZeOps &o) {
+        auto step2 = [&](const ZeOps &o, int t) {
 #pragma unroll
-            for (int jw = 0; jw < kZeWordsPerWave; ++jw) {
-                if (wave + kPWaves * jw < p.W) {
-                    const uint32_t vw[8] = {o.v[jw][0].x, o.v[jw][0].y, o.v[jw][0].z, o.v[jw][0].w,
-                                            o.v[jw][1].x, o.v[jw][1].y, o.v[jw][1].z, o.v[jw][1].w};
+            for (int s2 = 0; s2 < 2; ++s2) {
+                if (s2 == 1 && t + 1 >= ns) break;
 #pragma unroll
-                    for (int ib = 0; ib < 2; ++ib) {
-                        // bits of rank 16 ib + col at k = 2e and 2e + 1 into one dword
-                        const uint32_t sel = ib ? 0x07060302u : 0x05040100u;
-                        u32x4_t bv;
+                for (int jw = 0; jw < kZeWordsPerWave; ++jw) {
+                    if (jw < nwords) {
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            bv[e] = sign_pair_bf16(__builtin_amdgcn_perm(vw[2 * e + 1], vw[2 * e], sel), col);
+                        for (int ib = 0; ib < 2; ++ib) {
+                            const u32x4_t bv = s2 == 0 ? (ib == 0 ? signs_from_row<0>(o.pv[jw], mcol, col)
+                                                                  : signs_from_row<4>(o.pv[jw], mcol, col))
+                                                       : (ib == 0 ? signs_from_row<8>(o.pv[jw], mcol, col)
+                                                                  : signs_from_row<12>(o.pv[jw], mcol, col));
 #pragma unroll
-                        for (int mb = 0; mb < MB; ++mb) acc[jw][ib][mb] = mfma_bf16(o.a[mb], bv, acc[jw][ib][mb]);
+                            for (int mb = 0; mb < MB; ++mb)
+                                acc[jw][ib][mb] = mfma_bf16(o.a[s2][mb], bv, acc[jw][ib][mb]);
+                        }
                     }
                 }
             }
         };
         ZeOps oa, ob;
         ld_ops(0, oa);
-        for (int t = 0; t < ns; t += 2) {
-            if (t + 1 < ns) ld_ops(t + 1, ob);
-            step(oa);
-            if (t + 2 < ns) ld_ops(t + 2, oa);
-            if (t + 1 < ns) step(ob);
+        for (int t = 0; t < ns; t += 4) {
+            if (t + 2 < ns) ld_ops(t + 2, ob);
+            step2(oa, t);
+            if (t + 4 < ns) ld_ops(t + 4, oa);
+            if (t + 2 < ns) step2(ob, t + 2);
         }
     }
     TLM(2);
@@ -717,16 +749,12 @@ __device__ void ze_side_workgroup(const MfmaParams &p, float4_t *lds) {
     __syncthreads();
     __shared__ uint32_t s_ok;
     if (threadIdx.x == 0) {
-        const uint32_t gen = s_gen;
+        // the counter starts the call at zero (the K-slice sum launch of the
+        // previous call cleared it) and only grows during the launch
         bool ok = true;
-        if (arrive(p.zecnt) == (uint32_t)(P - 1)) {
-            // (the cleared counter is needed only by the next call, after
-            // the launch boundary)
-            st_u32(p.zecnt, 0u);
-            st_u32(p.zecnt + 1, gen + 1u);
-        } else {
+        if (arrive(p.zecnt) != (uint32_t)(P - 1)) {
             const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-            while (ld_u32(p.zecnt + 1) == gen) {
+            while (ld_u32(p.zecnt) < (uint32_t)P) {
                 if (!p.spin_limit || __builtin_amdgcn_s_memrealtime() - t0 >= (uint64_t)p.spin_limit) {
                     ok = false;
                     break;
@@ -821,6 +849,9 @@ __global__ void __launch_bounds__(64 * kEpWaves) mfma_epilogue_zc_kernel(MfmaPar
     extern __shared__ u32x4_t s_za[];             // [W][2 hi/lo][64 lanes]
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int col = lane & 15, grp = lane >> 4;
+    // the side workgroups' counter, for the next call (none of them reads it
+    // after the launch boundary)
+    if (blockIdx.x == 0 && threadIdx.x == 0) st_u32(p.zecnt, 0u);
     const int mb = blockIdx.x % MB, rb0 = ((blockIdx.x / MB) * kEpWaves + wave) * kEpRbw;
     const int m0 = 16 * mb + 4 * grp;
     // z's operands (at most 32 words: 8 16-byte pieces per thread), U's
