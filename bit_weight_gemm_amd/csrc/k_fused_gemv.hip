@@ -392,60 +392,55 @@ __host__ __device__ constexpr int gemv_rows_per_wave(int kbl, int mm) {
          : ((200 - 8 * kbl * mm) / (3 * kbl + 4) <= 1 ? 1 : (200 - 8 * kbl * mm) / (3 * kbl + 4));
 }
 
-// z in LDS: value (m, i) at m (rpad + rpad / 16) + i + 2 (i / 32).  The two
-// spare floats per 32 put the values one read of the correction takes (16
-// words apart by 32 indices, 4 lane groups apart by 1) on distinct banks.
-__device__ __forceinline__ int zslot(const GemvParams &p, int m, int i) {
-    return m * (p.rpad + (p.rpad >> 4)) + i + 2 * (i >> 5);
+// One launch: z as sign tables in LDS.  Group g of row m holds ranks
+// 4 g .. 4 g + 3; its table holds, for every nibble n of U's sign bits over
+// those ranks (bit j set: sign -1 on rank 4 g + j), the sum of the four
+// signed z values.  Rows of tables are kTabStride floats apart, so that the
+// 64 lanes of one lookup (64 groups, any nibbles) spread over the banks.
+constexpr int kTabStride = 17;
+
+// Lane c of the caller's quad's value (DPP quad_perm [c, c, c, c]).
+template <int C>
+__device__ __forceinline__ float quad_bcast(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), C * 0x55, 0xF, 0xF, false));
 }
 
-// Correction of the wave's first NR rows: bit pairs (pb, pb + 16),
-// pb = lane / 16 + 4 j, of the lane's U words (lane % 16) + 16 q, against z
-// (LDS) split into bf16 high + bf16 low parts; added to the per-lane row sums.
-template <int MM, int NR, int R, int QMAX>
-__device__ __forceinline__ void add_correction(const GemvParams &p, const float *s_z,
-                                               const uint32_t (&ul)[QMAX],
-                                               float (&part)[R][MM]) {
+// Correction of the wave's rows (one launch): lane l takes groups
+// g = l + 64 h, whose nibble is bits 4 (l % 8) .. of word g / 8 = l / 8 + 8 h
+// of the row (held, after the loads of request_correction_inputs, by lane
+// 16 rr + (g / 8) % 16 in round g / 128), and adds that group's table entry
+// to the per-lane row sum; the reduction over lanes follows.
+template <int MM, int R, int QMAX>
+__device__ __forceinline__ void add_correction_lut(const GemvParams &p, const float *s_tab,
+                                                   const uint32_t (&ul)[QMAX],
+                                                   float (&part)[R][MM]) {
     const int lane = threadIdx.x & 63;
-    const int W = p.rpad >> 5;
+    const int G = p.rpad >> 2;
+    const int sh = 4 * (lane & 7);
+    // every row slot is looked up (slots past the wave's rows add to sums
+    // that are never stored) and lanes past the last group read the last
+    // group's table and add zero, so that no branch splits the shuffles and
+    // reads of a round and their waits overlap
 #pragma unroll
-    for (int q = 0; q < QMAX; ++q) {
-        if (16 * q >= W) break;
-        const int w = (lane & 15) + 16 * q;
-        const bool wok = w < W;
-        // word w of row rr, from lane 16 rr + w % 16 (which loaded it)
-        uint32_t uw[NR];
+    for (int h = 0; h < 2 * QMAX; ++h) {
+        if (64 * h >= G) break;
+        const int g = lane + 64 * h;
+        const bool ok = g < G;
+        const int gc = ok ? g : G - 1;
+        uint32_t w[R];
 #pragma unroll
-        for (int rr = 0; rr < NR; ++rr) uw[rr] = __shfl(ul[q], 16 * rr + (lane & 15), 64);
-        uint32_t zhi[4][MM], zlo[4][MM];
+        for (int rr = 0; rr < R; ++rr)
+            w[rr] = __shfl(ul[h >> 1], 16 * rr + 8 * (h & 1) + (lane >> 3), 64);
+        float v[R][MM];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int pb = (lane >> 4) + 4 * j;
+        for (int rr = 0; rr < R; ++rr)
 #pragma unroll
-            for (int m = 0; m < MM; ++m) {
-                const int i0 = 32 * w + pb, i1 = i0 + 16;
-                const float z0 = (wok && i0 < p.r) ? s_z[zslot(p, m, i0)] : 0.0f;
-                const float z1 = (wok && i1 < p.r) ? s_z[zslot(p, m, i1)] : 0.0f;
-                const uint32_t h0 = __float_as_uint(z0) & 0xFFFF0000u;
-                const uint32_t h1 = __float_as_uint(z1) & 0xFFFF0000u;
-                const uint32_t l0 = __float_as_uint(z0 - __uint_as_float(h0));
-                const uint32_t l1 = __float_as_uint(z1 - __uint_as_float(h1));
-                zhi[j][m] = (h0 >> 16) | h1;
-                zlo[j][m] = (l0 >> 16) | (l1 & 0xFFFF0000u);
-            }
-        }
+            for (int m = 0; m < MM; ++m)
+                v[rr][m] = s_tab[(m * G + gc) * kTabStride + (int)((w[rr] >> sh) & 15u)];
 #pragma unroll
-        for (int rr = 0; rr < NR; ++rr) {
+        for (int rr = 0; rr < R; ++rr)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t sg = signs_bf16x2(uw[rr], (lane >> 4) + 4 * j);
-#pragma unroll
-                for (int m = 0; m < MM; ++m) {
-                    part[rr][m] = dot2_bf16(sg, zhi[j][m], part[rr][m]);
-                    part[rr][m] = dot2_bf16(sg, zlo[j][m], part[rr][m]);
-                }
-            }
-        }
+            for (int m = 0; m < MM; ++m) part[rr][m] += ok ? v[rr][m] : 0.0f;
     }
 }
 
@@ -493,19 +488,21 @@ __global__ void __launch_bounds__(kGemvThreads) fused_gemv_kernel(GemvParams p) 
     static_assert(R >= 1 && R <= 4, "the row-count switch covers 1 .. 4 rows per wave");
     constexpr bool has_z = ZMODE != 0;
     constexpr int QMAX = 2;                    // r <= 1024: two rounds of 16 words
-    constexpr int ZP = 2 * MM;                 // z values per thread (MM * r <= MM * 1024)
+    constexpr int ZP = 2 * MM;                 // z values per thread (MM * rpad <= MM * 1024)
     constexpr int AMAX = (MM * KBL * 64 + kGemvThreads - 1) / kGemvThreads;  // blocks per thread
-    __shared__ float s_red[8];
     __shared__ uint32_t s_bcast;
     __shared__ float s_zslots[kGemvThreads / 64][kZXR * MM];  // one launch: side workgroups' sums
-    extern __shared__ uint32_t s_dyn[];   // activation f16 pairs [MM][KB][8], then z [MM][rpad]
+    extern __shared__ uint32_t s_dyn[];   // activation f16 pairs [MM][KB][8]; one launch: then
+                                          // z's sign tables in the same place
 
     // the wave index as a scalar, so that the row count below is one too
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     TLG(0);
     const int KB = p.K >> 4, KH = p.K >> 1;
     uint32_t *s_act = s_dyn;
-    float *s_z = reinterpret_cast<float *>(s_dyn + (size_t)MM * KB * 8);
+    // one launch: the sign tables of z, over the activation's area (dead
+    // once every wave has its rows)
+    float *s_tab = reinterpret_cast<float *>(s_dyn);
 
     // the call's epoch (one launch): a device-scope load by every thread,
     // requested with the correction inputs (first, it would hold up the
@@ -589,21 +586,22 @@ __global__ void __launch_bounds__(kGemvThreads) fused_gemv_kernel(GemvParams p) 
     }
     (void)qx;
     // 2. one launch: this thread's z values, requested behind the rows' loads
-    const int nz = MM * p.r;
     // one launch: this thread's z values (requested after the first row)
     // Two reads of each value: the first right behind the first row's loads
     // (it returns with the stream when it reaches memory after the side
     // workgroups have published), the second after the first row's
     // arithmetic, for values the first one found not yet published.
+    // Thread t reads values t + 512 j of z (row m = (t + 512 j) / rpad, index
+    // (t + 512 j) % rpad; clamped to a value that exists): the four lanes of
+    // a quad hold the four values of one group of the sign tables.
     uint64_t zv[ZP], zv2[ZP];
     const __amdgpu_buffer_rsrc_t r_zt = buffer_of(p.zt, (int64_t)MM * p.rpad * 8);
+    const int nzp = MM * p.rpad;
     auto z_request = [&](uint64_t (&dst)[ZP]) {
 #pragma unroll
         for (int j = 0; j < ZP; ++j) {
-            const int idx = threadIdx.x + kGemvThreads * j;
-            const int ic = idx < nz ? idx : nz - 1;
-            const int m = ic / p.r, i = ic - m * p.r;
-            dst[j] = ld_tagged(r_zt, opaque((m * p.rpad + i) * 8));
+            const int idx = (int)threadIdx.x + kGemvThreads * j;
+            dst[j] = ld_tagged(r_zt, opaque((idx < nzp ? idx : nzp - 1) * 8));
         }
     };
     // one launch: the epoch has been read (the bookkeeper may advance it once
@@ -713,6 +711,11 @@ __global__ void __launch_bounds__(kGemvThreads) fused_gemv_kernel(GemvParams p) 
             }
         }
     };
+    auto qa_all = [&]() {
+        qa_share();
+        __syncthreads();
+        qa_fetch();
+    };
     if constexpr (!lane_act && !QA) {
 #pragma unroll
     for (int a = 0; a < AMAX; ++a) {
@@ -763,7 +766,7 @@ __global__ void __launch_bounds__(kGemvThreads) fused_gemv_kernel(GemvParams p) 
     auto rows = [&](auto nr_c) {
         constexpr int NR = decltype(nr_c)::value;
         u32x2_t codes[NR][KBL];
-        uint32_t sc[NR][KBL];
+        uint8_t sc[NR][KBL];
         auto load_row = [&](int rr) {
             const int n = row0 + rr;
 #pragma unroll
@@ -785,6 +788,14 @@ __global__ void __launch_bounds__(kGemvThreads) fused_gemv_kernel(GemvParams p) 
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (ZMODE == 1) z_produce();
         __builtin_amdgcn_sched_barrier(0);
+        // QA: the activation is quantised while the first row streams in
+        if constexpr (QA) qa_all();
+        __builtin_amdgcn_sched_barrier(0);
+        // With r > 0 the widening of the first row's scale bytes sits here,
+        // so the other rows are requested once the first has arrived.
+        // Measured at M = 1, K = N = 5120, r = 512: 0.15 us faster than
+        // requesting every row at once (scales as aligned words, no wait);
+        // at r = 0 (no wait here) the word loads were 0.1 us slower too.
 #pragma unroll
         for (int rr = 1; rr < NR; ++rr) load_row(rr);
         __builtin_amdgcn_sched_barrier(0);
@@ -814,7 +825,7 @@ __global__ void __launch_bounds__(kGemvThreads) fused_gemv_kernel(GemvParams p) 
 #pragma unroll
             for (int t = 0; t < KBL; ++t) {
                 const bool valid = lane + 64 * t < KB;
-                const float sw = __builtin_amdgcn_cvt_f32_fp8(sc[rr][t], 0);
+                const float sw = __builtin_amdgcn_cvt_f32_fp8((uint32_t)sc[rr][t], 0);
                 const float mant = scale_mant(sw);
                 const uint32_t c0 = valid ? codes[rr][t].x : 0u;
                 const uint32_t c1 = valid ? codes[rr][t].y : 0u;
@@ -845,17 +856,10 @@ __global__ void __launch_bounds__(kGemvThreads) fused_gemv_kernel(GemvParams p) 
         // are consumed, so no row waits for them
         if constexpr (ZMODE == 2) add_correction_ops<MM, NR, R, QMAX>(p, ul, zo, part);
     };
-    // QA: the activation first (the x loads are the oldest in flight): each
-    // wave quantises its share into LDS, one barrier, every lane takes its
-    // blocks; the rows are requested after that.  (Quantised after the rows'
-    // loads were issued, the shares waited for the slowest wave's issue, up
-    // to 3 us under the stream's back-pressure: 7.3 us per quantising r = 0
-    // call against 6.4 us this way, config 1.)
-    if constexpr (QA) {
-        qa_share();
-        __syncthreads();
-        qa_fetch();
-    }
+    // QA: the activation is quantised after the first row's loads (the x
+    // loads are the oldest in flight): each wave quantises its share into
+    // LDS, one barrier, every lane takes its blocks; the other rows are
+    // requested after that.
     request_correction_inputs();
     __builtin_amdgcn_sched_barrier(0);
     switch (nrows) {
@@ -867,42 +871,58 @@ __global__ void __launch_bounds__(kGemvThreads) fused_gemv_kernel(GemvParams p) 
             if constexpr (ZMODE == 1) {
                 z_request(zv);
                 z_produce();
-                z_request(zv2);
             }
+            if constexpr (QA) qa_all();
+            if constexpr (ZMODE == 1) z_request(zv2);
             break;
     }
 
     TLG(3);
-    // 9. one launch: z into LDS, then the correction.  Values whose tag is not
+    // 9. one launch: z into sign tables in LDS (the four lanes of a quad
+    // hold one group's values; each builds four of its 16 entries), then the
+    // correction looks the rows' sign nibbles up.  Values whose tag is not
     // yet this call's are re-read within a bounded time, and computed here if
     // still missing.
     if (ZMODE == 1 && wg_rows > 0) {
         if (threadIdx.x == 0) s_bcast = ep;
         __syncthreads();
         const uint32_t tag = s_bcast + 1u;
+        const int G = p.rpad >> 2, q = lane & 3;
 #pragma unroll
         for (int j = 0; j < ZP; ++j) {
-            const int idx = threadIdx.x + kGemvThreads * j;
-            if (idx < nz) {
-                const int m = idx / p.r, i = idx - m * p.r;
+            const int idx = (int)threadIdx.x + kGemvThreads * j;
+            const int m = idx / p.rpad, i = idx - m * p.rpad;
+            float zj = 0.0f;
+            if (idx < nzp && i < p.r) {
                 uint64_t a = (uint32_t)(zv[j] >> 32) == tag ? zv[j] : zv2[j];
                 if ((uint32_t)(a >> 32) != tag && p.spin_limit) {
                     const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
                     do {
                         __builtin_amdgcn_s_sleep(1);
-                        a = ld_tagged(r_zt, (m * p.rpad + i) * 8);
+                        a = ld_tagged(r_zt, idx * 8);
                     } while ((uint32_t)(a >> 32) != tag &&
                              __builtin_amdgcn_s_memrealtime() - t0 < (uint64_t)p.spin_limit);
                 }
-                s_z[zslot(p, m, i)] = ((uint32_t)(a >> 32) == tag && p.spin_limit)
-                                          ? __uint_as_float((uint32_t)a)
-                                          : z_local(p, m, i);
+                zj = ((uint32_t)(a >> 32) == tag && p.spin_limit) ? __uint_as_float((uint32_t)a)
+                                                                  : z_local(p, m, i);
+            }
+            // the quad's four values (every lane active), then this lane's
+            // entries n = 4 q .. 4 q + 3 of group i / 4
+            const float z0 = quad_bcast<0>(zj), z1 = quad_bcast<1>(zj);
+            const float z2 = quad_bcast<2>(zj), z3 = quad_bcast<3>(zj);
+            if (idx < nzp) {
+                const float hq = ((q & 1) ? -z2 : z2) + ((q & 2) ? -z3 : z3);
+                float *t = s_tab + (m * G + (i >> 2)) * kTabStride + 4 * q;
+                t[0] = (z0 + z1) + hq;
+                t[1] = (z1 - z0) + hq;
+                t[2] = (z0 - z1) + hq;
+                t[3] = -(z0 + z1) + hq;
             }
         }
         TLG(4);
         __syncthreads();
         TLG(5);
-        add_correction<MM, R, R, QMAX>(p, s_z, ul, part);
+        add_correction_lut<MM, R, QMAX>(p, s_tab, ul, part);
     }
 
     // 10. one reduction per row and m, then the bf16 (or fp32) store
@@ -989,7 +1009,9 @@ __global__ void __launch_bounds__(kGemvThreads) z_kernel(GemvParams p) {
 
 namespace {
 size_t gemv_lds_bytes(int M, int K, int rpad) {
-    return (size_t)M * (size_t)(K / 16) * 32 + (size_t)M * (size_t)(rpad + rpad / 16) * 4;
+    const size_t act = (size_t)M * (size_t)(K / 16) * 32;
+    const size_t tab = (size_t)M * (size_t)(rpad / 4) * kTabStride * 4;
+    return act > tab ? act : tab;
 }
 
 template <int MM, int KBL, int ZMODE>
