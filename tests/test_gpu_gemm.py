@@ -331,3 +331,20 @@ def test_graph_replay_as_timed(cfg, sched):
             assert torch.equal(t, y_eager), f"config {cfg} schedule {sched} replay {rep} call {i}"
         np.testing.assert_array_equal(p.a_codes.cpu().numpy(), rc, err_msg=f"replay {rep}")
         np.testing.assert_array_equal(p.a_scales.cpu().numpy(), rs, err_msg=f"replay {rep}")
+
+
+# The one-launch vector schedule applies z through sign tables of 4 ranks,
+# 64 groups per lane round: ranks on either side of every group, word and
+# round boundary, at both batch sizes it takes.
+@pytest.mark.parametrize("M", [1, 2])
+@pytest.mark.parametrize("r", [1, 3, 4, 5, 31, 32, 33, 255, 256, 257, 511, 513, 1023, 1024])
+def test_vector_schedule_rank_boundaries(M, r):
+    K, N = 640, 300
+    d = wl.make_inputs(M, K, N, r, seed=900 + 7 * r + M)
+    y_ref = oracle.gemm_lowrank(d["x"], d["wcode"], d["wscales"], d["g"], d["V"], d["U"],
+                                d["alpha"])
+    assert B.BILOCO_SCHED_FUSED_GEMV in _schedules(d)
+    p = DeviceProblem(d)
+    for rep in range(2):          # the second call finds the first call's tags in the workspace
+        y, _ = _run(d, B.BILOCO_SCHED_FUSED_GEMV, p)
+        check_y(y, y_ref, f"M={M} r={r} call {rep}")
