@@ -622,6 +622,11 @@ def timeline(args) -> int:
     out = {"config": cfg, "r": d["r"], "schedule": SCHED_NAMES.get(sched, sched),
            "call": "quantise + product" if step else "product", "us_per_call_timeline_build":
            round(t * 1e6, 3), "workgroups": int(len(wgs)), "groups": {}}
+    if fam == "gemv" and (tl[:, :, 8] > 0).any():
+        # one launch: the stream waves' z values by the read that had the tag
+        cnt = {k: int((tl[:, :, s] - 1)[tl[:, :, s] > 0].sum()) for k, s in
+               (("first read", 8), ("second read", 9), ("read again", 10))}
+        out["z_reads"] = cnt
     if fam == "mfma":
         out["finishers"] = int((tl[:, 0, 12] == 1).sum())
         out["waves_computing_z_locally"] = int((tl[:, :, 13] == 1).sum())
@@ -667,6 +672,10 @@ def timeline(args) -> int:
              "(the library built with BILOCO_TIMELINE), for the last call of a graph of 20 calls over "
              "rotated weights; microseconds from the earliest workgroup start.  The stamps' stores "
              f"slow the call a little: {out['us_per_call_timeline_build']} us per call in this build.", ""]
+    if "z_reads" in out:
+        zr = out["z_reads"]
+        lines += ["z values of the stream waves by the read that carried the call's tag: "
+                  + "; ".join(f"{k} {v}" for k, v in zr.items()) + ".", ""]
     if fam == "mfma":
         lines += [f"Finisher workgroups: {out['finishers']}; waves that computed z locally: "
                   f"{out['waves_computing_z_locally']}.", ""]

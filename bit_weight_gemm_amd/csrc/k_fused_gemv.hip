@@ -55,7 +55,9 @@ constexpr int kGemvThreads = 512;   // 8 waves per workgroup
 
 // measurement build only: per-wave stamps (slots: 0 start, 1 first row's
 // loads issued, 2 every row's loads issued (side workgroups: z published),
-// 3 rows done, 4 z values checked, 5 correction started, 6 stored)
+// 3 rows done, 4 z values checked, 5 correction started, 6 stored) and, one
+// launch, counts + 1 of the wave's z values whose first read had the call's
+// tag (8), whose second read had it (9), and that were read again (10)
 #ifdef BILOCO_TIMELINE
 __device__ uint64_t g_tl_gemv[kTlMaxWorkgroups * 8 * kTlSlots];
 #define TLG(pt) BILOCO_TL_AT(g_tl_gemv, pt, __builtin_amdgcn_s_memrealtime())
@@ -888,6 +890,9 @@ __global__ void __launch_bounds__(kGemvThreads) fused_gemv_kernel(GemvParams p) 
         __syncthreads();
         const uint32_t tag = s_bcast + 1u;
         const int G = p.rpad >> 2, q = lane & 3;
+#ifdef BILOCO_TIMELINE
+        uint32_t n_first = 0, n_second = 0, n_reread = 0;   // this wave's values, by the read that had the tag
+#endif
 #pragma unroll
         for (int j = 0; j < ZP; ++j) {
             const int idx = (int)threadIdx.x + kGemvThreads * j;
@@ -895,6 +900,12 @@ __global__ void __launch_bounds__(kGemvThreads) fused_gemv_kernel(GemvParams p) 
             float zj = 0.0f;
             if (idx < nzp && i < p.r) {
                 uint64_t a = (uint32_t)(zv[j] >> 32) == tag ? zv[j] : zv2[j];
+#ifdef BILOCO_TIMELINE
+                n_first += (uint32_t)__builtin_popcountll(__ballot((uint32_t)(zv[j] >> 32) == tag));
+                n_second += (uint32_t)__builtin_popcountll(
+                    __ballot((uint32_t)(zv[j] >> 32) != tag && (uint32_t)(zv2[j] >> 32) == tag));
+                n_reread += (uint32_t)__builtin_popcountll(__ballot((uint32_t)(a >> 32) != tag));
+#endif
                 if ((uint32_t)(a >> 32) != tag && p.spin_limit) {
                     const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
                     do {
@@ -920,6 +931,11 @@ __global__ void __launch_bounds__(kGemvThreads) fused_gemv_kernel(GemvParams p) 
             }
         }
         TLG(4);
+#ifdef BILOCO_TIMELINE
+        BILOCO_TL_AT(g_tl_gemv, 8, n_first + 1u);
+        BILOCO_TL_AT(g_tl_gemv, 9, n_second + 1u);
+        BILOCO_TL_AT(g_tl_gemv, 10, n_reread + 1u);
+#endif
         __syncthreads();
         TLG(5);
         add_correction_lut<MM, R, QMAX>(p, s_tab, ul, part);
