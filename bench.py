@@ -662,6 +662,18 @@ def timeline(args) -> int:
                                            (("p10", 10), ("median", 50), ("p90", 90))},
             "stored_median_by_xcd": [round(float(np.nanmedian(rel[prod, 0, ks][xcd == x])), 2)
                                      if (xcd == x).any() else None for x in range(8)]}
+    if fam == "gemv":
+        # the stream waves' rows by wave index inside the workgroup (wave w
+        # is the (w // 4 + 1)-th wave of SIMD w % 4) and the spread inside a
+        # workgroup
+        sw = tl[:, 0, 1] > 0
+        done = rel[sw, :, names.index("rows done")]
+        if np.isfinite(done).any():
+            spread = np.nanmax(done, axis=1) - np.nanmin(done, axis=1)
+            out["stream_breakdown"] = {
+                "rows_done_median_by_wave": [round(float(np.nanmedian(done[:, w])), 2) for w in range(8)],
+                "within_workgroup_spread_us": {q: round(float(np.nanpercentile(spread, pc)), 2) for q, pc in
+                                               (("p10", 10), ("median", 50), ("p90", 90))}}
     cmd = "python3 bench.py --timeline --config %d%s%s%s" % (
         cfg, f" --schedule {args.schedule}" if args.schedule else "",
         " --timeline-r0" if args.timeline_r0 else "", " --timeline-step" if step else "")
@@ -693,6 +705,13 @@ def timeline(args) -> int:
                   "- spread between a workgroup's first and last wave to finish its row blocks (p10 / median / p90): "
                   + " / ".join(str(v) for v in pb["within_workgroup_spread_us"].values()),
                   "- stored, median by XCD 0..7: " + ", ".join(str(v) for v in pb["stored_median_by_xcd"]), ""]
+    if "stream_breakdown" in out:
+        sb = out["stream_breakdown"]
+        lines += ["## stream workgroups: where the time goes", "",
+                  "- rows done, median by wave index 0..7: " +
+                  ", ".join(str(v) for v in sb["rows_done_median_by_wave"]),
+                  "- spread between a workgroup's first and last wave to finish its rows (p10 / median / p90): "
+                  + " / ".join(str(v) for v in sb["within_workgroup_spread_us"].values()), ""]
     tag = "_step" if step else ""
     path = os.path.join(ROOT, "profiles", f"timeline_{out['schedule']}_{wname}{tag}.md")
     with open(path, "w") as f:
