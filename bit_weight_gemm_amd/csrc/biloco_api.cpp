@@ -50,16 +50,16 @@ biloco_status check_shape(int32_t M, int32_t N, int32_t K, int32_t r) {
 
 // Measured on MI355X (M = 1, K = N = 5120, r = 512, graph replay): the
 // one-launch vector-ALU schedule (side workgroups compute z while the
-// others stream R) takes 7.3 us per call and 9.1 us per quantising call,
-// against 8.8 and 9.5 us for two launches (z, then the product).  r = 0
+// others stream R) takes 7.0-7.2 us per call and 7.7-7.9 us per quantising
+// call, against 8.8 and 9.5 us for two launches (z, then the product).  r = 0
 // has one launch either way.  From M = 3 on, the matrix-core schedules: with
 // side workgroups where x is small enough for one workgroup to read it per
-// word (M = 8, K = 5120, N = 13824, r = 512: 16.7-17.4 us per call against
-// 20.8-21.6 us with z in launches of its own), else with z in launches of
+// word (M = 8, K = 5120, N = 13824, r = 512: 16.4-16.9 us per call against
+// 20.9-21.1 us with z in launches of its own), else with z in launches of
 // its own.  Where K is split over workgroups and x is larger (M = 32,
 // K = 13824, N = 5120, r = 512 and M = 32, K = 8192, N = 8192, r = 1024),
 // z computed by K-part in side workgroups and applied in the K-slice sum
-// launch: 23.4-23.9 us against 27.4-28.0 us with z in launches of its own.
+// launch: 20.5-22.5 us against 26.4-27.4 us with z in launches of its own.
 int resolve_schedule(int M, int N, int K, int r) {
     if (M >= 3 && mfma_side_supported(M, N, K, r)) return BILOCO_SCHED_MFMA_SIDE;
     if (M >= 3 && mfma_ze_supported(M, N, K, r)) return BILOCO_SCHED_MFMA_ZEPI;

@@ -20,24 +20,27 @@
 //    LDS behind one barrier;
 //  * z: v_dot2 (bf16) of x against bf16 pairs of +-1 built from V's words,
 //    exact products, one workgroup per two indices i over all of K;
-//  * the correction multiplies U's signs (bf16 pairs) with z split into bf16
-//    high and low parts (about 16 bits of z) and joins the row sum before
-//    the one reduction per row and m.
+//  * the correction joins the row sums before the one reduction per row and
+//    m: in one launch through sign tables of z in LDS (per group of 4 ranks,
+//    the 16 signed sums of their z values, looked up by U's sign nibbles);
+//    with two launches U's signs (bf16 pairs) meet z split into bf16 high and
+//    low parts (about 16 bits of z) in v_dot2.
 //
 // Two forms of the z hand-off:
-//  * two launches (the default): z_kernel writes z, already split into its
-//    high/low parts in the lane order of the correction, and (in the
-//    quantising call) quantises x in workgroups of its own; the product then
-//    loads those operands straight into registers;
-//  * one launch: the first workgroups also produce z while every workgroup
-//    streams R.  Each z value is published as one 64-bit word (fp32 value |
-//    epoch << 32) with a relaxed device-scope store and read back with
-//    device-scope loads, so data and tag travel together and no fence is
-//    needed.  The call's epoch is a plain load at start; every workgroup
-//    then writes a "seen" flag, and workgroup 0 advances the epoch at its
-//    end once every flag is in.  A consumer's wait for z is bounded: when it
-//    runs out the consumer computes the z values itself, so the kernel ends
-//    whatever else runs.
+//  * one launch (the default at r > 0): the first workgroups compute z while
+//    the others stream R.  Each z value is published as one 64-bit word
+//    (fp32 value | epoch << 32) with a relaxed device-scope store and read
+//    back with device-scope loads, so data and tag travel together and no
+//    fence is needed.  The call's epoch is a plain load at start; every
+//    workgroup then writes a "seen" flag, and workgroup 0 advances the epoch
+//    at its end once every flag is in.  A consumer's wait for z is bounded:
+//    when it runs out the consumer computes the z values itself, so the
+//    kernel ends whatever else runs.  The quantising call also quantises x
+//    in every stream workgroup, while its first row of R streams in;
+//  * two launches: z_kernel writes z, already split into its high/low parts
+//    in the lane order of the correction, and (in the quantising call)
+//    quantises x in workgroups of its own; the product then loads those
+//    operands straight into registers.
 #include <algorithm>
 #include <type_traits>
 

@@ -58,8 +58,15 @@ typedef int32_t biloco_status;
 #define BILOCO_SCHED_AUTO        0  /* pick per shape (biloco_default_schedule) */
 #define BILOCO_SCHED_UNFUSED     1  /* two launches: z, then a vector-ALU product kernel that
                                        adds the correction before the store (the default at
-                                       M <= 2; a plain, slow fallback at larger M) */
-#define BILOCO_SCHED_FUSED_GEMV  2  /* one launch; vector-ALU dot products; M <= 2 */
+                                       M <= 2 with r == 0, where it is one launch; a plain,
+                                       slow fallback at larger M) */
+#define BILOCO_SCHED_FUSED_GEMV  2  /* one launch; vector-ALU dot products; M <= 2, r >= 1
+                                       (the default there): its first workgroups compute z
+                                       while the others stream R, which apply z through
+                                       sign tables in LDS.  Needs every workgroup resident
+                                       at once for its speed, not for its results: a wait
+                                       for z is bounded, after which the waiting thread
+                                       computes the value itself */
 #define BILOCO_SCHED_FUSED_MFMA  3  /* matrix-core products for any M <= 32: a z kernel
                                        (skipped when r == 0; for K > 7168 a second launch
                                        sums its K-slices), then one product kernel whose
