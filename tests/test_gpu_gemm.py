@@ -221,6 +221,22 @@ def test_quant_and_product_in_one_call_edges(M, K, N, r):
     _fused_quant_case(d, y_ref, [B.BILOCO_SCHED_AUTO] + _schedules(d))
 
 
+# The quantising vector-schedule calls quantise x while each wave's first
+# row streams in: every activation layout they take (per-lane blocks or the
+# workgroup's LDS copy, 1 to 16 blocks per lane), with and without z, with
+# rows per wave from 1 to the register budget's maximum.
+@pytest.mark.parametrize("M,K", [(1, 256), (1, 1056), (1, 5120), (1, 16384), (2, 256), (2, 3072),
+                                 (2, 8192)])
+@pytest.mark.parametrize("N,r", [(77, 0), (2300, 0), (77, 9), (2300, 512)])
+def test_quant_vector_schedule_layouts(M, K, N, r):
+    d = wl.make_inputs(M, K, N, r, seed=1300 + M + K + N + r)
+    y_ref = oracle.gemm_lowrank(d["x"], d["wcode"], d["wscales"], d["g"], d["V"], d["U"],
+                                d["alpha"])
+    scheds = [B.BILOCO_SCHED_AUTO] + [s for s in _schedules(d)
+                                      if s in (B.BILOCO_SCHED_UNFUSED, B.BILOCO_SCHED_FUSED_GEMV)]
+    _fused_quant_case(d, y_ref, scheds)
+
+
 def _degenerate(d, what):
     """Degenerate operands of the method: the oracle's y for them has a plain
     form, checked before the GPU is compared with it."""
