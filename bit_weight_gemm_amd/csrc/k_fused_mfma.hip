@@ -155,6 +155,8 @@ struct MfmaParams {
     // K-part partials (zs K-steps each, ze_sub of them staged in LDS at a
     // time), then finish its words; the K-slice epilogue applies them
     int ze_sub;
+    int ze_wg;                  // word groups: side workgroup p takes K-part p % (n_side / ze_wg)
+                                // of the words of group p / (n_side / ze_wg)
     float4_t *zep;              // partials [kZeParts][W][2 rank halves][MB][64 lanes] (D layout)
     uint32_t *zecnt;            // the side workgroups' arrival counter (zero between calls)
 };
@@ -620,7 +622,10 @@ template <int MB>
 __device__ void ze_side_workgroup(const MfmaParams &p, float4_t *lds) {
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int col = lane & 15, grp = lane >> 4;
-    const int part = blockIdx.x, P = p.n_side;
+    const int P = p.n_side, Pk = P / p.ze_wg;
+    const int part = (int)blockIdx.x % Pk, wgrp = (int)blockIdx.x / Pk;
+    const int Wg = (p.W + p.ze_wg - 1) / p.ze_wg, w0 = wgrp * Wg;
+    const int nw = max(0, min(Wg, p.W - w0));                  // words of this group
     TLM(0);
     TLMV(14, 1);
     const int steps = p.K >> 5;
@@ -642,7 +647,8 @@ __device__ void ze_side_workgroup(const MfmaParams &p, float4_t *lds) {
     const __amdgpu_buffer_rsrc_t r_v = buffer_of(p.v, (int64_t)p.W * p.K * 4);
     // this lane's two sign bits of every pair dword (rank col, rank 16 + col)
     const uint32_t mcol = 0x00010001u << col;
-    const int nwords = (p.W - wave + kPWaves - 1) / kPWaves;    // words of this wave
+    const int nwords = (nw - wave + kPWaves - 1) / kPWaves;     // words of this wave (group-local
+                                                                // wave + 8 jw)
     for (int sub0 = 0; sub0 < nst; sub0 += p.ze_sub) {
         const int ns = min(p.ze_sub, nst - sub0);
         const int k00 = (st0 + sub0) * 32;
@@ -657,14 +663,14 @@ __device__ void ze_side_workgroup(const MfmaParams &p, float4_t *lds) {
             const int m = 16 * mb + (l & 15), k0 = k00 + t * 32 + 8 * (l >> 4);
             lx[j] = load16(r_x, opaque(t < ns && m < p.M ? (m * p.K + k0) * 2 : kOob));
             const int w = idx / (ns * 8), j4 = idx - w * (ns * 8);
-            lv[j] = load16(r_v, opaque(w < p.W ? (w * p.K + k00 + 4 * j4) * 4 : kOob));
+            lv[j] = load16(r_v, opaque(w < nw ? ((w0 + w) * p.K + k00 + 4 * j4) * 4 : kOob));
         }
 #pragma unroll
         for (int j = 0; j < kZeLoads; ++j) {
             const int idx = (int)threadIdx.x + kPThreads * j;
             if (idx < ns * MB * 64) s_x[idx] = lx[j];
             const int w = idx / (ns * 8), j4 = idx - w * (ns * 8);
-            if (w < p.W) {
+            if (w < nw) {
                 // k = 4 q .. 4 q + 3 of step t: pairs e = 2 h and 2 h + 1 of
                 // group q / 2
                 const int t = j4 >> 3, q = j4 & 7, gq = q >> 1, h = q & 1;
@@ -733,8 +739,8 @@ __device__ void ze_side_workgroup(const MfmaParams &p, float4_t *lds) {
     const __amdgpu_buffer_rsrc_t r_zep = buffer_of(p.zep, (int64_t)kZeParts * p.W * 2 * MB * 64 * 16);
 #pragma unroll
     for (int jw = 0; jw < kZeWordsPerWave; ++jw) {
-        const int w = wave + kPWaves * jw;
-        if (w < p.W) {
+        const int wl = wave + kPWaves * jw, w = w0 + wl;
+        if (wl < nw) {
 #pragma unroll
             for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
@@ -767,7 +773,7 @@ __device__ void ze_side_workgroup(const MfmaParams &p, float4_t *lds) {
     __syncthreads();
     TLM(4);
     const bool all_in = s_ok != 0u;
-    for (int w = part; w < p.W; w += P) {
+    for (int w = (int)blockIdx.x; w < p.W; w += P) {
         if (!all_in) {
             // fallback: wave 0 computes the word from x and V alone
             if (wave == 0) {
@@ -785,13 +791,14 @@ __device__ void ze_side_workgroup(const MfmaParams &p, float4_t *lds) {
         // per word) of the parts t / F, t / F + 2, ... (16-byte coherent
         // loads, all requested first), the two halves meet in LDS
         constexpr int F = 2 * MB * 64, NH = kPThreads / F, PPH = kZeParts / NH;
+        // (the parts of word w: the K-parts of its group, Pk of them)
         const int f = threadIdx.x % F, h = threadIdx.x / F;
         float4_t pv[PPH];
 #pragma unroll
         for (int j = 0; j < PPH; ++j) {
             const int pp = h + NH * j;
             pv[j] = __builtin_bit_cast(float4_t,
-                load16_sc1(r_zep, opaque(pp < P ? ((pp * p.W + w) * F + f) * 16 : kOob)));
+                load16_sc1(r_zep, opaque(pp < Pk ? ((pp * p.W + w) * F + f) * 16 : kOob)));
         }
         float4_t sum4 = pv[0];
 #pragma unroll
@@ -1572,7 +1579,7 @@ struct MfmaPlan {
     int n_side, side_split;
     // z-in-epilogue schedule: K-steps per side workgroup's part, and per
     // round staged in LDS
-    int ze_steps, ze_sub;
+    int ze_steps, ze_sub, ze_wg;
     // workspace offsets inside the matrix-core area
     size_t off_zpart, off_za, off_ypart, off_zpt, off_zat, off_zhp, off_zep, bytes;
 };
@@ -1736,12 +1743,28 @@ MfmaPlan ze_plan(int M, int N, int K, int r) {
     MfmaPlan q = mfma_plan(M, N, K, r, kGridTarget - kZeParts);
     q.n_side = kZeParts;
     if (q.grid + q.n_side > kGridTarget && kGridTarget - q.grid >= 8) q.n_side = (kGridTarget - q.grid) / 8 * 8;
-    // K-steps per part for this many parts, and per staged round
-    q.ze_steps = (K / 32 + q.n_side - 1) / q.n_side;
-    const size_t per_step = (size_t)q.mb * 64 * 16 + (size_t)q.W * 32 * 4;
-    q.ze_sub = (int)std::min<size_t>(q.lds / per_step, (size_t)q.ze_steps);
-    q.ze_sub = std::min(q.ze_sub, kZeLoads * kPThreads / (64 * q.mb));
-    q.ze_sub = std::min(q.ze_sub, kZeLoads * kPThreads / (8 * q.W));
+    // K-steps per part and per staged round for ze_wg word groups; two
+    // groups (each side workgroup a K-part twice as long, of half the words:
+    // half the partials to store and to sum) where every wave still has a
+    // word and the part still fits one staged round, one round trip under
+    // the stream.  Measured: M = 32, K = N = 8192, r = 1024: 21.6-21.9 us
+    // per call against 22.3-22.5 us with one group; M = 32, K = 13824,
+    // N = 5120, r = 512 would take two rounds: 24.2-24.4 us against
+    // 21.4-21.7 us.
+    auto steps_for = [&](int wg) {
+        const int Pk = q.n_side / wg, Wg = (q.W + wg - 1) / wg;
+        q.ze_wg = wg;
+        q.ze_steps = (K / 32 + Pk - 1) / Pk;
+        const size_t per_step = (size_t)q.mb * 64 * 16 + (size_t)Wg * 32 * 4;
+        q.ze_sub = (int)std::min<size_t>(q.lds / per_step, (size_t)q.ze_steps);
+        q.ze_sub = std::min(q.ze_sub, kZeLoads * kPThreads / (64 * q.mb));
+        q.ze_sub = std::min(q.ze_sub, kZeLoads * kPThreads / (8 * Wg));
+    };
+    if (q.W >= 2 * kPWaves && q.n_side % 2 == 0) {
+        steps_for(2);
+        if (q.ze_sub >= q.ze_steps) return q;
+    }
+    steps_for(1);
     return q;
 }
 }  // namespace
@@ -1941,6 +1964,7 @@ hipError_t launch_gemm_mfma_ze(const GemmArgs &a, hipStream_t stream) {
     p.n_side = q.n_side;
     p.zsteps = q.ze_steps;
     p.ze_sub = q.ze_sub;
+    p.ze_wg = q.ze_wg;
     return launch_product<3>(q, p, stream);
 }
 
