@@ -716,6 +716,7 @@ __global__ void __launch_bounds__(kGemvThreads) fused_gemv_kernel(GemvParams p) 
             }
         }
     };
+    constexpr bool qa_in_rows = KBL * MM <= 8;
     auto qa_all = [&]() {
         qa_share();
         __syncthreads();
@@ -794,7 +795,7 @@ __global__ void __launch_bounds__(kGemvThreads) fused_gemv_kernel(GemvParams p) 
         if constexpr (ZMODE == 1) z_produce();
         __builtin_amdgcn_sched_barrier(0);
         // QA: the activation is quantised while the first row streams in
-        if constexpr (QA) qa_all();
+        if constexpr (QA && qa_in_rows) qa_all();
         __builtin_amdgcn_sched_barrier(0);
         // With r > 0 the widening of the first row's scale bytes sits here,
         // so the other rows are requested once the first has arrived.
@@ -864,7 +865,11 @@ __global__ void __launch_bounds__(kGemvThreads) fused_gemv_kernel(GemvParams p) 
     // QA: the activation is quantised after the first row's loads (the x
     // loads are the oldest in flight): each wave quantises its share into
     // LDS, one barrier, every lane takes its blocks; the other rows are
-    // requested after that.
+    // requested after that.  With more blocks per lane (KBL MM > 8) the first
+    // row's registers and the quantisation's do not fit beside each other
+    // (spills), so there the activation is quantised before any row of R is
+    // requested.
+    if constexpr (QA && !qa_in_rows) qa_all();
     request_correction_inputs();
     __builtin_amdgcn_sched_barrier(0);
     switch (nrows) {
@@ -877,7 +882,7 @@ __global__ void __launch_bounds__(kGemvThreads) fused_gemv_kernel(GemvParams p) 
                 z_request(zv);
                 z_produce();
             }
-            if constexpr (QA) qa_all();
+            if constexpr (QA && qa_in_rows) qa_all();
             if constexpr (ZMODE == 1) z_request(zv2);
             break;
     }
