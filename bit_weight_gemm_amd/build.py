@@ -31,12 +31,33 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-function"]
 
 
-def _compile(src: str, build_dir: str = BUILD, extra=()) -> str:
+RESOURCES = os.path.join(BUILD, "resource_usage.json")
+
+
+def _resources(stderr: str) -> dict:
+    """Per-kernel VGPRs and scratch bytes per lane from hipcc's
+    -Rpass-analysis=kernel-resource-usage remarks."""
+    out, name = {}, None
+    for line in stderr.splitlines():
+        if "Function Name: " in line:
+            name = line.split("Function Name: ", 1)[1].split(" [")[0].strip()
+            out[name] = {}
+        elif name and "VGPRs: " in line:
+            out[name]["vgprs"] = int(line.split("VGPRs: ", 1)[1].split()[0])
+        elif name and "ScratchSize [bytes/lane]: " in line:
+            out[name]["scratch_bytes_per_lane"] = int(line.split("ScratchSize [bytes/lane]: ", 1)[1].split()[0])
+    return out
+
+
+def _compile(src: str, build_dir: str = BUILD, extra=(), usage: dict | None = None) -> str:
     obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC] + COMMON + list(extra) + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC] + COMMON + list(extra) + ["-Rpass-analysis=kernel-resource-usage", "-x", "hip",
+                                            "-c", os.path.join(CSRC, src), "-o", obj]
     p = subprocess.run(cmd, capture_output=True, text=True)
     if p.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{p.stderr}")
+    if usage is not None:
+        usage[src] = _resources(p.stderr)
     return obj
 
 
@@ -61,8 +82,13 @@ def build_floor(verbose: bool = True) -> str:
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
     srcs = [s for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
+    usage: dict = {}
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
+        objs = list(ex.map(lambda s: _compile(s, BUILD, (), usage), srcs))
+    # the kernels' register use, for tests/test_build_resources.py
+    import json
+    with open(RESOURCES, "w") as f:
+        json.dump(usage, f, indent=1, sort_keys=True)
     tmp = LIB + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     p = subprocess.run(cmd, capture_output=True, text=True)
