@@ -204,7 +204,7 @@ def weight_quant_table() -> dict:
 
 
 def decompose_time(m: int = 5120, n: int = 5120, r: int = 512, T: int = 5) -> dict:
-    """biloco_peel_decompose on a seeded fp32 weight of the config-1 shape: one
+    """biloco_peel_decompose on a seeded fp32 5120 x 5120 weight: one
     full decomposition (r terms of T sign steps, refit, residual) between HIP
     events on torch's stream, after one untimed run.  Each sign step is one
     pass over W for R v and one for R^T u; the residual reads W and writes R:
@@ -228,7 +228,10 @@ def decompose_time(m: int = 5120, n: int = 5120, r: int = 512, T: int = 5) -> di
     return {"m": m, "n": n, "r": r, "T": T, "ms": round(t * 1e3, 2),
             "GBps": round(nbytes / t / 1e9, 1),
             "pct_peak": round(100 * nbytes / t / 1e9 / PEAK_HBM_GBS, 2),
-            "bytes": nbytes}
+            "bytes": nbytes,
+            "note": f"W is {4 * m * n / 1e6:.0f} MB, which the 256 MB Infinity Cache holds: most of "
+                    "its passes are served from that cache, so pct_peak is a rate against the HBM "
+                    "peak, not an HBM measurement"}
 
 
 def stream_floor(configs=(1, 2, 3, 4), calls: int = 200) -> dict:
